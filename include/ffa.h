@@ -1,0 +1,147 @@
+/*
+ * ffa.h -- C ABI of the MI355X (gfx950) range-masked ("flex") flash attention library.
+ *
+ * The operation: attention over packed, variable-length tokens whose mask is
+ * a list of slices.  Slice r covers query rows [q_ranges[r][0], q_ranges[r][1])
+ * and key columns [k_ranges[r][0], k_ranges[r][1]); attn_type_map[r] is
+ * FFA_FULL (every cell of that rectangle is visible) or FFA_CAUSAL (cell
+ * (i, j) is visible iff j - ke <= i - qe: the causal diagonal runs through
+ * the rectangle's bottom-right corner).  A slice whose q range or k range is
+ * empty (start == end) covers nothing and costs nothing, so callers may pad
+ * the slice list to a fixed length with such rows.  These are the
+ * q_ranges / k_ranges / attn_type_map arguments of flex_flash_attn_func in the
+ * MagiAttention issue "Using dummy/padded attention slices with
+ * flex_flash_attn_func for torch.compile static shapes" (repro script: int32
+ * [R,2] ranges, 0 = FULL, 1 = CAUSAL; maintainer reply: zero-area slices are
+ * skipped).
+ *
+ * Per q head h (kv head g = h / (hq / hkv)) and query row i:
+ *   u_ij  = scale * <q_i, k_j>
+ *   s_ij  = softcap > 0 ? softcap * tanh(u_ij / softcap) : u_ij   (masked cells: -inf)
+ *   lse_i = log(sum_j exp(s_ij))                                  (natural log)
+ *   out_i = sum_j exp(s_ij - lse_i) v_j
+ * A row with no visible key gets out = 0 and lse = -inf.
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors are packed token-major ("THD"): q, out, dq, do are [Tq][hq][d],
+ *    k, v, dk, dv are [Tk][hkv][d], all bf16 and densely contiguous; lse is
+ *    fp32 [Tq][hq].  Device pointers, allocated and owned by the caller; the
+ *    library keeps none of them after the call returns.  Inputs are never
+ *    written.  Inputs must be finite.
+ *  - q_ranges, k_ranges (int32 [R][2]) and attn_type_map (int32 [R]) are HOST
+ *    arrays, read before the call returns.  Slices may come in any order; no
+ *    (i, j) cell may be covered by two slices.
+ *  - d is 64 or 128; hq is a positive multiple of hkv; scale > 0 and finite;
+ *    softcap >= 0 and finite (0 = off).  Tq, Tk >= 0 and every tensor must be
+ *    below 2^31 elements.
+ *  - stream is a hipStream_t (NULL = the default stream).  Calls enqueue work
+ *    and return; argument errors are reported synchronously before any GPU
+ *    work is enqueued.  The return value is FFA_OK or a negative FFA_ERR_*;
+ *    ffa_last_error() then describes the failure (thread-local).
+ */
+#ifndef FFA_H
+#define FFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* attn_type_map values (repro script: 0 = FULL, 1 = CAUSAL) */
+enum { FFA_FULL = 0, FFA_CAUSAL = 1 };
+
+/* status codes */
+enum {
+  FFA_OK = 0,
+  FFA_ERR_INVALID_ARG = -1, /* bad shape, range, type, scale or softcap */
+  FFA_ERR_UNSUPPORTED = -2, /* valid but not built (e.g. head size 96) */
+  FFA_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed */
+  FFA_ERR_NOMEM = -4        /* host or device allocation failed */
+};
+
+/*
+ * ffa_fwd -- forward pass: out and lse.
+ *
+ * Plans the block-sparse work on the host (drops empty slices, lists for each
+ * 128-row q tile the 64-column k tiles any slice makes visible, FULL or
+ * PARTIAL; FlexAttention paper summary, section 4, block sparsity and the
+ * full-block optimisation), uploads the plan on `stream`, and runs one fused
+ * kernel.  out: bf16 [Tq][hq][d], lse: fp32 [Tq][hq], both written in full
+ * (rows nothing sees included).  Deterministic: the same inputs give the
+ * same bits, also when empty slices are added anywhere or the slices are
+ * permuted.
+ */
+int ffa_fwd(const void* q, const void* k, const void* v,
+            int64_t Tq, int64_t Tk, int hq, int hkv, int d,
+            const int32_t* q_ranges, const int32_t* k_ranges,
+            const int32_t* attn_type_map, int R,
+            float scale, float softcap,
+            void* out, float* lse,
+            void* stream);
+
+/*
+ * ffa_bwd_workspace_size -- bytes of device workspace ffa_bwd needs
+ * (the fp32 row term D = rowsum(dO * out), [Tq][hq]).
+ */
+size_t ffa_bwd_workspace_size(int64_t Tq, int hq);
+
+/*
+ * ffa_bwd -- backward pass of ffa_fwd for upstream gradient `dout`.
+ *
+ * Inputs q, k, v, out (bf16) and lse (fp32) are those of the forward call
+ * with the same slices, scale and softcap.  Writes dq [Tq][hq][d] and dk, dv
+ * [Tk][hkv][d] (bf16) in full, zeros where a row or key takes part in no
+ * visible cell.  dk and dv of a kv head sum over the q heads that read it.
+ * `workspace` is device memory of ffa_bwd_workspace_size(Tq, hq) bytes
+ * (or NULL: then the library allocates it on `stream`).  Deterministic.
+ */
+int ffa_bwd(const void* q, const void* k, const void* v,
+            const void* out, const float* lse, const void* dout,
+            int64_t Tq, int64_t Tk, int hq, int hkv, int d,
+            const int32_t* q_ranges, const int32_t* k_ranges,
+            const int32_t* attn_type_map, int R,
+            float scale, float softcap,
+            void* dq, void* dk, void* dv,
+            void* workspace, size_t workspace_bytes,
+            void* stream);
+
+/*
+ * ffa_plan_host -- the block-sparse plan, on the host only (no GPU call).
+ *
+ * For tiles of bm query rows by bn key columns, lists every (tile, other
+ * tile, slice) triple where slice r makes at least one cell visible.  With
+ * transpose == 0 the tiles are q tiles and the other tiles k tiles (the
+ * forward's list); with transpose == 1 it is the reverse (the key-side list
+ * the backward walks).  Kind 0 (FULL) means slice r makes every cell of the
+ * whole bm x bn tile visible, kind 1 (PARTIAL) means the kernel must mask.
+ * Empty slices are dropped; r indexes the caller's slice list.
+ *
+ * row_ptr    [n_tiles + 1] CSR offsets (may be NULL)
+ * entries    [cap][3] int32 (other_tile, r, kind), sorted within each tile
+ *            by other_tile and then by the slice's bounds (may be NULL)
+ * order      [n_tiles] tiles by descending entry count (may be NULL)
+ * Returns the number of entries (>= 0, even when cap is too small: call with
+ * cap = 0 to size the buffers) or a negative FFA_ERR_*.
+ */
+int64_t ffa_plan_host(int64_t Tq, int64_t Tk,
+                      const int32_t* q_ranges, const int32_t* k_ranges,
+                      const int32_t* attn_type_map, int R,
+                      int bm, int bn, int transpose,
+                      int64_t* row_ptr, int32_t* entries, int64_t cap,
+                      int32_t* order);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* ffa_last_error(void);
+
+/* Build facts: target architecture, tile sizes, compiler (cf. the build-flag
+ * file exposed at run time in flash-attention PR "Add torch.compile support
+ * to flash attention 3"). */
+const char* ffa_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FFA_H */

@@ -1,0 +1,256 @@
+"""Range-masked ("flex") flash attention on MI355X (gfx950).
+
+A thin ctypes binding over the C ABI in ``include/ffa.h``.  Every step of the
+computation (planning, kernels) runs in the native library; this module only
+marshals arguments: torch tensors supply device memory and the current HIP
+stream.  If the library is not built the functions raise; there is no
+fallback implementation.
+
+``flex_flash_attn_func`` mirrors the call in the MagiAttention issue "Using
+dummy/padded attention slices with flex_flash_attn_func for torch.compile
+static shapes" (q, k, v packed as [tokens, heads, head_dim]; int32 q_ranges,
+k_ranges [R, 2] and attn_type_map [R] with 0 = FULL, 1 = CAUSAL;
+softmax_scale None = 1/sqrt(head_dim); softcap 0 = off) and returns
+``(out, lse)``; it supports autograd.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+__all__ = [
+    "FULL", "CAUSAL", "FfaError", "lib_path", "load_library", "ffa_fwd", "ffa_bwd",
+    "ffa_bwd_workspace_size", "ffa_plan_host", "ffa_last_error", "ffa_build_info",
+    "flex_flash_attn_func",
+]
+
+FULL = 0
+CAUSAL = 1
+
+_STATUS = {0: "FFA_OK", -1: "FFA_ERR_INVALID_ARG", -2: "FFA_ERR_UNSUPPORTED",
+           -3: "FFA_ERR_HIP", -4: "FFA_ERR_NOMEM"}
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+class FfaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def lib_path() -> str:
+    return os.path.join(_PKG, "_lib", "libffa.so")
+
+
+def load_library():
+    """Load the native library (once).  Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    p = lib_path()
+    if not os.path.exists(p):
+        raise RuntimeError(f"native library missing: {p} (build it with "
+                           "`python -m range_masked_attention_amd._build`)")
+    lib = ctypes.CDLL(p)
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
+    ip32 = ctypes.POINTER(ctypes.c_int32)
+    lib.ffa_fwd.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, ip32, ip32, ip32, i32,
+                            f32, f32, vp, vp, vp]
+    lib.ffa_fwd.restype = ctypes.c_int
+    lib.ffa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, ip32, ip32, ip32,
+                            i32, f32, f32, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.ffa_bwd.restype = ctypes.c_int
+    lib.ffa_bwd_workspace_size.argtypes = [i64, i32]
+    lib.ffa_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.ffa_plan_host.argtypes = [i64, i64, ip32, ip32, ip32, i32, i32, i32, i32,
+                                  ctypes.POINTER(ctypes.c_int64), ip32, i64, ip32]
+    lib.ffa_plan_host.restype = ctypes.c_int64
+    lib.ffa_last_error.restype = ctypes.c_char_p
+    lib.ffa_build_info.restype = ctypes.c_char_p
+    _LIB = lib
+    return lib
+
+
+def ffa_last_error() -> str:
+    return load_library().ffa_last_error().decode()
+
+
+def ffa_build_info() -> str:
+    return load_library().ffa_build_info().decode()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise FfaError(rc, ffa_last_error())
+
+
+def _host_slices(q_ranges, k_ranges, attn_type_map):
+    """Slice arrays as contiguous host int32 (device tensors are copied: one sync)."""
+    def to_np(x, shape_tail):
+        if hasattr(x, "detach"):
+            x = x.detach().cpu().numpy()
+        a = np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+        return a.reshape((-1,) + shape_tail)
+    qr = to_np(q_ranges, (2,))
+    kr = to_np(k_ranges, (2,))
+    ty = to_np(attn_type_map, ())
+    if not (qr.shape[0] == kr.shape[0] == ty.shape[0]):
+        raise ValueError("q_ranges, k_ranges and attn_type_map must have the same number of rows")
+    return qr, kr, ty
+
+
+def _iptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _stream_handle(t) -> int:
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check_tensor(name, t, dtype, ndim):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def ffa_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, scale: float, softcap: float = 0.0,
+            out=None, lse=None):
+    """C ABI ``ffa_fwd`` on torch tensors.  Returns (out [Tq,hq,d] bf16, lse [Tq,hq] fp32)."""
+    import torch
+    lib = load_library()
+    for nm, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(nm, t, torch.bfloat16, 3)
+    Tq, hq, d = q.shape
+    Tk, hkv, _ = k.shape
+    if tuple(v.shape) != tuple(k.shape) or k.shape[2] != d:
+        raise ValueError("k and v must both be [Tk, hkv, d] with q's head_dim")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((Tq, hq), dtype=torch.float32, device=q.device)
+    _check_tensor("out", out, torch.bfloat16, 3)
+    _check_tensor("lse", lse, torch.float32, 2)
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (Tq, hq):
+        raise ValueError("out must be shaped like q and lse [Tq, hq]")
+    qr, kr, ty = _host_slices(q_ranges, k_ranges, attn_type_map)
+    rc = lib.ffa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), Tq, Tk, hq, hkv, d,
+                     _iptr(qr), _iptr(kr), _iptr(ty), qr.shape[0], float(scale), float(softcap),
+                     out.data_ptr(), lse.data_ptr(), _stream_handle(q))
+    _check(rc)
+    return out, lse
+
+
+def ffa_bwd_workspace_size(Tq: int, hq: int) -> int:
+    return int(load_library().ffa_bwd_workspace_size(Tq, hq))
+
+
+def ffa_bwd(q, k, v, out, lse, dout, q_ranges, k_ranges, attn_type_map, scale: float,
+            softcap: float = 0.0, dq=None, dk=None, dv=None, workspace=None):
+    """C ABI ``ffa_bwd`` on torch tensors.  Returns (dq, dk, dv) in bf16."""
+    import torch
+    lib = load_library()
+    for nm, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _check_tensor(nm, t, torch.bfloat16, 3)
+    _check_tensor("lse", lse, torch.float32, 2)
+    Tq, hq, d = q.shape
+    Tk, hkv, _ = k.shape
+    if tuple(out.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("out and dout must be shaped like q")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for nm, t, ref in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_tensor(nm, t, torch.bfloat16, 3)
+        if tuple(t.shape) != tuple(ref.shape):
+            raise ValueError(f"{nm} must be shaped like its input")
+    ws_bytes = ffa_bwd_workspace_size(Tq, hq)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    qr, kr, ty = _host_slices(q_ranges, k_ranges, attn_type_map)
+    rc = lib.ffa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                     dout.data_ptr(), Tq, Tk, hq, hkv, d, _iptr(qr), _iptr(kr), _iptr(ty),
+                     qr.shape[0], float(scale), float(softcap), dq.data_ptr(), dk.data_ptr(),
+                     dv.data_ptr(), ws_ptr, ws_len, _stream_handle(q))
+    _check(rc)
+    return dq, dk, dv
+
+
+def ffa_plan_host(Tq: int, Tk: int, q_ranges, k_ranges, attn_type_map, bm: int, bn: int,
+                  transpose: bool = False):
+    """C ABI ``ffa_plan_host``: (row_ptr [n+1] int64, entries [E,3] int32, order [n] int32)."""
+    lib = load_library()
+    qr, kr, ty = _host_slices(q_ranges, k_ranges, attn_type_map)
+    args = (Tq, Tk, _iptr(qr), _iptr(kr), _iptr(ty), qr.shape[0], bm, bn, int(bool(transpose)))
+    n = lib.ffa_plan_host(*args, None, None, 0, None)
+    if n < 0:
+        raise FfaError(int(n), ffa_last_error())
+    n_tiles = -(-(Tk if transpose else Tq) // (bn if transpose else bm))
+    row_ptr = np.zeros(n_tiles + 1, dtype=np.int64)
+    entries = np.zeros((max(n, 1), 3), dtype=np.int32)
+    order = np.zeros(max(n_tiles, 1), dtype=np.int32)
+    n2 = lib.ffa_plan_host(*args, row_ptr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                           _iptr(entries), n, _iptr(order))
+    if n2 != n:
+        raise FfaError(int(n2), ffa_last_error())
+    return row_ptr, entries[:n], order[:n_tiles]
+
+
+def _autograd_fn():
+    import torch
+
+    class _FlexAttn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, qr, kr, ty, scale, softcap):
+            out, lse = ffa_fwd(q, k, v, qr, kr, ty, scale, softcap)
+            ctx.save_for_backward(q, k, v, out, lse)
+            ctx.slices = (qr, kr, ty)
+            ctx.scale, ctx.softcap = scale, softcap
+            ctx.mark_non_differentiable(lse)
+            return out, lse
+
+        @staticmethod
+        def backward(ctx, dout, dlse):
+            q, k, v, out, lse = ctx.saved_tensors
+            dq, dk, dv = ffa_bwd(q, k, v, out, lse, dout.contiguous(), *ctx.slices,
+                                 ctx.scale, ctx.softcap)
+            return dq, dk, dv, None, None, None, None, None
+
+    return _FlexAttn
+
+
+_FN = None
+
+
+def flex_flash_attn_func(q, k, v, q_ranges, k_ranges, attn_type_map,
+                         max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
+                         softmax_scale: Optional[float] = None, softcap: float = 0.0):
+    """Range-masked attention with autograd.  Returns (out, lse).
+
+    ``max_seqlen_q`` / ``max_seqlen_k`` are accepted for call compatibility and
+    unused: the host planner derives the tiling from the ranges themselves.
+    Slice tensors on the GPU are copied to the host (one synchronisation).
+    """
+    global _FN
+    if _FN is None:
+        _FN = _autograd_fn()
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(q.shape[-1])
+    qr, kr, ty = _host_slices(q_ranges, k_ranges, attn_type_map)
+    return _FN.apply(q, k, v, qr, kr, ty, float(softmax_scale), float(softcap))

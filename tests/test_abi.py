@@ -1,0 +1,98 @@
+"""The C ABI: the library loads, exports what include/ffa.h declares, and
+rejects bad arguments before any GPU work (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from _lib import ROOT, ensure_built, ffa
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ensure_built()
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "ffa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ffa_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert {"ffa_fwd", "ffa_bwd", "ffa_bwd_workspace_size", "ffa_plan_host",
+            "ffa_last_error", "ffa_build_info"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    # the python binding carries the same names
+    for n in names:
+        assert hasattr(ffa, n), n
+
+
+def test_build_info(lib):
+    info = ffa.ffa_build_info()
+    assert "gfx950" in info and "128x64" in info
+
+
+def _fwd(lib, Tq=16, Tk=16, hq=2, hkv=1, d=64, qr=((0, 16),), kr=((0, 16),), ty=(0,),
+         scale=0.125, softcap=0.0, ptr=64):
+    qr = np.ascontiguousarray(np.asarray(qr, np.int32).reshape(-1, 2))
+    kr = np.ascontiguousarray(np.asarray(kr, np.int32).reshape(-1, 2))
+    ty = np.ascontiguousarray(np.asarray(ty, np.int32).reshape(-1))
+    ip = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    # pointers are never dereferenced: every case fails validation (or Tq == 0)
+    return lib.ffa_fwd(ptr, ptr, ptr, Tq, Tk, hq, hkv, d, ip(qr), ip(kr), ip(ty), qr.shape[0],
+                       scale, softcap, ptr, ptr, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(hq=3, hkv=2), -1, "multiple"),
+    (dict(hkv=0), -1, "positive"),
+    (dict(d=96), -2, "96"),
+    (dict(scale=0.0), -1, "scale"),
+    (dict(scale=float("nan")), -1, "scale"),
+    (dict(softcap=-1.0), -1, "softcap"),
+    (dict(softcap=float("inf")), -1, "softcap"),
+    (dict(qr=((5, 3),)), -1, "q range"),
+    (dict(kr=((0, 17),)), -1, "k range"),
+    (dict(qr=((-1, 3),)), -1, "q range"),
+    (dict(ty=(2,)), -1, "type"),
+    (dict(Tq=-1), -1, ">= 0"),
+    (dict(Tq=1 << 30, hq=2, d=64), -1, "2^31"),
+])
+def test_invalid_arguments(lib, kw, code, msg):
+    rc = _fwd(lib, **kw)
+    assert rc == code
+    assert msg in ffa.ffa_last_error()
+
+
+def test_null_pointers_rejected(lib):
+    assert _fwd(lib, ptr=None) == -1
+    assert "NULL" in ffa.ffa_last_error()
+
+
+def test_empty_query_axis_is_a_no_op(lib):
+    # nothing to compute: returns before any HIP call
+    assert _fwd(lib, Tq=0, qr=((0, 0),)) == 0
+
+
+def test_overlap_rejected_in_debug_mode(lib, monkeypatch):
+    monkeypatch.setenv("FFA_DEBUG", "1")
+    assert _fwd(lib, qr=((0, 16), (4, 8)), kr=((0, 16), (3, 5)), ty=(0, 1), ptr=None) == -1
+    assert "same cells" in ffa.ffa_last_error()
+    # disjoint slices (causal triangles that never meet) pass the debug check and then
+    # fail only on the NULL pointers
+    assert _fwd(lib, qr=((0, 8), (8, 16)), kr=((0, 8), (0, 16)), ty=(1, 1), ptr=None) == -1
+    assert "NULL" in ffa.ffa_last_error()
+
+
+def test_bwd_validation(lib):
+    ip = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    qr = np.array([[0, 4]], np.int32); kr = np.array([[0, 9]], np.int32); ty = np.array([1], np.int32)
+    rc = lib.ffa_bwd(64, 64, 64, 64, 64, 64, 4, 8, 2, 2, 64, ip(qr), ip(kr), ip(ty), 1,
+                     0.1, 0.0, 64, 64, 64, None, 0, None)
+    assert rc == -1 and "k range" in ffa.ffa_last_error()
+    assert lib.ffa_bwd_workspace_size(100, 8) == 100 * 8 * 4

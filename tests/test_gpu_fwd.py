@@ -1,0 +1,189 @@
+"""Forward parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small configurations are compared element by element over the whole output;
+the full-size configurations on sampled rows (the oracle computes those rows
+one block at a time) plus properties that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from gpu_util import (LSE_TOL, OUT_TOL, O, compare_out_lse, dev, ffa, run_fwd, sample_rows, say,
+                      to64)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("n", [1, 2])
+def test_config_full_compare(n):
+    w = W.config(n)
+    say(f"fwd full compare config {n} ({w.name})")
+    q, k, v, _ = W.workload_tensors(w, with_dout=False)
+    qr, kr, ty = w.slices()
+    out, lse = run_fwd(q, k, v, qr, kr, ty, w.scale, w.softcap, dev())
+    ref_out, ref_lse = O.attention_fwd(to64(q), to64(k), to64(v), qr, kr, ty, w.scale, w.softcap)
+    e_out, e_lse = compare_out_lse(out.cpu(), lse.cpu(), ref_out, ref_lse, f"config {n}")
+    say(f"  out max-abs {e_out:.3e}  lse max-abs {e_lse:.3e}")
+
+
+@pytest.mark.parametrize("n", [3, 4, 5])
+def test_config_sampled_rows(n):
+    w = W.config(n)
+    say(f"fwd sampled-row compare config {n} ({w.name}) at full size")
+    q, k, v, _ = W.workload_tensors(w, with_dout=False)
+    qr, kr, ty = w.slices()
+    out, lse = run_fwd(q, k, v, qr, kr, ty, w.scale, w.softcap, dev())
+    # properties over the whole output: finite, every row of these configs
+    # sees a key, and each output row is a convex combination of v rows
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    vmax = v.float().abs().amax().item()
+    assert out.float().abs().amax().item() <= vmax + OUT_TOL
+    rng = np.random.default_rng(n)
+    edges = [int(a) for a in np.asarray(qr)[:, 0]] + [int(b) - 1 for b in np.asarray(qr)[:, 1] if b > 0]
+    rows = sample_rows(w.Tq, rng, n=160, extra=tuple(edges))
+    ref_out, ref_lse = O.attention_fwd(to64(q), to64(k), to64(v), qr, kr, ty, w.scale, w.softcap,
+                                       rows=rows)
+    e_out, e_lse = compare_out_lse(out[rows].cpu(), lse[rows].cpu(), ref_out, ref_lse, f"config {n}")
+    say(f"  {len(rows)} rows: out max-abs {e_out:.3e}  lse max-abs {e_lse:.3e}")
+
+
+CASES = [
+    # (Tq, Tk, hq, hkv, d, softcap, seed): ragged tails, GQA ratios, both head sizes
+    (300, 300, 2, 1, 64, 0.0, 0),
+    (257, 190, 4, 2, 128, 0.0, 1),
+    (520, 700, 4, 4, 128, 30.0, 2),
+    (129, 65, 8, 1, 64, 5.0, 3),
+    (1000, 1000, 2, 2, 128, 0.0, 4),
+    (64, 64, 1, 1, 64, 0.0, 5),
+    (1, 1, 1, 1, 128, 0.0, 6),
+    (3, 700, 2, 1, 64, 0.0, 7),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"T{c[0]}x{c[1]}_h{c[2]}:{c[3]}_d{c[4]}_cap{c[5]}" for c in CASES])
+def test_random_slices_full_compare(case):
+    Tq, Tk, hq, hkv, d, cap, seed = case
+    say(f"fwd random slices {case}")
+    rng = np.random.default_rng(seed)
+    for trial in range(3):
+        qr, kr, ty = W.random_slices(rng, Tq, Tk, max_slices=6, n_dummies=2)
+        q, k, v, _ = W.make_tensors(Tq, Tk, hq, hkv, d, seed=seed * 10 + trial, with_dout=False)
+        scale = float(rng.uniform(0.05, 0.3))
+        out, lse = run_fwd(q, k, v, qr, kr, ty, scale, cap, dev())
+        ref_out, ref_lse = O.attention_fwd(to64(q), to64(k), to64(v), qr, kr, ty, scale, cap)
+        compare_out_lse(out.cpu(), lse.cpu(), ref_out, ref_lse, f"{case} trial {trial}")
+
+
+def test_short_key_range_causal_rows_empty():
+    say("fwd causal slice with Lk < Lq")
+    q, k, v, _ = W.make_tensors(300, 100, 2, 1, 128, seed=11, with_dout=False)
+    qr, kr, ty = [[0, 300]], [[0, 100]], [1]
+    out, lse = run_fwd(q, k, v, qr, kr, ty, 0.1, 0.0, dev())
+    ref_out, ref_lse = O.attention_fwd(to64(q), to64(k), to64(v), qr, kr, ty, 0.1, 0.0)
+    compare_out_lse(out.cpu(), lse.cpu(), ref_out, ref_lse, "Lk<Lq")
+    assert torch.all(lse[:200] == float("-inf")) and torch.all(out[:200] == 0)
+
+
+@pytest.mark.parametrize("slices", [
+    (np.zeros((0, 2)), np.zeros((0, 2)), np.zeros(0)),
+    (np.zeros((5, 2)), np.zeros((5, 2)), np.ones(5)),
+    ([[7, 7], [0, 300]], [[0, 300], [9, 9]], [0, 1]),
+], ids=["no_slices", "all_dummies", "both_dummy_kinds"])
+def test_nothing_visible(slices):
+    say(f"fwd nothing visible")
+    q, k, v, _ = W.make_tensors(300, 300, 2, 1, 64, seed=12, with_dout=False)
+    d = dev()
+    out = torch.full((300, 2, 64), 7.0, dtype=torch.bfloat16, device=d)
+    lse = torch.full((300, 2), 7.0, dtype=torch.float32, device=d)
+    ffa.ffa_fwd(q.to(d), k.to(d), v.to(d), *slices, 0.1, 0.0, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0) and torch.all(lse == float("-inf"))
+
+
+def test_dummy_padding_bitwise():
+    """The repro script's check: padded (R_max=20) vs unpadded slices, 0.0 max rel diff."""
+    w = W.config(2)
+    say("fwd dummy padding bitwise (config 2)")
+    q, k, v, _ = W.workload_tensors(w, with_dout=False)
+    d = dev()
+    qd, kd, vd = q.to(d), k.to(d), v.to(d)
+    o0, l0 = ffa.ffa_fwd(qd, kd, vd, *w.slices(padded=False), w.scale, 0.0)
+    o1, l1 = ffa.ffa_fwd(qd, kd, vd, *w.slices(padded=True), w.scale, 0.0)
+    # dummies in front, either kind, and the real slices swapped
+    qr, kr, ty = w.slices(padded=False)
+    qx = np.concatenate([[[5, 5], [0, 2048]], qr[::-1]])
+    kx = np.concatenate([[[0, 2048], [100, 100]], kr[::-1]])
+    tx = np.concatenate([[1, 0], ty[::-1]])
+    o2, l2 = ffa.ffa_fwd(qd, kd, vd, qx, kx, tx, w.scale, 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)
+    assert torch.equal(o0, o2) and torch.equal(l0, l2)
+
+
+def test_run_twice_bitwise():
+    w = W.config(3)
+    say("fwd determinism (config 3, twice)")
+    q, k, v, _ = W.workload_tensors(w, with_dout=False)
+    d = dev()
+    qd, kd, vd = q.to(d), k.to(d), v.to(d)
+    a = ffa.ffa_fwd(qd, kd, vd, *w.slices(), w.scale, 0.0)
+    b = ffa.ffa_fwd(qd, kd, vd, *w.slices(), w.scale, 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_guard_band():
+    """Tensors inside NaN-filled allocations: no read past the ends leaks in,
+    no write lands outside, results match the unguarded run bitwise."""
+    say("fwd guard band")
+    Tq, Tk, hq, hkv, dd = 333, 251, 4, 2, 128
+    q, k, v, _ = W.make_tensors(Tq, Tk, hq, hkv, dd, seed=21, with_dout=False)
+    qr, kr, ty = [[0, 200], [200, 333], [200, 333]], [[0, 251], [0, 30], [40, 251]], [1, 0, 1]
+    d = dev()
+    G = 4096
+
+    def guarded(t, dtype=torch.bfloat16):
+        n = t.numel()
+        buf = torch.full((n + 2 * G,), float("nan"), dtype=dtype, device=d)
+        view = buf[G:G + n].view(t.shape)
+        view.copy_(t.to(d))
+        return buf, view
+
+    bq, gq = guarded(q)
+    bk, gk = guarded(k)
+    bv, gv = guarded(v)
+    bo, go = guarded(torch.zeros(Tq, hq, dd))
+    bl, gl = guarded(torch.zeros(Tq, hq), torch.float32)
+    ffa.ffa_fwd(gq, gk, gv, qr, kr, ty, 0.09, 0.0, out=go, lse=gl)
+    ro, rl = ffa.ffa_fwd(q.to(d), k.to(d), v.to(d), qr, kr, ty, 0.09, 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(go, ro) and torch.equal(gl, rl)
+    for buf in (bo, bl):
+        assert torch.isnan(buf[:G].float()).all() and torch.isnan(buf[-G:].float()).all()
+
+
+def test_flex_flash_attn_func_api():
+    """The pages' call shape: slice tensors on the device, max_seqlen args, default scale."""
+    w = W.config(2)
+    say("flex_flash_attn_func API")
+    q, k, v, _ = W.workload_tensors(w, with_dout=False)
+    d = dev()
+    qr, kr, ty = (torch.from_numpy(x).to(d) for x in w.slices())
+    out, lse = ffa.flex_flash_attn_func(q.to(d), k.to(d), v.to(d), qr, kr, ty,
+                                        max_seqlen_q=w.Tq, max_seqlen_k=w.Tk,
+                                        softmax_scale=None, softcap=0)
+    ref, ref_lse = ffa.ffa_fwd(q.to(d), k.to(d), v.to(d), *w.slices(), w.scale, 0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref) and torch.equal(lse, ref_lse)
+
+
+def test_invalid_tensor_arguments_raise():
+    d = dev()
+    q = torch.zeros(16, 2, 64, dtype=torch.bfloat16, device=d)
+    with pytest.raises(TypeError):
+        ffa.ffa_fwd(q.float(), q, q, [[0, 16]], [[0, 16]], [0], 0.1)
+    with pytest.raises(ValueError):
+        ffa.ffa_fwd(q.transpose(0, 1), q, q, [[0, 16]], [[0, 16]], [0], 0.1)
+    with pytest.raises(ffa.FfaError, match="q range"):
+        ffa.ffa_fwd(q, q, q, [[0, 17]], [[0, 16]], [0], 0.1)
