@@ -34,6 +34,7 @@
  *  - d is 64 or 128; hq is a positive multiple of hkv; scale > 0 and finite;
  *    softcap >= 0 and finite (0 = off).  Tq, Tk >= 0 and every tensor must be
  *    below 2^31 elements.
+ *  - Device pointers must be 16-byte aligned.
  *  - stream is a hipStream_t (NULL = the default stream).  Calls enqueue work
  *    and return; argument errors are reported synchronously before any GPU
  *    work is enqueued.  The return value is FFA_OK or a negative FFA_ERR_*;
@@ -131,6 +132,44 @@ int64_t ffa_plan_host(int64_t Tq, int64_t Tk,
                       int bm, int bn, int transpose,
                       int64_t* row_ptr, int32_t* entries, int64_t cap,
                       int32_t* order);
+
+/*
+ * Plans that outlive one call.  A plan depends only on Tq, Tk and the slice
+ * list (not on heads, head size, scale or data), so callers whose layers
+ * share one mask plan once and launch many times.
+ */
+typedef struct ffa_plan_s* ffa_plan_t;
+
+/*
+ * ffa_plan_create -- validate the slices, build the forward (per q tile) and
+ * backward (per key tile) block lists on the host and copy them to device
+ * memory on `stream`.  *plan receives the handle.  Use the plan on `stream`
+ * (or after synchronising with it).  Errors as for ffa_fwd.
+ */
+int ffa_plan_create(int64_t Tq, int64_t Tk,
+                    const int32_t* q_ranges, const int32_t* k_ranges,
+                    const int32_t* attn_type_map, int R,
+                    void* stream, ffa_plan_t* plan);
+
+/* ffa_fwd with a plan from ffa_plan_create: launches the forward kernel only
+ * (no host planning, no copy, no allocation).  Tensors as for ffa_fwd. */
+int ffa_fwd_planned(ffa_plan_t plan,
+                    const void* q, const void* k, const void* v,
+                    int hq, int hkv, int d, float scale, float softcap,
+                    void* out, float* lse, void* stream);
+
+/* ffa_bwd with a plan from ffa_plan_create: launches the backward kernels
+ * only.  With workspace == NULL it allocates one on `stream`. */
+int ffa_bwd_planned(ffa_plan_t plan,
+                    const void* q, const void* k, const void* v,
+                    const void* out, const float* lse, const void* dout,
+                    int hq, int hkv, int d, float scale, float softcap,
+                    void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Release a plan: its device memory is freed in order on `stream`, after the
+ * work already enqueued there.  NULL is a no-op. */
+int ffa_plan_destroy(ffa_plan_t plan, void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* ffa_last_error(void);

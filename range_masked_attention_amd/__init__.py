@@ -25,6 +25,7 @@ import numpy as np
 __all__ = [
     "FULL", "CAUSAL", "FfaError", "lib_path", "load_library", "ffa_fwd", "ffa_bwd",
     "ffa_bwd_workspace_size", "ffa_plan_host", "ffa_last_error", "ffa_build_info",
+    "ffa_plan_create", "ffa_fwd_planned", "ffa_bwd_planned", "ffa_plan_destroy",
     "flex_flash_attn_func",
 ]
 
@@ -71,6 +72,15 @@ def load_library():
     lib.ffa_plan_host.argtypes = [i64, i64, ip32, ip32, ip32, i32, i32, i32, i32,
                                   ctypes.POINTER(ctypes.c_int64), ip32, i64, ip32]
     lib.ffa_plan_host.restype = ctypes.c_int64
+    lib.ffa_plan_create.argtypes = [i64, i64, ip32, ip32, ip32, i32, vp, ctypes.POINTER(vp)]
+    lib.ffa_plan_create.restype = ctypes.c_int
+    lib.ffa_fwd_planned.argtypes = [vp, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp, vp]
+    lib.ffa_fwd_planned.restype = ctypes.c_int
+    lib.ffa_bwd_planned.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, f32,
+                                    vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.ffa_bwd_planned.restype = ctypes.c_int
+    lib.ffa_plan_destroy.argtypes = [vp, vp]
+    lib.ffa_plan_destroy.restype = ctypes.c_int
     lib.ffa_last_error.restype = ctypes.c_char_p
     lib.ffa_build_info.restype = ctypes.c_char_p
     _LIB = lib
@@ -210,6 +220,71 @@ def ffa_plan_host(Tq: int, Tk: int, q_ranges, k_ranges, attn_type_map, bm: int, 
     if n2 != n:
         raise FfaError(int(n2), ffa_last_error())
     return row_ptr, entries[:n], order[:n_tiles]
+
+
+def ffa_plan_create(Tq: int, Tk: int, q_ranges, k_ranges, attn_type_map, device=None) -> int:
+    """C ABI ``ffa_plan_create`` on the current stream of ``device``; returns the handle."""
+    import torch
+    lib = load_library()
+    qr, kr, ty = _host_slices(q_ranges, k_ranges, attn_type_map)
+    dev_ = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    h = ctypes.c_void_p()
+    rc = lib.ffa_plan_create(Tq, Tk, _iptr(qr), _iptr(kr), _iptr(ty), qr.shape[0],
+                             torch.cuda.current_stream(dev_).cuda_stream, ctypes.byref(h))
+    _check(rc)
+    return h.value
+
+
+def ffa_plan_destroy(plan, device=None) -> None:
+    """C ABI ``ffa_plan_destroy`` (stream-ordered on the current stream)."""
+    import torch
+    if plan is None:
+        return
+    dev_ = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    _check(load_library().ffa_plan_destroy(plan, torch.cuda.current_stream(dev_).cuda_stream))
+
+
+def ffa_fwd_planned(plan, q, k, v, scale: float, softcap: float = 0.0, out=None, lse=None):
+    """C ABI ``ffa_fwd_planned``: the forward kernel alone, on a prepared plan."""
+    import torch
+    lib = load_library()
+    for nm, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(nm, t, torch.bfloat16, 3)
+    Tq, hq, d = q.shape
+    hkv = k.shape[1]
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((Tq, hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_tensor("out", out, torch.bfloat16, 3)
+    _check_tensor("lse", lse, torch.float32, 2)
+    _check(lib.ffa_fwd_planned(plan, q.data_ptr(), k.data_ptr(), v.data_ptr(), hq, hkv, d,
+                               float(scale), float(softcap), out.data_ptr(), lse.data_ptr(),
+                               _stream_handle(q)))
+    return out, lse
+
+
+def ffa_bwd_planned(plan, q, k, v, out, lse, dout, scale: float, softcap: float = 0.0,
+                    dq=None, dk=None, dv=None, workspace=None):
+    """C ABI ``ffa_bwd_planned``: the backward kernels alone, on a prepared plan."""
+    import torch
+    lib = load_library()
+    for nm, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        _check_tensor(nm, t, torch.bfloat16, 3)
+    _check_tensor("lse", lse, torch.float32, 2)
+    Tq, hq, d = q.shape
+    hkv = k.shape[1]
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    ws_bytes = ffa_bwd_workspace_size(Tq, hq)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.ffa_bwd_planned(plan, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               lse.data_ptr(), dout.data_ptr(), hq, hkv, d, float(scale),
+                               float(softcap), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                               ws_ptr, ws_len, _stream_handle(q)))
+    return dq, dk, dv
 
 
 def _autograd_fn():

@@ -4,10 +4,12 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <new>
 #include <string>
 #include <vector>
 
@@ -33,70 +35,71 @@ bool debug_checks() {
 }
 
 // ---------------------------------------------------------------- validation
-struct Shape {
-  int64_t Tq, Tk;
-  int hq, hkv, d;
-};
-
-std::string check_shape(const Shape& s, float scale, float softcap) {
-  if (s.Tq < 0 || s.Tk < 0) return "Tq and Tk must be >= 0";
-  if (s.hq <= 0 || s.hkv <= 0) return "hq and hkv must be positive";
-  if (s.hq % s.hkv != 0) return "hq must be a multiple of hkv";
-  if (s.d <= 0) return "d must be positive";
-  const int64_t lim = int64_t(1) << 31;
-  if (s.Tq * s.hq * int64_t(s.d) >= lim || s.Tk * s.hkv * int64_t(s.d) >= lim)
-    return "tensors must have fewer than 2^31 elements";
-  if (!(std::isfinite(scale) && scale > 0.f)) return "scale must be finite and > 0";
-  if (!(std::isfinite(softcap) && softcap >= 0.f)) return "softcap must be finite and >= 0";
+std::string check_sizes(int64_t Tq, int64_t Tk) {
+  if (Tq < 0 || Tk < 0) return "Tq and Tk must be >= 0";
+  if (Tq >= (int64_t(1) << 31) || Tk >= (int64_t(1) << 31)) return "token counts must be below 2^31";
   return "";
 }
 
-int check_common(const Shape& sh, float scale, float softcap, const int32_t* qr, const int32_t* kr,
-                 const int32_t* ty, int R, std::vector<ffa::Slice>* slices) {
-  std::string m = check_shape(sh, scale, softcap);
-  if (!m.empty()) return fail(FFA_ERR_INVALID_ARG, m);
-  if (sh.d != 64 && sh.d != 128)
-    return fail(FFA_ERR_UNSUPPORTED, "head size " + std::to_string(sh.d) + " is not built (64, 128)");
-  m = ffa::validate_slices(sh.Tq, sh.Tk, qr, kr, ty, R, slices);
+int check_heads(int64_t Tq, int64_t Tk, int hq, int hkv, int d, float scale, float softcap) {
+  if (hq <= 0 || hkv <= 0) return fail(FFA_ERR_INVALID_ARG, "hq and hkv must be positive");
+  if (hq % hkv != 0) return fail(FFA_ERR_INVALID_ARG, "hq must be a multiple of hkv");
+  if (d <= 0) return fail(FFA_ERR_INVALID_ARG, "d must be positive");
+  const int64_t lim = int64_t(1) << 31;
+  if (Tq * hq * int64_t(d) >= lim || Tk * hkv * int64_t(d) >= lim)
+    return fail(FFA_ERR_INVALID_ARG, "tensors must have fewer than 2^31 elements");
+  if (!(std::isfinite(scale) && scale > 0.f)) return fail(FFA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (!(std::isfinite(softcap) && softcap >= 0.f))
+    return fail(FFA_ERR_INVALID_ARG, "softcap must be finite and >= 0");
+  if (d != 64 && d != 128)
+    return fail(FFA_ERR_UNSUPPORTED, "head size " + std::to_string(d) + " is not built (64, 128)");
+  return FFA_OK;
+}
+
+// Device pointers must be non-NULL when their tensor is non-empty and
+// 16-byte aligned (the kernels move 16-byte vectors).
+int check_ptr(const void* p, bool needed, const char* name) {
+  if (!needed) return FFA_OK;
+  if (!p) return fail(FFA_ERR_INVALID_ARG, std::string(name) + " must not be NULL");
+  if (reinterpret_cast<uintptr_t>(p) & 15)
+    return fail(FFA_ERR_INVALID_ARG, std::string(name) + " must be 16-byte aligned");
+  return FFA_OK;
+}
+
+// Slice list checks (plus the overlap scan when FFA_DEBUG is set).
+int check_slices(int64_t Tq, int64_t Tk, const int32_t* qr, const int32_t* kr, const int32_t* ty, int R) {
+  std::vector<ffa::Slice> slices;
+  std::string m = ffa::validate_slices(Tq, Tk, qr, kr, ty, R, &slices);
   if (!m.empty()) return fail(FFA_ERR_INVALID_ARG, m);
   if (debug_checks()) {
-    m = ffa::check_disjoint(*slices);
+    m = ffa::check_disjoint(slices);
     if (!m.empty()) return fail(FFA_ERR_INVALID_ARG, m);
   }
   return FFA_OK;
 }
 
 // ---------------------------------------------------------------- plan upload
-// A plan is packed into one host image, copied through a pinned staging
-// slot, and read by the kernels from one stream-ordered device allocation.
-struct PlanImage {
-  std::vector<unsigned char> bytes;
-  size_t off_row_ptr = 0, off_entries = 0, off_order = 0, off_slices = 0;
+struct PlanPart {
+  size_t off_row_ptr = 0, off_entries = 0, off_order = 0;
+  int64_t n_tiles = 0;
 };
 
 size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
 
-std::string pack_plan(const ffa::Plan& plan, const std::vector<ffa::Slice>& slices, PlanImage* img) {
-  if (plan.entries.size() >= (size_t(1) << 31)) return "plan has too many entries";
+void append_part(const ffa::Plan& plan, std::vector<unsigned char>* img, PlanPart* part) {
   const size_t n_rp = plan.row_ptr.size(), n_e = plan.entries.size(), n_o = plan.order.size();
-  img->off_row_ptr = 0;
-  img->off_entries = align16(n_rp * 4);
-  img->off_order = img->off_entries + align16(n_e * sizeof(ffa::HostDevEntry));
-  img->off_slices = img->off_order + align16(n_o * 4);
-  const size_t total = img->off_slices + align16((slices.size() + 1) * sizeof(ffa::HostDevSlice));
-  img->bytes.assign(total, 0);
-  auto* rp = reinterpret_cast<int32_t*>(img->bytes.data() + img->off_row_ptr);
+  part->n_tiles = plan.n_tiles;
+  part->off_row_ptr = img->size();
+  part->off_entries = part->off_row_ptr + align16(n_rp * 4);
+  part->off_order = part->off_entries + align16(n_e * sizeof(ffa::HostDevEntry));
+  img->resize(part->off_order + align16(std::max<size_t>(n_o, 1) * 4), 0);
+  auto* rp = reinterpret_cast<int32_t*>(img->data() + part->off_row_ptr);
   for (size_t i = 0; i < n_rp; ++i) rp[i] = static_cast<int32_t>(plan.row_ptr[i]);
-  auto* en = reinterpret_cast<ffa::HostDevEntry*>(img->bytes.data() + img->off_entries);
+  auto* en = reinterpret_cast<ffa::HostDevEntry*>(img->data() + part->off_entries);
   for (size_t i = 0; i < n_e; ++i)
     en[i] = ffa::HostDevEntry{plan.entries[i].other, (plan.entries[i].slice << 1) | plan.entries[i].kind};
-  auto* od = reinterpret_cast<int32_t*>(img->bytes.data() + img->off_order);
+  auto* od = reinterpret_cast<int32_t*>(img->data() + part->off_order);
   for (size_t i = 0; i < n_o; ++i) od[i] = plan.order[i];
-  auto* sl = reinterpret_cast<ffa::HostDevSlice*>(img->bytes.data() + img->off_slices);
-  for (size_t i = 0; i < slices.size(); ++i)
-    sl[i] = ffa::HostDevSlice{slices[i].qs, slices[i].qe, slices[i].ks, slices[i].ke,
-                              slices[i].type == ffa::kCausal ? 1 : 0, 0, 0, 0};
-  return "";
 }
 
 struct StageSlot {
@@ -155,23 +158,157 @@ int upload(const void* src, size_t bytes, void* dst, hipStream_t stream) {
   return FFA_OK;
 }
 
-// Device copy of a plan image; freed on the stream after the kernels.
-struct DevicePlan {
-  unsigned char* base = nullptr;
-  hipStream_t stream = nullptr;
-  ~DevicePlan() {
-    if (base) (void)hipFreeAsync(base, stream);
-  }
+enum : int { kWantFwd = 1, kWantBwd = 2 };
+
+}  // namespace
+
+// The plan handle: sizes, the non-empty slices and the device copy of the
+// block-sparse lists.
+struct ffa_plan_s {
+  int64_t Tq = 0, Tk = 0;
+  int want = 0;
+  size_t n_slices = 0;
+  size_t off_slices = 0;
+  PlanPart fwd, kv;  // kv: per key tile (dK/dV); the dQ pass walks `fwd`
+  unsigned char* dev = nullptr;
+  size_t bytes = 0;
 };
 
-int stage_plan(const PlanImage& img, hipStream_t stream, DevicePlan* dp) {
-  dp->stream = stream;
-  hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&dp->base), img.bytes.size(), stream);
+namespace {
+
+int plan_create(int64_t Tq, int64_t Tk, const int32_t* qr, const int32_t* kr, const int32_t* ty,
+                int R, int want, hipStream_t stream, ffa_plan_s** out) {
+  *out = nullptr;
+  std::string m = check_sizes(Tq, Tk);
+  if (!m.empty()) return fail(FFA_ERR_INVALID_ARG, m);
+  std::vector<ffa::Slice> slices;
+  m = ffa::validate_slices(Tq, Tk, qr, kr, ty, R, &slices);
+  if (!m.empty()) return fail(FFA_ERR_INVALID_ARG, m);
+  if (debug_checks()) {
+    m = ffa::check_disjoint(slices);
+    if (!m.empty()) return fail(FFA_ERR_INVALID_ARG, m);
+  }
+  // the dQ pass reuses the forward's per-q-tile list
+  if (ffa::bwd_q_tile_rows() != ffa::fwd_tile_rows() || ffa::bwd_q_tile_cols() != ffa::fwd_tile_cols())
+    return fail(FFA_ERR_UNSUPPORTED, "dQ tiles differ from forward tiles");
+
+  ffa_plan_s* p = new (std::nothrow) ffa_plan_s;
+  if (!p) return fail(FFA_ERR_NOMEM, "out of host memory");
+  p->Tq = Tq;
+  p->Tk = Tk;
+  p->want = want;
+  p->n_slices = slices.size();
+  std::vector<unsigned char> img;
+  try {
+    img.resize(align16((slices.size() + 1) * sizeof(ffa::HostDevSlice)), 0);
+    auto* sl = reinterpret_cast<ffa::HostDevSlice*>(img.data());
+    for (size_t i = 0; i < slices.size(); ++i)
+      sl[i] = ffa::HostDevSlice{slices[i].qs, slices[i].qe, slices[i].ks, slices[i].ke,
+                                slices[i].type == ffa::kCausal ? 1 : 0, 0, 0, 0};
+    ffa::Plan plan;
+    ffa::build_plan(slices, Tq, Tk, ffa::fwd_tile_rows(), ffa::fwd_tile_cols(), false, &plan);
+    if (plan.entries.size() >= (size_t(1) << 30)) {
+      delete p;
+      return fail(FFA_ERR_UNSUPPORTED, "plan has too many entries");
+    }
+    append_part(plan, &img, &p->fwd);
+    if (want & kWantBwd) {
+      ffa::build_plan(slices, Tq, Tk, ffa::bwd_kv_tile_rows(), ffa::bwd_kv_tile_cols(), true, &plan);
+      append_part(plan, &img, &p->kv);
+    }
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return fail(FFA_ERR_NOMEM, "out of host memory while planning");
+  }
+  p->bytes = img.size();
+  hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&p->dev), p->bytes, stream);
   if (e != hipSuccess) {
-    dp->base = nullptr;
+    delete p;
     return fail(FFA_ERR_NOMEM, std::string("hipMallocAsync(plan): ") + hipGetErrorString(e));
   }
-  return upload(img.bytes.data(), img.bytes.size(), dp->base, stream);
+  int rc = upload(img.data(), img.size(), p->dev, stream);
+  if (rc != FFA_OK) {
+    (void)hipFreeAsync(p->dev, stream);
+    delete p;
+    return rc;
+  }
+  *out = p;
+  return FFA_OK;
+}
+
+int plan_destroy(ffa_plan_s* p, hipStream_t stream) {
+  if (!p) return FFA_OK;
+  hipError_t e = hipSuccess;
+  if (p->dev) e = hipFreeAsync(p->dev, stream);
+  delete p;
+  if (e != hipSuccess) return hip_fail(e, "hipFreeAsync(plan)");
+  return FFA_OK;
+}
+
+int fwd_planned(const ffa_plan_s* p, const void* q, const void* k, const void* v, int hq, int hkv,
+                int d, float scale, float softcap, void* out, float* lse, hipStream_t stream) {
+  int rc = check_heads(p->Tq, p->Tk, hq, hkv, d, scale, softcap);
+  if (rc != FFA_OK) return rc;
+  const bool has_q = p->Tq > 0, has_k = p->Tk > 0;
+  if ((rc = check_ptr(q, has_q, "q")) || (rc = check_ptr(out, has_q, "out")) ||
+      (rc = check_ptr(lse, has_q, "lse")) || (rc = check_ptr(k, has_k, "k")) ||
+      (rc = check_ptr(v, has_k, "v")))
+    return rc;
+  if (p->Tq == 0) return FFA_OK;
+  ffa::FwdLaunch L;
+  L.q = q; L.k = k; L.v = v; L.out = out; L.lse = lse;
+  L.Tq = p->Tq; L.Tk = p->Tk; L.hq = hq; L.hkv = hkv; L.d = d;
+  L.scale = scale; L.softcap = softcap;
+  L.row_ptr = reinterpret_cast<const int32_t*>(p->dev + p->fwd.off_row_ptr);
+  L.entries = p->dev + p->fwd.off_entries;
+  L.order = reinterpret_cast<const int32_t*>(p->dev + p->fwd.off_order);
+  L.slices = p->dev + p->off_slices;
+  hipError_t e = ffa::launch_fwd(L, stream);
+  if (e != hipSuccess) return hip_fail(e, "forward kernel launch");
+  return FFA_OK;
+}
+
+int bwd_planned(const ffa_plan_s* p, const void* q, const void* k, const void* v, const void* out,
+                const float* lse, const void* dout, int hq, int hkv, int d, float scale, float softcap,
+                void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  if (!(p->want & kWantBwd)) return fail(FFA_ERR_INVALID_ARG, "plan was built without the backward lists");
+  int rc = check_heads(p->Tq, p->Tk, hq, hkv, d, scale, softcap);
+  if (rc != FFA_OK) return rc;
+  const bool has_q = p->Tq > 0, has_k = p->Tk > 0;
+  if ((rc = check_ptr(q, has_q, "q")) || (rc = check_ptr(out, has_q, "out")) ||
+      (rc = check_ptr(lse, has_q, "lse")) || (rc = check_ptr(dout, has_q, "dout")) ||
+      (rc = check_ptr(dq, has_q, "dq")) || (rc = check_ptr(k, has_k, "k")) ||
+      (rc = check_ptr(v, has_k, "v")) || (rc = check_ptr(dk, has_k, "dk")) ||
+      (rc = check_ptr(dv, has_k, "dv")))
+    return rc;
+  const size_t need = ffa_bwd_workspace_size(p->Tq, hq);
+  if (workspace && workspace_bytes < need)
+    return fail(FFA_ERR_INVALID_ARG, "workspace is smaller than ffa_bwd_workspace_size()");
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 15))
+    return fail(FFA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (p->Tq == 0 && p->Tk == 0) return FFA_OK;
+  void* ws = workspace;
+  if (!ws && need) {
+    hipError_t e = hipMallocAsync(&ws, need, stream);
+    if (e != hipSuccess) return fail(FFA_ERR_NOMEM, std::string("hipMallocAsync(workspace): ") + hipGetErrorString(e));
+  }
+  ffa::BwdLaunch L;
+  L.q = q; L.k = k; L.v = v; L.out = out; L.lse = lse; L.dout = dout;
+  L.dq = dq; L.dk = dk; L.dv = dv; L.dvec = static_cast<float*>(ws);
+  L.Tq = p->Tq; L.Tk = p->Tk; L.hq = hq; L.hkv = hkv; L.d = d;
+  L.scale = scale; L.softcap = softcap;
+  L.kv_row_ptr = reinterpret_cast<const int32_t*>(p->dev + p->kv.off_row_ptr);
+  L.kv_entries = p->dev + p->kv.off_entries;
+  L.kv_order = reinterpret_cast<const int32_t*>(p->dev + p->kv.off_order);
+  L.q_row_ptr = reinterpret_cast<const int32_t*>(p->dev + p->fwd.off_row_ptr);
+  L.q_entries = p->dev + p->fwd.off_entries;
+  L.q_order = reinterpret_cast<const int32_t*>(p->dev + p->fwd.off_order);
+  L.slices = p->dev + p->off_slices;
+  hipError_t e = ffa::launch_bwd(L, stream);
+  if (ws != workspace) (void)hipFreeAsync(ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
+  return FFA_OK;
 }
 
 }  // namespace
@@ -183,8 +320,9 @@ const char* ffa_last_error(void) { return g_err.c_str(); }
 const char* ffa_build_info(void) {
   static std::string info = [] {
     std::string s = "arch=gfx950 fwd_tile=" + std::to_string(ffa::fwd_tile_rows()) + "x" +
-                    std::to_string(ffa::fwd_tile_cols()) + " head_dims=64,128 softcap=tanh" +
-                    " compiler=" + __VERSION__;
+                    std::to_string(ffa::fwd_tile_cols()) + " bwd_kv_tile=" +
+                    std::to_string(ffa::bwd_kv_tile_rows()) + "x" + std::to_string(ffa::bwd_kv_tile_cols()) +
+                    " head_dims=64,128 softcap=tanh compiler=" + __VERSION__;
     return s;
   }();
   return info.c_str();
@@ -193,12 +331,12 @@ const char* ffa_build_info(void) {
 int64_t ffa_plan_host(int64_t Tq, int64_t Tk, const int32_t* q_ranges, const int32_t* k_ranges,
                       const int32_t* attn_type_map, int R, int bm, int bn, int transpose,
                       int64_t* row_ptr, int32_t* entries, int64_t cap, int32_t* order) {
-  if (Tq < 0 || Tk < 0) return fail(FFA_ERR_INVALID_ARG, "Tq and Tk must be >= 0");
+  g_err.clear();
+  std::string m = check_sizes(Tq, Tk);
+  if (!m.empty()) return fail(FFA_ERR_INVALID_ARG, m);
   if (bm <= 0 || bn <= 0) return fail(FFA_ERR_INVALID_ARG, "tile sizes must be positive");
-  if (Tq >= (int64_t(1) << 31) || Tk >= (int64_t(1) << 31))
-    return fail(FFA_ERR_INVALID_ARG, "token counts must be below 2^31");
   std::vector<ffa::Slice> slices;
-  std::string m = ffa::validate_slices(Tq, Tk, q_ranges, k_ranges, attn_type_map, R, &slices);
+  m = ffa::validate_slices(Tq, Tk, q_ranges, k_ranges, attn_type_map, R, &slices);
   if (!m.empty()) return fail(FFA_ERR_INVALID_ARG, m);
   ffa::Plan plan;
   try {
@@ -220,48 +358,65 @@ int64_t ffa_plan_host(int64_t Tq, int64_t Tk, const int32_t* q_ranges, const int
   return n;
 }
 
+int ffa_plan_create(int64_t Tq, int64_t Tk, const int32_t* q_ranges, const int32_t* k_ranges,
+                    const int32_t* attn_type_map, int R, void* stream, ffa_plan_t* plan) {
+  g_err.clear();
+  if (!plan) return fail(FFA_ERR_INVALID_ARG, "plan must not be NULL");
+  return plan_create(Tq, Tk, q_ranges, k_ranges, attn_type_map, R, kWantFwd | kWantBwd,
+                     static_cast<hipStream_t>(stream), plan);
+}
+
+int ffa_plan_destroy(ffa_plan_t plan, void* stream) {
+  g_err.clear();
+  return plan_destroy(plan, static_cast<hipStream_t>(stream));
+}
+
+int ffa_fwd_planned(ffa_plan_t plan, const void* q, const void* k, const void* v, int hq, int hkv,
+                    int d, float scale, float softcap, void* out, float* lse, void* stream) {
+  g_err.clear();
+  if (!plan) return fail(FFA_ERR_INVALID_ARG, "plan must not be NULL");
+  return fwd_planned(plan, q, k, v, hq, hkv, d, scale, softcap, out, lse, static_cast<hipStream_t>(stream));
+}
+
+int ffa_bwd_planned(ffa_plan_t plan, const void* q, const void* k, const void* v, const void* out,
+                    const float* lse, const void* dout, int hq, int hkv, int d, float scale,
+                    float softcap, void* dq, void* dk, void* dv, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!plan) return fail(FFA_ERR_INVALID_ARG, "plan must not be NULL");
+  return bwd_planned(plan, q, k, v, out, lse, dout, hq, hkv, d, scale, softcap, dq, dk, dv,
+                     workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
 int ffa_fwd(const void* q, const void* k, const void* v, int64_t Tq, int64_t Tk, int hq, int hkv,
             int d, const int32_t* q_ranges, const int32_t* k_ranges, const int32_t* attn_type_map,
             int R, float scale, float softcap, void* out, float* lse, void* stream) {
   g_err.clear();
-  std::vector<ffa::Slice> slices;
-  const Shape sh{Tq, Tk, hq, hkv, d};
-  int rc = check_common(sh, scale, softcap, q_ranges, k_ranges, attn_type_map, R, &slices);
+  std::string m = check_sizes(Tq, Tk);
+  if (!m.empty()) return fail(FFA_ERR_INVALID_ARG, m);
+  int rc = check_heads(Tq, Tk, hq, hkv, d, scale, softcap);
   if (rc != FFA_OK) return rc;
-  if (Tq > 0 && (!q || !out || !lse)) return fail(FFA_ERR_INVALID_ARG, "q, out and lse must not be NULL");
-  if (Tk > 0 && (!k || !v)) return fail(FFA_ERR_INVALID_ARG, "k and v must not be NULL");
+  if ((rc = check_slices(Tq, Tk, q_ranges, k_ranges, attn_type_map, R)) != FFA_OK) return rc;
+  const bool has_q = Tq > 0, has_k = Tk > 0;
+  if ((rc = check_ptr(q, has_q, "q")) || (rc = check_ptr(out, has_q, "out")) ||
+      (rc = check_ptr(lse, has_q, "lse")) || (rc = check_ptr(k, has_k, "k")) ||
+      (rc = check_ptr(v, has_k, "v")))
+    return rc;
   if (Tq == 0) return FFA_OK;
-
-  ffa::Plan plan;
-  PlanImage img;
-  try {
-    ffa::build_plan(slices, Tq, Tk, ffa::fwd_tile_rows(), ffa::fwd_tile_cols(), false, &plan);
-    std::string m = pack_plan(plan, slices, &img);
-    if (!m.empty()) return fail(FFA_ERR_UNSUPPORTED, m);
-  } catch (const std::bad_alloc&) {
-    return fail(FFA_ERR_NOMEM, "out of host memory while planning");
-  }
   hipStream_t st = static_cast<hipStream_t>(stream);
-  DevicePlan dp;
-  rc = stage_plan(img, st, &dp);
+  ffa_plan_s* p = nullptr;
+  rc = plan_create(Tq, Tk, q_ranges, k_ranges, attn_type_map, R, kWantFwd, st, &p);
   if (rc != FFA_OK) return rc;
-
-  ffa::FwdLaunch p;
-  p.q = q; p.k = k; p.v = v; p.out = out; p.lse = lse;
-  p.Tq = Tq; p.Tk = Tk; p.hq = hq; p.hkv = hkv; p.d = d;
-  p.scale = scale; p.softcap = softcap;
-  p.row_ptr = reinterpret_cast<const int32_t*>(dp.base + img.off_row_ptr);
-  p.entries = dp.base + img.off_entries;
-  p.order = reinterpret_cast<const int32_t*>(dp.base + img.off_order);
-  p.slices = dp.base + img.off_slices;
-  hipError_t e = ffa::launch_fwd(p, st);
-  if (e != hipSuccess) return hip_fail(e, "forward kernel launch");
-  return FFA_OK;
+  rc = fwd_planned(p, q, k, v, hq, hkv, d, scale, softcap, out, lse, st);
+  const std::string err = g_err;
+  const int rc2 = plan_destroy(p, st);
+  if (rc != FFA_OK) return fail(rc, err);
+  return rc2;
 }
 
 size_t ffa_bwd_workspace_size(int64_t Tq, int hq) {
   if (Tq <= 0 || hq <= 0) return 0;
-  return static_cast<size_t>(Tq) * static_cast<size_t>(hq) * sizeof(float);
+  return align16(static_cast<size_t>(Tq) * static_cast<size_t>(hq) * sizeof(float));
 }
 
 int ffa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
@@ -270,13 +425,31 @@ int ffa_bwd(const void* q, const void* k, const void* v, const void* out, const 
             float scale, float softcap, void* dq, void* dk, void* dv, void* workspace,
             size_t workspace_bytes, void* stream) {
   g_err.clear();
-  (void)q; (void)k; (void)v; (void)out; (void)lse; (void)dout; (void)dq; (void)dk; (void)dv;
-  (void)workspace; (void)workspace_bytes; (void)stream;
-  std::vector<ffa::Slice> slices;
-  const Shape sh{Tq, Tk, hq, hkv, d};
-  int rc = check_common(sh, scale, softcap, q_ranges, k_ranges, attn_type_map, R, &slices);
+  std::string m = check_sizes(Tq, Tk);
+  if (!m.empty()) return fail(FFA_ERR_INVALID_ARG, m);
+  int rc = check_heads(Tq, Tk, hq, hkv, d, scale, softcap);
   if (rc != FFA_OK) return rc;
-  return fail(FFA_ERR_UNSUPPORTED, "backward pass not built yet");
+  if ((rc = check_slices(Tq, Tk, q_ranges, k_ranges, attn_type_map, R)) != FFA_OK) return rc;
+  const bool has_q = Tq > 0, has_k = Tk > 0;
+  if ((rc = check_ptr(q, has_q, "q")) || (rc = check_ptr(out, has_q, "out")) ||
+      (rc = check_ptr(lse, has_q, "lse")) || (rc = check_ptr(dout, has_q, "dout")) ||
+      (rc = check_ptr(dq, has_q, "dq")) || (rc = check_ptr(k, has_k, "k")) ||
+      (rc = check_ptr(v, has_k, "v")) || (rc = check_ptr(dk, has_k, "dk")) ||
+      (rc = check_ptr(dv, has_k, "dv")))
+    return rc;
+  if (workspace && workspace_bytes < ffa_bwd_workspace_size(Tq, hq))
+    return fail(FFA_ERR_INVALID_ARG, "workspace is smaller than ffa_bwd_workspace_size()");
+  if (Tq == 0 && Tk == 0) return FFA_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  ffa_plan_s* p = nullptr;
+  rc = plan_create(Tq, Tk, q_ranges, k_ranges, attn_type_map, R, kWantFwd | kWantBwd, st, &p);
+  if (rc != FFA_OK) return rc;
+  rc = bwd_planned(p, q, k, v, out, lse, dout, hq, hkv, d, scale, softcap, dq, dk, dv, workspace,
+                   workspace_bytes, st);
+  const std::string err = g_err;
+  const int rc2 = plan_destroy(p, st);
+  if (rc != FFA_OK) return fail(rc, err);
+  return rc2;
 }
 
 }  // extern "C"

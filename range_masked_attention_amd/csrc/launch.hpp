@@ -30,8 +30,39 @@ struct FwdLaunch {
   const void* slices;      // device: HostDevSlice[]
 };
 
+struct BwdLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dvec;  // device workspace [Tq * hq]
+  int64_t Tq, Tk;
+  int hq, hkv, d;
+  float scale, softcap;
+  // key-side plan (dK, dV): per key tile, the q tiles
+  const int32_t* kv_row_ptr;
+  const void* kv_entries;
+  const int32_t* kv_order;
+  // query-side plan (dQ): per q tile, the key tiles
+  const int32_t* q_row_ptr;
+  const void* q_entries;
+  const int32_t* q_order;
+  const void* slices;
+};
+
 int fwd_tile_rows();
 int fwd_tile_cols();
 hipError_t launch_fwd(const FwdLaunch& p, hipStream_t stream);
+
+int bwd_kv_tile_rows();  // q rows per step of the dK/dV kernel
+int bwd_kv_tile_cols();  // keys per dK/dV workgroup
+int bwd_q_tile_rows();   // q rows per dQ workgroup
+int bwd_q_tile_cols();   // keys per dQ step
+hipError_t launch_bwd(const BwdLaunch& p, hipStream_t stream);
 
 }  // namespace ffa

@@ -24,7 +24,8 @@ def _declared():
 def test_exports_every_declared_symbol(lib):
     names = _declared()
     assert {"ffa_fwd", "ffa_bwd", "ffa_bwd_workspace_size", "ffa_plan_host",
-            "ffa_last_error", "ffa_build_info"} <= set(names)
+            "ffa_last_error", "ffa_build_info", "ffa_plan_create", "ffa_fwd_planned",
+            "ffa_bwd_planned", "ffa_plan_destroy"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
     # the python binding carries the same names
@@ -96,3 +97,20 @@ def test_bwd_validation(lib):
                      0.1, 0.0, 64, 64, 64, None, 0, None)
     assert rc == -1 and "k range" in ffa.ffa_last_error()
     assert lib.ffa_bwd_workspace_size(100, 8) == 100 * 8 * 4
+
+
+def test_plan_api_validation(lib):
+    ip = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    qr = np.array([[0, 4]], np.int32); kr = np.array([[2, 1]], np.int32); ty = np.array([0], np.int32)
+    h = ctypes.c_void_p()
+    assert lib.ffa_plan_create(4, 8, ip(qr), ip(kr), ip(ty), 1, None, ctypes.byref(h)) == -1
+    assert "k range" in ffa.ffa_last_error() and h.value is None
+    assert lib.ffa_plan_create(4, 8, ip(qr), ip(kr), ip(ty), 1, None, None) == -1
+    assert lib.ffa_fwd_planned(None, 64, 64, 64, 1, 1, 64, 0.1, 0.0, 64, 64, None) == -1
+    assert "plan" in ffa.ffa_last_error()
+    assert lib.ffa_plan_destroy(None, None) == 0
+
+
+def test_misaligned_pointer_rejected(lib):
+    assert _fwd(lib, ptr=72) == -1
+    assert "aligned" in ffa.ffa_last_error()
