@@ -178,7 +178,7 @@ def attention_fwd(q, k, v, q_ranges, k_ranges, types, scale, softcap=0.0,
 # backward
 # --------------------------------------------------------------------------
 def attention_bwd(q, k, v, dout, q_ranges, k_ranges, types, scale, softcap=0.0,
-                  rows=None, keys=None, block=256):
+                  rows=None, keys=None, block=256, magnitudes=False):
     """Gradients of ``sum(dout * out)``: dq at ``rows``, dk and dv at ``keys``.
 
     Chain rule through the forward above, in the usual flash-attention form:
@@ -187,6 +187,13 @@ def attention_bwd(q, k, v, dout, q_ranges, k_ranges, types, scale, softcap=0.0,
     ``1 - tanh^2 = 1 - (s / c)^2``, ``dQ = scale * dU K``, ``dK = scale * dU^T Q``.
     GQA: dk and dv of a kv head sum over the q heads that read it.
     Returns (dq [len(rows), hq, d], dk [len(keys), hkv, d], dv [len(keys), hkv, d]).
+
+    With ``magnitudes=True`` it also returns, per gradient element, the scale
+    of the rounding error an implementation in rounded arithmetic can carry:
+    the sum of the absolute values of the terms that add up to it, where the
+    row term D is taken as uncertain by A_i = sum_d |dO_id| (|out_id| +
+    (P|V|)_id) (D is formed from a rounded copy of out):
+      dq: scale (|dU| + P A) |K|,  dk: scale (|dU| + P A)^T |Q|,  dv: P^T |dO|.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -216,6 +223,8 @@ def attention_bwd(q, k, v, dout, q_ranges, k_ranges, types, scale, softcap=0.0,
     dq = np.zeros((rows.size, hq, d))
     dk = np.zeros((keys.size, hkv, d))
     dv = np.zeros((keys.size, hkv, d))
+    if magnitudes:
+        dq_m, dk_m, dv_m = np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv)
     for b0 in range(0, work.size, block):
         rb = work[b0:b0 + block]
         cols, vis, res = _row_block_attention(q, k, v, slices, scale, softcap, rb, Tk)
@@ -241,6 +250,16 @@ def attention_bwd(q, k, v, dout, q_ranges, k_ranges, types, scale, softcap=0.0,
             if kmask.any():
                 dv[kp[kmask], g, :] += p[:, kmask].T @ do
                 dk[kp[kmask], g, :] += scale * (dU[:, kmask].T @ q[rb, h, :])
+            if magnitudes:
+                A = (np.abs(do) * (np.abs(out) + p @ np.abs(v[cols, g, :]))).sum(axis=1)
+                dU_abs = np.abs(dU) + p * A[:, None]
+                if dq_mask.any():
+                    dq_m[dq_rows[dq_mask], h, :] += scale * (dU_abs[dq_mask] @ np.abs(k[cols, g, :]))
+                if kmask.any():
+                    dv_m[kp[kmask], g, :] += p[:, kmask].T @ np.abs(do)
+                    dk_m[kp[kmask], g, :] += scale * (dU_abs[:, kmask].T @ np.abs(q[rb, h, :]))
+    if magnitudes:
+        return dq, dk, dv, (dq_m, dk_m, dv_m)
     return dq, dk, dv
 
 

@@ -419,3 +419,18 @@ def test_doc_config_closed_form():
     sl = O.normalise_slices(*w.slices(), w.Tq, w.Tk)
     assert len(sl) == 10 and w.slices()[0].shape == (64, 2)
     assert O.visible_count(sl, w.Tq, w.Tk) == sum(n * (n + 1) // 2 for n in lens)
+
+
+def test_backward_term_magnitudes_bound_the_gradients():
+    """Triangle inequality, and equality when every term has one sign."""
+    rng = np.random.default_rng(19)
+    T = 90
+    qr, kr, ty = W.random_slices(rng, T, T, max_slices=4)
+    q, k, v = _rand((T, 2, 8), rng), _rand((T, 1, 8), rng), _rand((T, 1, 8), rng)
+    do = _rand((T, 2, 8), rng)
+    dq, dk, dv, (mq, mk, mv) = O.attention_bwd(q, k, v, do, qr, kr, ty, 0.4, magnitudes=True)
+    for g, m in ((dq, mq), (dk, mk), (dv, mv)):
+        assert np.all(np.abs(g) <= m + 1e-12)
+    # dO >= 0 and P >= 0: dv is a sum of non-negative terms, so it equals its magnitude
+    _, _, dv2, (_, _, mv2) = O.attention_bwd(q, k, v, np.abs(do), qr, kr, ty, 0.4, magnitudes=True)
+    np.testing.assert_allclose(dv2, mv2, rtol=1e-12, atol=1e-14)
