@@ -12,10 +12,14 @@
 // Working with transposed tiles keeps a query row inside one lane (16 keys
 // per 32x32 block), so the row max and row sum are in-lane work plus one
 // exchange between the two half-waves, and the rescale of O is a per-lane
-// scalar.  K is staged row-major in LDS, V transposed (the PV contraction
-// runs over keys), both double-buffered so the next tile's global loads are
-// in flight while the current tile computes (prefetching later KV tiles:
-// same section, data prefetching pipeline).  The per-cell mask is evaluated
+// scalar.  K and V are staged row-major in LDS, double-buffered so the next
+// tile's global loads are in flight while the current tile computes
+// (prefetching later KV tiles: same section, data prefetching pipeline); the
+// PV contraction runs over keys, so V^T fragments are read with the gfx950
+// LDS transpose load (ds_read_b64_tr_b16) instead of transposing in
+// registers.  The running max moves only when a row's tile max exceeds it by
+// more than 2^8 (in exp2 units), so the O rescale is skipped for most tiles.
+// The per-cell mask is evaluated
 // only on PARTIAL tiles (full-block optimisation); invisible cells become
 // -inf before the softmax (masking P in softmax, as recommended in CUTLASS
 // issue #2192 on ex77 varlen handling), and rows past the end of a tensor
@@ -46,14 +50,15 @@ struct FwdArgs {
   float score_mult;         // exponent multiplier: scale*log2(e), or 1 with softcap
   float cap_in;             // softcap: 2*scale*log2(e)/softcap (tanh argument, see tanh_from_2xlog2e)
   float cap_out;            // softcap: softcap*log2(e)
+  float rescale_thr;        // 8 exp2 units in the units of the running max
 };
 
 template <int D>
 struct FwdSmem {
   static constexpr int kStr = D + 8;      // K row stride (bf16): 16 B pad
-  static constexpr int vStr = kBN + 4;    // V^T row stride (bf16): 8 B pad
+  static constexpr int vStr = D + 32;     // V row stride (bf16): 64 B pad, so a transpose read's four rows x 64 B fill the 64 LDS banks
   static constexpr int kBuf = kBN * kStr;
-  static constexpr int vBuf = D * vStr;
+  static constexpr int vBuf = kBN * vStr;
   static constexpr int kElems = 2 * (kBuf + vBuf);
 };
 
@@ -76,16 +81,13 @@ __device__ __forceinline__ bool decode_item(const FwdArgs& a, int* qt, int* head
 
 template <int D>
 struct TileLoader {
-  // K tile: kBN rows x D, 16-byte chunks spread over the workgroup
+  // K and V tiles: kBN rows x D, 16-byte chunks spread over the workgroup
   static constexpr int kChunksPerRow = D / 8;
   static constexpr int kLoads = kBN * kChunksPerRow / kThreads;
-  // V tile: units of (4 keys x 8 dims), transposed into LDS
-  static constexpr int vUnits = (kBN / 4) * (D / 8);
-  static_assert(kLoads * kThreads == kBN * kChunksPerRow, "K tile must split evenly");
-  static_assert(vUnits <= kThreads, "one V unit per thread at most");
+  static_assert(kLoads * kThreads == kBN * kChunksPerRow, "tile must split evenly");
 
   u32x4 kreg[kLoads];
-  u32x4 vreg[4];
+  u32x4 vreg[kLoads];
 
   __device__ __forceinline__ void load(const FwdArgs& a, int ktile, int g, int tid) {
     const int64_t row_bytes = (int64_t)a.hkv * D * 2;
@@ -98,13 +100,9 @@ struct TileLoader {
     for (int c = 0; c < kLoads; ++c) {
       const int idx = tid + kThreads * c;
       const int row = idx / kChunksPerRow, col = idx % kChunksPerRow;
-      kreg[c] = buf_load16(rk, (uint32_t)(row * row_bytes + col * 16));
-    }
-    if (tid < vUnits) {
-      const int cc = tid / (kBN / 4), grp4 = tid % (kBN / 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        vreg[i] = buf_load16(rv, (uint32_t)((4 * grp4 + i) * row_bytes + cc * 16));
+      const uint32_t off = (uint32_t)(row * row_bytes + col * 16);
+      kreg[c] = buf_load16(rk, off);
+      vreg[c] = buf_load16(rv, off);
     }
   }
 
@@ -114,26 +112,19 @@ struct TileLoader {
       const int idx = tid + kThreads * c;
       const int row = idx / kChunksPerRow, col = idx % kChunksPerRow;
       *reinterpret_cast<u32x4*>(kl + row * FwdSmem<D>::kStr + col * 8) = kreg[c];
-    }
-    if (tid < vUnits) {
-      const int cc = tid / (kBN / 4), grp4 = tid % (kBN / 4);
-      // vreg[i] holds dims cc*8 .. cc*8+7 of key 4*grp4+i; write, per dim,
-      // the 4 keys as one 8-byte word of the transposed tile
-#pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        const int sh = (p & 1) * 16;
-        const uint32_t x0 = (vreg[0][p >> 1] >> sh) & 0xFFFFu;
-        const uint32_t x1 = (vreg[1][p >> 1] >> sh) & 0xFFFFu;
-        const uint32_t x2 = (vreg[2][p >> 1] >> sh) & 0xFFFFu;
-        const uint32_t x3 = (vreg[3][p >> 1] >> sh) & 0xFFFFu;
-        u32x2 w;
-        w[0] = x0 | (x1 << 16);
-        w[1] = x2 | (x3 << 16);
-        *reinterpret_cast<u32x2*>(vl + (cc * 8 + p) * FwdSmem<D>::vStr + 4 * grp4) = w;
-      }
+      *reinterpret_cast<u32x4*>(vl + row * FwdSmem<D>::vStr + col * 8) = vreg[c];
     }
   }
 };
+
+// Transpose read of a row-major tile: in each 16-lane group, lane i receives
+// element i % 4 of the 8-byte chunks addressed by lanes 4r + i / 4, r = 0..3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const __bf16* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(const_cast<__bf16*>(p)));
+  return __builtin_bit_cast(u32x2, r);
+}
 
 template <int D, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
@@ -229,44 +220,55 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[b][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2((m_run - m_use) * a.score_mult);
-    const float neg = -m_use * a.score_mult;
-    float rs = 0.f;
+    // move the running max only when this tile's max exceeds it by more than
+    // 2^8 in exp2 units (all lanes together, so the branch is uniform); until
+    // then exp2 values stay <= 2^8 and O, l need no rescale
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + a.rescale_thr) != 0) {
+      const float m_new = fmaxf(m_run, mx);
+      // rows whose max does not move keep their scale (this also covers rows
+      // that have seen nothing yet: -inf - -inf would be NaN); a row whose
+      // first visible key arrives gets exp2(-inf) = 0
+      const float alpha = (m_new == m_run) ? 1.0f : fast_exp2((m_run - m_new) * a.score_mult);
+      l_part *= alpha;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = fast_exp2(__builtin_fmaf(s[b][v], a.score_mult, neg));
-        s[b][v] = p;
-        rs += p;
-      }
-    l_part = l_part * alpha + rs;
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < DB; ++i) o[i] *= alpha;
-
-    // ---- O^T += V^T P^T : four k-steps of 16 keys
+      for (int i = 0; i < DB; ++i) o[i] *= alpha;
+      m_run = m_new;
+    }
+    const float neg = (m_run == -INFINITY) ? 0.f : -m_run * a.score_mult;
+    // exp2 weights; the row sum is taken in fp32 on the unrounded values (the
+    // lse must hold to 1e-3 even for rows with a handful of keys), in four
+    // independent chains
     bf16x8 pf[4];
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int b = t >> 1, h8 = (t & 1) * 8;
 #pragma unroll
-      for (int e8 = 0; e8 < 8; ++e8) pf[t][e8] = (__bf16)s[b][h8 + e8];
-    }
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const __bf16* vrow = vl + (32 * db + n) * Smem::vStr + 4 * hh;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int kb = 32 * (t >> 1) + 16 * (t & 1);
-        const u32x2 lo4 = *reinterpret_cast<const u32x2*>(vrow + kb);
-        const u32x2 hi4 = *reinterpret_cast<const u32x2*>(vrow + kb + 8);
-        u32x4 av;
-        av[0] = lo4[0]; av[1] = lo4[1]; av[2] = hi4[0]; av[3] = hi4[1];
-        o[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8, av), pf[t], o[db]);
+      for (int e8 = 0; e8 < 8; ++e8) {
+        const float p = fast_exp2(__builtin_fmaf(s[b][h8 + e8], a.score_mult, neg));
+        rs[e8 & 3] += p;
+        pf[t][e8] = (__bf16)p;
       }
+    }
+    l_part += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+
+    // ---- O^T += V^T P^T : four k-steps of 16 keys; A = V^T by transpose reads
+    {
+      const int g16 = lane >> 4, sl = lane & 15;
+      const int col = 16 * (g16 & 1) + 4 * (sl & 3);
+      const int krow = 4 * hh + (sl >> 2);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int kb = 32 * (t >> 1) + 16 * (t & 1) + krow;
+          const __bf16* vp = vl + kb * Smem::vStr + 32 * db + col;
+          const u32x2 lo4 = lds_read_tr16(vp);
+          const u32x2 hi4 = lds_read_tr16(vp + 8 * Smem::vStr);
+          u32x4 av;
+          av[0] = lo4[0]; av[1] = lo4[1]; av[2] = hi4[0]; av[3] = hi4[1];
+          o[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8, av), pf[t], o[db]);
+        }
     }
 
     if (has_next) {
@@ -325,6 +327,7 @@ hipError_t launch_fwd_t(const FwdLaunch& p, hipStream_t stream) {
     a.score_mult = p.scale * log2e;
     a.cap_in = a.cap_out = 0.f;
   }
+  a.rescale_thr = 8.0f / a.score_mult;
   const int64_t n_wg = ((a.n_units + 7) / 8) * 8 * (int64_t)a.grp;
   if (n_wg == 0) return hipSuccess;
   hipLaunchKernelGGL((fwd_kernel<D, SC>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream, a);
