@@ -24,6 +24,8 @@
 // -inf before the softmax (masking P in softmax, as recommended in CUTLASS
 // issue #2192 on ex77 varlen handling), and rows past the end of a tensor
 // are read as zeros through range-checked buffer loads and never stored.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -53,13 +55,20 @@ struct FwdArgs {
   float rescale_thr;        // 8 exp2 units in the units of the running max
 };
 
+// LDS tiles are unpadded kBN x D bf16, filled by direct-to-LDS loads; 16-byte
+// chunks are XOR-swizzled within each row so the reads below hit all 64
+// banks: K (row-major reads of one chunk by 16 rows) uses slot = chunk ^
+// (row & 15) (d = 128) or ^ ((row >> 1) & 7) (d = 64); V (transpose reads of
+// 4 rows x 64 bytes per half-wave) uses slot = chunk ^ 4 (row & 3) (d = 128)
+// or ^ 4 ((row >> 1) & 1) (d = 64).
 template <int D>
 struct FwdSmem {
-  static constexpr int kStr = D + 8;      // K row stride (bf16): 16 B pad
-  static constexpr int vStr = D + 32;     // V row stride (bf16): 64 B pad, so a transpose read's four rows x 64 B fill the 64 LDS banks
-  static constexpr int kBuf = kBN * kStr;
-  static constexpr int vBuf = kBN * vStr;
-  static constexpr int kElems = 2 * (kBuf + vBuf);
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kChunks = D / 8;                 // 16-byte chunks per row
+  static constexpr int kTileBytes = kBN * kRowBytes;
+  static constexpr int kElems = 4 * kTileBytes / 2;     // K[2], V[2]
+  __device__ __forceinline__ static int k_swz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+  __device__ __forceinline__ static int v_swz(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 };
 
 // Work-item decode.  Workgroups are handed to the 8 XCDs round-robin
@@ -79,43 +88,62 @@ __device__ __forceinline__ bool decode_item(const FwdArgs& a, int* qt, int* head
   return true;
 }
 
+// Direct-to-LDS tile loads: lane L of a load instruction writes 16 bytes at
+// the instruction's LDS base + 16 L; each lane fetches the global chunk that
+// belongs at that slot under the swizzle.  Rows past the end of the tensor
+// read as zeros (buffer range check).
 template <int D>
-struct TileLoader {
-  // K and V tiles: kBN rows x D, 16-byte chunks spread over the workgroup
-  static constexpr int kChunksPerRow = D / 8;
-  static constexpr int kLoads = kBN * kChunksPerRow / kThreads;
-  static_assert(kLoads * kThreads == kBN * kChunksPerRow, "tile must split evenly");
+struct TileDma {
+  using Smem = FwdSmem<D>;
+  static constexpr int kPerThread = kBN * Smem::kChunks / kThreads;  // 16-byte loads per thread
+  static constexpr int kRowsPerLoad = 64 / Smem::kChunks;            // rows one wave load covers
+  static_assert(kPerThread * kThreads == kBN * Smem::kChunks, "tile must split evenly");
 
-  u32x4 kreg[kLoads];
-  u32x4 vreg[kLoads];
+  // Load c of wave w: lane L fills chunk slot P = (w * kPerThread + c) * 64 + L,
+  // i.e. row (w * kPerThread + c) * kRowsPerLoad + L / kChunks, slot L % kChunks.
+  // The swizzle of that row depends on L and c only through row bits that
+  // L / kChunks and c set without carries, so the global offset splits into a
+  // per-lane part and a wave-uniform part.
+  uint32_t lane_row_bytes;  // (L / kChunks) * row_bytes
+  int lane_slot, lane_row;  // L % kChunks, L / kChunks
 
-  __device__ __forceinline__ void load(const FwdArgs& a, int ktile, int g, int tid) {
+  __device__ __forceinline__ void init(const FwdArgs& a, int lane) {
+    lane_slot = lane % Smem::kChunks;
+    lane_row = lane / Smem::kChunks;
+    lane_row_bytes = (uint32_t)lane_row * ((uint32_t)a.hkv * D * 2);
+  }
+  __device__ __forceinline__ static __amdgpu_buffer_rsrc_t rsrc(const FwdArgs& a, const __bf16* t, int ktile, int g) {
     const int64_t row_bytes = (int64_t)a.hkv * D * 2;
     const int64_t k0 = (int64_t)ktile * kBN;
-    const int64_t base_off = (k0 * a.hkv + g) * D;
-    const int64_t valid = ((int64_t)a.Tk - k0) * row_bytes - (int64_t)g * D * 2;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + base_off, valid);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + base_off, valid);
+    return make_rsrc(t + (k0 * a.hkv + g) * D, ((int64_t)a.Tk - k0) * row_bytes - (int64_t)g * D * 2);
+  }
+  template <bool IS_K>
+  __device__ __forceinline__ void load(const FwdArgs& a, const __bf16* t, int ktile, int g, __bf16* dst, int w) const {
+    const __amdgpu_buffer_rsrc_t r = rsrc(a, t, ktile, g);
+    const uint32_t row_bytes = (uint32_t)a.hkv * D * 2;
 #pragma unroll
-    for (int c = 0; c < kLoads; ++c) {
-      const int idx = tid + kThreads * c;
-      const int row = idx / kChunksPerRow, col = idx % kChunksPerRow;
-      const uint32_t off = (uint32_t)(row * row_bytes + col * 16);
-      kreg[c] = buf_load16(rk, off);
-      vreg[c] = buf_load16(rv, off);
+    for (int c = 0; c < kPerThread; ++c) {
+      const int row0 = (w * kPerThread + c) * kRowsPerLoad;  // wave-uniform
+      const int row = row0 + lane_row;
+      const int swz = IS_K ? Smem::k_swz(row) : Smem::v_swz(row);
+      const uint32_t off = (uint32_t)row0 * row_bytes + lane_row_bytes + (uint32_t)((lane_slot ^ swz) * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(dst + (w * kPerThread + c) * 512), 16, off, 0, 0, 0);
     }
   }
-
-  __device__ __forceinline__ void store(__bf16* kl, __bf16* vl, int tid) {
-#pragma unroll
-    for (int c = 0; c < kLoads; ++c) {
-      const int idx = tid + kThreads * c;
-      const int row = idx / kChunksPerRow, col = idx % kChunksPerRow;
-      *reinterpret_cast<u32x4*>(kl + row * FwdSmem<D>::kStr + col * 8) = kreg[c];
-      *reinterpret_cast<u32x4*>(vl + row * FwdSmem<D>::vStr + col * 8) = vreg[c];
-    }
+  __device__ __forceinline__ void load_k(const FwdArgs& a, int ktile, int g, __bf16* dst, int w) const {
+    load<true>(a, a.k, ktile, g, dst, w);
+  }
+  __device__ __forceinline__ void load_v(const FwdArgs& a, int ktile, int g, __bf16* dst, int w) const {
+    load<false>(a, a.v, ktile, g, dst, w);
   }
 };
+
+// Wait for this wave's direct-to-LDS loads, then for the whole workgroup.
+__device__ __forceinline__ void dma_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
 
 // Transpose read of a row-major tile: in each 16-lane group, lane i receives
 // element i % 4 of the 8-byte chunks addressed by lanes 4r + i / 4, r = 0..3.
@@ -126,12 +154,67 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const __bf16* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+// S^T = K Q^T for one 64-key tile: two 32-key blocks.  Lane (n, hh) reads
+// row 32b + n, logical chunk 2ks + hh.
+template <int D>
+__device__ __forceinline__ void qk_tile(const __bf16* kl, const bf16x8* qf, int n, int hh, f32x16* s) {
+  using Smem = FwdSmem<D>;
+  const int swz = Smem::k_swz(n);  // rows n and 32 + n share it
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    s[b] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const int byte = (32 * b + n) * Smem::kRowBytes + (((2 * ks + hh) ^ swz) * 16);
+      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(kl) + byte);
+      s[b] = mfma_32x32x16(kf, qf[ks], s[b]);
+    }
+  }
+}
+
+// Softcap in exp2 units: cap*log2(e) * tanh(scale * s / cap).
+__device__ __forceinline__ void softcap_tile(const FwdArgs& a, f32x16* s) {
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[b][v] = a.cap_out * tanh_from_2xlog2e(s[b][v] * a.cap_in);
+}
+
+// Row max over this lane's 32 scores and the other half-wave's 32.
+__device__ __forceinline__ float tile_max(const f32x16* s) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[b][v]);
+  return fmaxf(mx, __shfl_xor(mx, 32));
+}
+
+// Invisible cells of a PARTIAL tile become -inf (cell (row, key) of slice sl).
+__device__ __forceinline__ void mask_tile(const DevSlice& sl, int ktile, int row, int hh, f32x16* s) {
+  int lo = sl.ks, hi = sl.ke;
+  if (sl.causal) hi = min(hi, row + 1 + (sl.ke - sl.qe));
+  if (row < sl.qs || row >= sl.qe) hi = lo;  // row outside the slice: nothing visible
+  const int base = ktile * kBN + 4 * hh;
+  lo -= base;
+  hi -= base;
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int off = 32 * b + 8 * (v >> 2) + (v & 3);
+      if (off < lo || off >= hi) s[b][v] = -INFINITY;
+    }
+}
+
 template <int D, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   using Smem = FwdSmem<D>;
   constexpr int KS = D / 16;  // k steps of the QK^T contraction
   constexpr int DB = D / 32;  // 32-wide blocks of the head dim in O^T
-  __shared__ __attribute__((aligned(16))) __bf16 smem[Smem::kElems];
+  constexpr int kTileElems = Smem::kTileBytes / 2;
+  __shared__ __attribute__((aligned(1024))) __bf16 smem[Smem::kElems];
+  // K[0], K[1], V[0], V[1]
 
   int qt, head, g;
   if (!decode_item(a, &qt, &head, &g)) return;
@@ -155,6 +238,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   }
 
   const int e_begin = a.row_ptr[qt], e_end = a.row_ptr[qt + 1];
+  const int n_tiles = e_end - e_begin;
 
   f32x16 o[DB];
 #pragma unroll
@@ -162,120 +246,144 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   float m_run = -INFINITY;  // running row max, in the units fed to score_mult
   float l_part = 0.f;       // this half-wave's share of the row sum
 
-  TileLoader<D> ld;
-  if (e_begin < e_end) {
-    ld.load(a, a.entries[e_begin].tile, g, tid);
-    ld.store(smem, smem + Smem::kBuf, tid);
-  }
-  __syncthreads();
+  // V^T fragments by transpose reads: lane (group g16, index sl) points at
+  // key row v_krow (+ block offsets), 4 dims at v_col
+  const int g16 = lane >> 4, sl16 = lane & 15;
+  const int v_col = 16 * (g16 & 1) + 4 * (sl16 & 3);
+  const int v_krow = 4 * hh + (sl16 >> 2);
+  const int v_sw = Smem::v_swz(v_krow);  // every key row read by this lane shares it
 
-  for (int e = e_begin; e < e_end; ++e) {
-    const int buf = (e - e_begin) & 1;
-    const __bf16* kl = smem + buf * (Smem::kBuf + Smem::vBuf);
-    const __bf16* vl = kl + Smem::kBuf;
-    const DevEntry ent = a.entries[e];
-    const bool has_next = e + 1 < e_end;
-    if (has_next) ld.load(a, a.entries[e + 1].tile, g, tid);
+  if (n_tiles > 0) {
+    TileDma<D> dma;
+    dma.init(a, lane);
+    __bf16* const kb0 = smem;
+    __bf16* const kb1 = smem + kTileElems;
+    __bf16* const vb0 = smem + 2 * kTileElems;
+    __bf16* const vb1 = smem + 3 * kTileElems;
+    // ---- prologue: K0, V0 and K1 in LDS; S0 and its row max
+    dma.load_k(a, a.entries[e_begin].tile, g, kb0, w);
+    dma.load_v(a, a.entries[e_begin].tile, g, vb0, w);
+    if (n_tiles > 1) dma.load_k(a, a.entries[e_begin + 1].tile, g, kb1, w);
+    dma_barrier();
+    f32x16 sa[2], sb[2];
+    qk_tile<D>(kb0, qf, n, hh, sa);
+    if constexpr (SOFTCAP) softcap_tile(a, sa);
+    float mx_cur = tile_max(sa);
+    __syncthreads();  // K0's buffer is refilled in the first step
 
-    // ---- S^T = K Q^T : two 32-key blocks
-    f32x16 s[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      s[b] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + (32 * b + n) * Smem::kStr + 16 * ks + 8 * hh);
-        s[b] = mfma_32x32x16(kf, qf[ks], s[b]);
+    // One pipeline step on tile j whose scores are in s_cur.  K_j sits in
+    // kcur (already consumed), K_{j+1} in knext, V_j in vcur; V_{j-1}'s
+    // buffer is vnext.  With MORE, tile j+1 exists: its scores go to s_next.
+    auto step = [&](int j, f32x16* s_cur, f32x16* s_next, __bf16* kcur, const __bf16* knext,
+                    const __bf16* vcur, __bf16* vnext, auto more_tag) {
+      constexpr bool MORE = decltype(more_tag)::value;
+      const int e = e_begin + j;
+      if constexpr (MORE) {
+        // direct loads for later tiles: K two ahead, V one ahead
+        if (j + 2 < n_tiles) dma.load_k(a, a.entries[e + 2].tile, g, kcur, w);
+        dma.load_v(a, a.entries[e + 1].tile, g, vnext, w);
       }
-    }
+      // ---- tile j: mask (PARTIAL only) and the running max
+      const DevEntry ent = a.entries[e];
+      if (ent.meta & 1) {
+        mask_tile(a.slices[ent.meta >> 1], ent.tile, row, hh, s_cur);
+        mx_cur = tile_max(s_cur);
+      }
+      // move the running max only when this tile's max exceeds it by more
+      // than 2^8 in exp2 units (all lanes together, so the branch is
+      // uniform); until then exp2 values stay <= 2^8 and O, l keep their scale
+      if (__builtin_amdgcn_ballot_w64(mx_cur > m_run + a.rescale_thr) != 0) {
+        const float m_new = fmaxf(m_run, mx_cur);
+        // rows whose max does not move keep their scale (this also covers
+        // rows that have seen nothing yet: -inf - -inf would be NaN); a row
+        // whose first visible key arrives gets exp2(-inf) = 0
+        const float alpha = (m_new == m_run) ? 1.0f : fast_exp2((m_run - m_new) * a.score_mult);
+        l_part *= alpha;
+#pragma unroll
+        for (int i = 0; i < DB; ++i) o[i] *= alpha;
+        m_run = m_new;
+      }
+      const float neg = (m_run == -INFINITY) ? 0.f : -m_run * a.score_mult;
 
-    // ---- softcap, then mask (a capped -inf would come back finite)
-    if constexpr (SOFTCAP) {
+      // ---- A: S_{j+1} = K_{j+1} Q^T on the matrix cores, while
+      //      B: the VALU turns tile j into exp2 weights
+      if constexpr (MORE) qk_tile<D>(knext, qf, n, hh, s_next);
+      u32x4 pw[4];
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int t = 0; t < 4; ++t) {
+        const int b = t >> 1, h8 = (t & 1) * 8;
+        float p[8];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) s[b][v] = a.cap_out * tanh_from_2xlog2e(s[b][v] * a.cap_in);
-    }
-    if (ent.meta & 1) {
-      const DevSlice sl = a.slices[ent.meta >> 1];
-      const int k0 = ent.tile * kBN;
-      int lo = sl.ks, hi = sl.ke;
-      if (sl.causal) hi = min(hi, row + 1 + (sl.ke - sl.qe));
-      if (row < sl.qs || row >= sl.qe) hi = lo;  // row outside the slice: nothing visible
-      lo -= k0 + 4 * hh;
-      hi -= k0 + 4 * hh;
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int off = 32 * b + 8 * (v >> 2) + (v & 3);
-          if (off < lo || off >= hi) s[b][v] = -INFINITY;
+        for (int e8 = 0; e8 < 8; ++e8) {
+          p[e8] = fast_exp2(__builtin_fmaf(s_cur[b][h8 + e8], a.score_mult, neg));
+          rs[e8 & 3] += p[e8];
         }
-    }
-
-    // ---- online softmax (row = this lane's column; other half-wave holds the rest)
-    float mx = -INFINITY;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[b][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // move the running max only when this tile's max exceeds it by more than
-    // 2^8 in exp2 units (all lanes together, so the branch is uniform); until
-    // then exp2 values stay <= 2^8 and O, l need no rescale
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + a.rescale_thr) != 0) {
-      const float m_new = fmaxf(m_run, mx);
-      // rows whose max does not move keep their scale (this also covers rows
-      // that have seen nothing yet: -inf - -inf would be NaN); a row whose
-      // first visible key arrives gets exp2(-inf) = 0
-      const float alpha = (m_new == m_run) ? 1.0f : fast_exp2((m_run - m_new) * a.score_mult);
-      l_part *= alpha;
-#pragma unroll
-      for (int i = 0; i < DB; ++i) o[i] *= alpha;
-      m_run = m_new;
-    }
-    const float neg = (m_run == -INFINITY) ? 0.f : -m_run * a.score_mult;
-    // exp2 weights; the row sum is taken in fp32 on the unrounded values (the
-    // lse must hold to 1e-3 even for rows with a handful of keys), in four
-    // independent chains
-    bf16x8 pf[4];
-    float rs[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int b = t >> 1, h8 = (t & 1) * 8;
-#pragma unroll
-      for (int e8 = 0; e8 < 8; ++e8) {
-        const float p = fast_exp2(__builtin_fmaf(s[b][h8 + e8], a.score_mult, neg));
-        rs[e8 & 3] += p;
-        pf[t][e8] = (__bf16)p;
+        for (int i = 0; i < 4; ++i) pw[t][i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);
       }
-    }
-    l_part += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+      // fp32 sum of the unrounded weights (the lse must hold to 1e-3 even
+      // for rows with a handful of keys), four independent chains
+      l_part += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 
-    // ---- O^T += V^T P^T : four k-steps of 16 keys; A = V^T by transpose reads
-    {
-      const int g16 = lane >> 4, sl = lane & 15;
-      const int col = 16 * (g16 & 1) + 4 * (sl & 3);
-      const int krow = 4 * hh + (sl >> 2);
+      // ---- C: O^T += V_j^T P_j^T (V^T fragments by transpose reads), while
+      //      B': softcap and the unmasked row max of tile j+1
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const int kb = 32 * (t >> 1) + 16 * (t & 1) + krow;
-          const __bf16* vp = vl + kb * Smem::vStr + 32 * db + col;
+          const int kb = 32 * (t >> 1) + 16 * (t & 1) + v_krow;
+          const int col_byte = 2 * (32 * db + v_col);
+          const int byte = kb * Smem::kRowBytes + (((col_byte >> 4) ^ v_sw) << 4) + (col_byte & 15);
+          const __bf16* vp = reinterpret_cast<const __bf16*>(reinterpret_cast<const char*>(vcur) + byte);
           const u32x2 lo4 = lds_read_tr16(vp);
-          const u32x2 hi4 = lds_read_tr16(vp + 8 * Smem::vStr);
+          const u32x2 hi4 = lds_read_tr16(vp + 8 * D);
           u32x4 av;
           av[0] = lo4[0]; av[1] = lo4[1]; av[2] = hi4[0]; av[3] = hi4[1];
-          o[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8, av), pf[t], o[db]);
+          o[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, pw[t]), o[db]);
         }
-    }
+      if constexpr (MORE) {
+        if constexpr (SOFTCAP) softcap_tile(a, s_next);
+        mx_cur = tile_max(s_next);
+        // Instruction order for the block above: the K reads run 4 ahead of
+        // the QK products, and the softmax VALU fills the shadow of each
+        // MFMA; then the V transpose reads run 8 ahead of the PV products,
+        // with the row max of the next tile in their shadows.
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, SOFTCAP ? 5 : 7, 0);  // VALU
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, SOFTCAP ? 8 : 2, 0);
+        }
+        // K_{j+2} and V_{j+1} have landed, and every wave is done reading
+        // K_{j+1} and V_j, whose buffers the next steps refill
+        dma_barrier();
+      }
+    };
+    using More = std::integral_constant<bool, true>;
+    using Last = std::integral_constant<bool, false>;
 
-    if (has_next) {
-      __bf16* nk = smem + (buf ^ 1) * (Smem::kBuf + Smem::vBuf);
-      ld.store(nk, nk + Smem::kBuf, tid);
+    // steady state in pairs, so the two score arrays and the buffer roles
+    // alternate without copies
+    int j = 0;
+    for (; j + 2 < n_tiles; j += 2) {
+      step(j, sa, sb, kb0, kb1, vb0, vb1, More{});
+      step(j + 1, sb, sa, kb1, kb0, vb1, vb0, More{});
     }
-    __syncthreads();
+    if (j + 1 < n_tiles) {
+      step(j, sa, sb, kb0, kb1, vb0, vb1, More{});
+      step(j + 1, sb, sa, kb1, kb0, vb1, vb0, Last{});
+    } else {
+      step(j, sa, sb, kb0, kb1, vb0, vb1, Last{});
+    }
   }
 
   // ---- epilogue: normalise once in fp32, round to bf16 once
