@@ -169,7 +169,7 @@ struct ffa_plan_s {
   int want = 0;
   size_t n_slices = 0;
   size_t off_slices = 0;
-  PlanPart fwd, kv;  // kv: per key tile (dK/dV); the dQ pass walks `fwd`
+  PlanPart fwd, kv, dq;  // forward q tiles; per key tile (dK/dV); dQ q tiles
   unsigned char* dev = nullptr;
   size_t bytes = 0;
 };
@@ -188,10 +188,6 @@ int plan_create(int64_t Tq, int64_t Tk, const int32_t* qr, const int32_t* kr, co
     m = ffa::check_disjoint(slices);
     if (!m.empty()) return fail(FFA_ERR_INVALID_ARG, m);
   }
-  // the dQ pass reuses the forward's per-q-tile list
-  if (ffa::bwd_q_tile_rows() != ffa::fwd_tile_rows() || ffa::bwd_q_tile_cols() != ffa::fwd_tile_cols())
-    return fail(FFA_ERR_UNSUPPORTED, "dQ tiles differ from forward tiles");
-
   ffa_plan_s* p = new (std::nothrow) ffa_plan_s;
   if (!p) return fail(FFA_ERR_NOMEM, "out of host memory");
   p->Tq = Tq;
@@ -206,15 +202,28 @@ int plan_create(int64_t Tq, int64_t Tk, const int32_t* qr, const int32_t* kr, co
       sl[i] = ffa::HostDevSlice{slices[i].qs, slices[i].qe, slices[i].ks, slices[i].ke,
                                 slices[i].type == ffa::kCausal ? 1 : 0, 0, 0, 0};
     ffa::Plan plan;
-    ffa::build_plan(slices, Tq, Tk, ffa::fwd_tile_rows(), ffa::fwd_tile_cols(), false, &plan);
-    if (plan.entries.size() >= (size_t(1) << 30)) {
-      delete p;
-      return fail(FFA_ERR_UNSUPPORTED, "plan has too many entries");
+    if (want & kWantFwd) {
+      ffa::build_plan(slices, Tq, Tk, ffa::fwd_tile_rows(), ffa::fwd_tile_cols(), false, &plan);
+      if (plan.entries.size() >= (size_t(1) << 30)) {
+        delete p;
+        return fail(FFA_ERR_UNSUPPORTED, "plan has too many entries");
+      }
+      append_part(plan, &img, &p->fwd);
     }
-    append_part(plan, &img, &p->fwd);
     if (want & kWantBwd) {
       ffa::build_plan(slices, Tq, Tk, ffa::bwd_kv_tile_rows(), ffa::bwd_kv_tile_cols(), true, &plan);
+      if (plan.entries.size() >= (size_t(1) << 30)) {
+        delete p;
+        return fail(FFA_ERR_UNSUPPORTED, "plan has too many entries");
+      }
       append_part(plan, &img, &p->kv);
+      if ((want & kWantFwd) && ffa::bwd_q_tile_rows() == ffa::fwd_tile_rows() &&
+          ffa::bwd_q_tile_cols() == ffa::fwd_tile_cols()) {
+        p->dq = p->fwd;  // same tiles: the dQ pass walks the forward lists
+      } else {
+        ffa::build_plan(slices, Tq, Tk, ffa::bwd_q_tile_rows(), ffa::bwd_q_tile_cols(), false, &plan);
+        append_part(plan, &img, &p->dq);
+      }
     }
   } catch (const std::bad_alloc&) {
     delete p;
@@ -247,6 +256,7 @@ int plan_destroy(ffa_plan_s* p, hipStream_t stream) {
 
 int fwd_planned(const ffa_plan_s* p, const void* q, const void* k, const void* v, int hq, int hkv,
                 int d, float scale, float softcap, void* out, float* lse, hipStream_t stream) {
+  if (!(p->want & kWantFwd)) return fail(FFA_ERR_INVALID_ARG, "plan was built without the forward lists");
   int rc = check_heads(p->Tq, p->Tk, hq, hkv, d, scale, softcap);
   if (rc != FFA_OK) return rc;
   const bool has_q = p->Tq > 0, has_k = p->Tk > 0;
@@ -301,9 +311,9 @@ int bwd_planned(const ffa_plan_s* p, const void* q, const void* k, const void* v
   L.kv_row_ptr = reinterpret_cast<const int32_t*>(p->dev + p->kv.off_row_ptr);
   L.kv_entries = p->dev + p->kv.off_entries;
   L.kv_order = reinterpret_cast<const int32_t*>(p->dev + p->kv.off_order);
-  L.q_row_ptr = reinterpret_cast<const int32_t*>(p->dev + p->fwd.off_row_ptr);
-  L.q_entries = p->dev + p->fwd.off_entries;
-  L.q_order = reinterpret_cast<const int32_t*>(p->dev + p->fwd.off_order);
+  L.q_row_ptr = reinterpret_cast<const int32_t*>(p->dev + p->dq.off_row_ptr);
+  L.q_entries = p->dev + p->dq.off_entries;
+  L.q_order = reinterpret_cast<const int32_t*>(p->dev + p->dq.off_order);
   L.slices = p->dev + p->off_slices;
   hipError_t e = ffa::launch_bwd(L, stream);
   if (ws != workspace) (void)hipFreeAsync(ws, stream);
@@ -442,7 +452,7 @@ int ffa_bwd(const void* q, const void* k, const void* v, const void* out, const 
   if (Tq == 0 && Tk == 0) return FFA_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   ffa_plan_s* p = nullptr;
-  rc = plan_create(Tq, Tk, q_ranges, k_ranges, attn_type_map, R, kWantFwd | kWantBwd, st, &p);
+  rc = plan_create(Tq, Tk, q_ranges, k_ranges, attn_type_map, R, kWantBwd, st, &p);
   if (rc != FFA_OK) return rc;
   rc = bwd_planned(p, q, k, v, out, lse, dout, hq, hkv, d, scale, softcap, dq, dk, dv, workspace,
                    workspace_bytes, st);
