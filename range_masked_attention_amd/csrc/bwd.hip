@@ -14,11 +14,21 @@
 //  bwd_dkdv  one workgroup per (128-key tile, kv head); its 4 waves own 32
 //            keys each and walk the key-side plan (64-row q tiles) for every
 //            q head of the group, accumulating dK^T and dV^T in registers.
-//  bwd_dq    one workgroup per (128-row q tile, q head), walking the same
-//            per-q-tile list as the forward and accumulating dQ^T.
+//  bwd_dq    one workgroup per (128-row q tile, q head), walking the per-q-
+//            tile list of 64-key tiles and accumulating dQ^T.
 // dQ is recomputed in its own pass instead of being scattered with atomics:
 // no fp32 accumulator buffer, no contention, and the result does not depend
 // on the order in which workgroups finish.
+//
+// Tiles of 64 rows are fetched straight into LDS (buffer_load ... lds), one
+// load instruction per 16-byte chunk column: LDS holds a tile column-major by
+// chunk, 64 rows x 16 bytes per column plus 64 bytes of padding.  Row-wise
+// MFMA operands are then 16 lanes x 16 contiguous bytes, and transposed
+// operands come from transpose reads (ds_read_b64_tr_b16) hitting 4 columns
+// 16 banks apart: neither conflicts on the 64 LDS banks.  Tiles are double
+// buffered, with one barrier per step.
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -50,70 +60,93 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const __bf16* __restr
   dvec[r] = acc;
 }
 
-// ---------------------------------------------------------------- staging
-// A ROWS x D bf16 tile read from global in units of 4 rows x 8 columns (one
-// 16-byte load per row), written to LDS row-major (stride D + 8) and/or
-// transposed (stride ROWS + 4, i.e. [column][row]).
-template <int ROWS, int D>
-struct Stage {
-  static constexpr int kRmStr = D + 8;
-  static constexpr int kTStr = ROWS + 4;
-  static constexpr int kRm = ROWS * kRmStr;  // elements
-  static constexpr int kT = D * kTStr;
-  static constexpr int kUnits = (ROWS / 4) * (D / 8);
-  static constexpr int kPerThread = (kUnits + kThreads - 1) / kThreads;
+// ---------------------------------------------------------------- tiles
+// A 64-row x D tile in LDS, fetched by direct-to-LDS loads.  One load
+// instruction fills 64 consecutive 16-byte slots (lane L -> slot L); the
+// slots of instruction i start at byte 1088 * i (1024 + 64 bytes padding).
+//   D = 128: instruction i holds rows 4i .. 4i + 3, slot L = row 4i + L % 4,
+//            chunk L / 4, so one instruction reads 4 whole rows from HBM;
+//   D = 64:  instruction i holds chunk i of all 64 rows (slot L = row L).
+// Either way the byte offset of (row, chunk) is linear in row and chunk as
+// long as the row offsets added are multiples of 4 (D = 128) -- see off() --
+// so every read address is a per-lane base plus a compile-time immediate.
+// Row operands (16 lanes, 16 consecutive rows, one chunk) and transposed
+// operands (4 rows x 4 chunks per 32 lanes) both land on 16 distinct
+// 16-byte bank groups: no LDS bank conflicts on the 64 banks.
+template <int D>
+struct ColTile {
+  static constexpr int kChunks = D / 8;
+  static constexpr int kRG = (D == 128) ? 4 : 64;       // rows per instruction group
+  static constexpr int kCS = (D == 128) ? 64 : 1088;    // bytes between chunks
+  static constexpr int kGS = 1088;                      // bytes between row groups
+  static constexpr int kBytes = kChunks * 1088;
+  static_assert(D == 64 || D == 128, "head dim");
 
-  u32x4 reg[kPerThread][4];
-
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, int64_t row_bytes, int tid) {
-#pragma unroll
-    for (int c = 0; c < kPerThread; ++c) {
-      const int u = tid + kThreads * c;
-      if (kUnits % kThreads == 0 || u < kUnits) {
-        const int cc = u / (ROWS / 4), rg = u % (ROWS / 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          reg[c][i] = buf_load16(r, (uint32_t)((4 * rg + i) * row_bytes + cc * 16));
-      }
-    }
+  __device__ __forceinline__ static constexpr int off(int row, int chunk) {
+    return (row / kRG) * kGS + chunk * kCS + (row % kRG) * 16;
   }
 
-  __device__ __forceinline__ void store(__bf16* rm, __bf16* tr, int tid) const {
-#pragma unroll
-    for (int c = 0; c < kPerThread; ++c) {
-      const int u = tid + kThreads * c;
-      if (kUnits % kThreads == 0 || u < kUnits) {
-        const int cc = u / (ROWS / 4), rg = u % (ROWS / 4);
-        if (rm) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<u32x4*>(rm + (4 * rg + i) * kRmStr + 8 * cc) = reg[c][i];
-        }
-        if (tr) {
-#pragma unroll
-          for (int p = 0; p < 8; ++p) {
-            const int sh = (p & 1) * 16;
-            u32x2 w;
-            w[0] = ((reg[c][0][p >> 1] >> sh) & 0xFFFFu) | (((reg[c][1][p >> 1] >> sh) & 0xFFFFu) << 16);
-            w[1] = ((reg[c][2][p >> 1] >> sh) & 0xFFFFu) | (((reg[c][3][p >> 1] >> sh) & 0xFFFFu) << 16);
-            *reinterpret_cast<u32x2*>(tr + (8 * cc + p) * kTStr + 4 * rg) = w;
-          }
-        }
-      }
+  // Fetch rows [0, 64) of a tile whose row r starts at byte r * row_bytes
+  // of resource `r` (rows past the resource read as zeros); wave w issues
+  // instructions w * kChunks / 4 .. +kChunks / 4.
+  __device__ __forceinline__ static void load(__amdgpu_buffer_rsrc_t r, uint32_t row_bytes, char* dst,
+                                              int w, int lane) {
+    constexpr int kPer = kChunks / 4;
+    uint32_t lane_off, step;
+    if constexpr (D == 128) {
+      lane_off = (uint32_t)(lane & 3) * row_bytes + (uint32_t)(lane >> 2) * 16;
+      step = 4 * row_bytes;
+    } else {
+      lane_off = (uint32_t)lane * row_bytes;
+      step = 16;
     }
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+      const int i = w * kPer + c;  // wave-uniform
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(dst + i * 1088), 16, lane_off + (uint32_t)i * step, 0, 0, 0);
+    }
+  }
+  // Row operand: 8 elements (16 bytes) of row r0 + n, chunk c0 + hh, with
+  // lane_row = off(n, hh) and r0 a multiple of 32, c0 even.
+  __device__ __forceinline__ static bf16x8 row8(const char* t, int lane_row, int r0, int c0) {
+    return *reinterpret_cast<const bf16x8*>(t + lane_row + off(r0, c0));
   }
 };
 
-// Reads 8 bf16 of a transposed tile: positions base..base+3 and base+8..base+11
-// of row `row` -- the key (or query) order that matches a 32x32 accumulator's
-// rows when it is reused as an MFMA operand.
-__device__ __forceinline__ bf16x8 read_t8(const __bf16* t, int row, int stride, int base) {
-  const __bf16* p = t + row * stride + base;
-  const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
-  const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 8);
+// Byte offset of this lane's transpose-read source inside a ColTile: the
+// 16-lane group g16 / index sl of lane `lane` points at row 4*hh + sl/4 and
+// 4 dims at 16*(g16 & 1) + 4*(sl & 3).  Adding the block offsets below
+// gives, in each lane, 4 consecutive rows (of the 8 the MFMA k index needs)
+// of one dim: the order of a 32x32 accumulator's rows, so the accumulator's
+// registers can be the other operand directly.
+template <int D>
+__device__ __forceinline__ int tr_lane_offset(int lane) {
+  const int hh = lane >> 5, g16 = lane >> 4, sl = lane & 15;
+  const int col = 16 * (g16 & 1) + 4 * (sl & 3);
+  return ColTile<D>::off(4 * hh + (sl >> 2), col >> 3) + (col & 7) * 2;
+}
+
+// A operand of C[dims x 32] += T^T[dims 32db.. x rows] X[rows x 32]: the
+// transposed tile T, rows 32*(t >> 1) + 16*(t & 1) + {0..3, 8..11} + 4*hh.
+template <int D>
+__device__ __forceinline__ bf16x8 tr8(const char* t, int lane_off, int db, int t4) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const int r0 = 32 * (t4 >> 1) + 16 * (t4 & 1);
+  const char* p = t + lane_off + ColTile<D>::off(r0, 4 * db);
+  const char* p8 = t + lane_off + ColTile<D>::off(r0 + 8, 4 * db);
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(const_cast<char*>(p)));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(const_cast<char*>(p8)));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
   u32x4 x;
-  x[0] = lo[0]; x[1] = lo[1]; x[2] = hi[0]; x[3] = hi[1];
+  x[0] = l2[0]; x[1] = l2[1]; x[2] = h2[0]; x[3] = h2[1];
   return __builtin_bit_cast(bf16x8, x);
+}
+
+// Wait for this wave's direct-to-LDS loads, then for the whole workgroup.
+__device__ __forceinline__ void dma_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 }
 
 // Row range of slice `sl` that key j sees: [lo, hi) (empty if hi <= lo).
@@ -167,170 +200,217 @@ __device__ __forceinline__ float score_to_t(const BwdArgs& a, float s, float* th
   }
 }
 
-// ---------------------------------------------------------------- bwd_dkdv
-constexpr int kDkvKeys = 128;  // keys per workgroup (32 per wave)
-constexpr int kDkvRows = 64;   // q rows per step
+__device__ __forceinline__ u32x4 pack8(const float* p) {
+  u32x4 w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);
+  return w;
+}
 
-template <int D>
-struct DkvSmem {
-  using St = Stage<kDkvRows, D>;
-  static constexpr int kElems = 2 * (St::kRm + St::kT);  // Q and dO, row-major + transposed
-};
+// ---------------------------------------------------------------- bwd_dkdv
+// 8 waves in 4 pairs; pair p owns keys 32p .. 32p + 31 of the 128-key tile.
+// In a pair the producer wave (w < 4) computes S = Q K^T, P and dV^T += dO^T P
+// and hands P (times 1 - tanh^2 with softcap) to its consumer wave through
+// LDS; the consumer (w >= 4) computes dP = dO V^T and, one step behind,
+// dS = P (dP - D) and dK^T += Q^T dS.  Each wave keeps one K or V fragment
+// and one accumulator (half of what one wave doing both would need), so two
+// waves fit on each SIMD and one's exponentials overlap the other's matrix
+// work.  Q tiles are triple buffered (the consumer reads tile j - 1 while
+// the producer reads tile j and tile j + 1 is in flight), dO tiles double
+// buffered; one barrier per step.
+constexpr int kDkvKeys = 128;    // keys per workgroup (32 per wave pair)
+constexpr int kDkvRows = 64;     // q rows per step
+constexpr int kDkvThreads = 512;
 
 template <int D, bool SOFTCAP>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
-  using St = Stage<kDkvRows, D>;
+__global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  using T = ColTile<D>;
   constexpr int KS = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[DkvSmem<D>::kElems];
-  __shared__ float s_lse[kDkvRows], s_dv[kDkvRows];
-  __bf16* q_rm = smem;
-  __bf16* q_t = q_rm + St::kRm;
-  __bf16* o_rm = q_t + St::kT;
-  __bf16* o_t = o_rm + St::kRm;
+  constexpr int kXchg = kDkvRows * 32 * 4;  // fp32 P of one pair and step
+  constexpr int kQOff = 0, kOOff = 3 * T::kBytes, kXOff = 5 * T::kBytes;
+  __shared__ __attribute__((aligned(1024))) char smem[5 * T::kBytes + 2 * 4 * kXchg];
+  __shared__ float s_lse[3][kDkvRows], s_dv[3][kDkvRows];
 
   const int u = blockIdx.x;
   if (u >= a.n_units) return;
   const int kt = a.order[u / a.hkv], g = u % a.hkv;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 31, hh = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pair = w & 3;
+  const bool producer = w < 4;
   const int k0 = kt * kDkvKeys;
-  const int key = k0 + 32 * w + n;  // this lane's key (accumulator column)
+  const int key = k0 + 32 * pair + n;  // this lane's key (accumulator column)
   const int64_t kv_row_bytes = (int64_t)a.hkv * D * 2;
   const int64_t q_row_bytes = (int64_t)a.hq * D * 2;
 
-  // K and V fragments of this wave's 32 keys (B operands: key n, dims 16ks + 8hh ..)
-  bf16x8 kf[KS], vf[KS];
+  // K (producer) or V (consumer) fragment of the pair's 32 keys
+  // (B operand: key n, dims 16ks + 8hh ..)
+  bf16x8 frag[KS];
   {
-    const int64_t r0 = k0 + 32 * w;
+    const int64_t r0 = k0 + 32 * pair;
     const int64_t off = (r0 * a.hkv + g) * D;
     const int64_t valid = ((int64_t)a.Tk - r0) * kv_row_bytes - (int64_t)g * D * 2;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + off, valid);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(a.v + off, valid);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc((producer ? a.k : a.v) + off, valid);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint32_t o = (uint32_t)(n * kv_row_bytes + (16 * ks + 8 * hh) * 2);
-      kf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rk, o));
-      vf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rv, o));
-    }
+    for (int ks = 0; ks < KS; ++ks)
+      frag[ks] = __builtin_bit_cast(bf16x8, buf_load16(rs, (uint32_t)(n * kv_row_bytes + (16 * ks + 8 * hh) * 2)));
   }
 
-  f32x16 dk_acc[DB], dv_acc[DB];
+  f32x16 acc[DB];  // dV^T (producer) or dK^T (consumer): rows dims, column key
 #pragma unroll
-  for (int i = 0; i < DB; ++i) dk_acc[i] = dv_acc[i] = f32x16{};
+  for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
 
   const int e_begin = a.row_ptr[kt], e_end = a.row_ptr[kt + 1];
   const int n_steps = (e_end - e_begin) * a.grp;
+  const int tro = tr_lane_offset<D>(lane);
+  const int lrow = T::off(n, hh);
 
-  St sq, so;
-  auto issue = [&](int step) {
-    const int e = e_begin + step / a.grp;
-    const int head = g * a.grp + step % a.grp;
+  // step st = (entry e, q head): producers fetch the Q tile, consumers the
+  // dO tile; wave 0 also fetches the step's lse (exp2 units) and D
+  float lse_reg = 0.f, d_reg = 0.f;
+  auto issue = [&](int st) {
+    const int e = e_begin + st / a.grp;
+    const int head = g * a.grp + st % a.grp;
     const int64_t q0 = (int64_t)a.entries[e].tile * kDkvRows;
     const int64_t off = (q0 * a.hq + head) * D;
     const int64_t valid = ((int64_t)a.Tq - q0) * q_row_bytes - (int64_t)head * D * 2;
-    sq.load(make_rsrc(a.q + off, valid), q_row_bytes, tid);
-    so.load(make_rsrc(a.dout + off, valid), q_row_bytes, tid);
-  };
-  if (n_steps > 0) issue(0);
-
-  for (int step = 0; step < n_steps; ++step) {
-    const int e = e_begin + step / a.grp;
-    const int head = g * a.grp + step % a.grp;
-    const DevEntry ent = a.entries[e];
-    const int q0 = ent.tile * kDkvRows;
-
-    __syncthreads();  // previous step's LDS reads are done
-    sq.store(q_rm, q_t, tid);
-    so.store(o_rm, o_t, tid);
+    char* dst = producer ? smem + kQOff + (st % 3) * T::kBytes : smem + kOOff + (st & 1) * T::kBytes;
+    T::load(make_rsrc((producer ? a.q : a.dout) + off, valid), (uint32_t)q_row_bytes, dst, pair, lane);
     if (tid < kDkvRows) {
-      const int r = q0 + tid;
+      const int64_t r = q0 + tid;
       const bool ok = r < a.Tq;
-      const float l = ok ? a.lse[(int64_t)r * a.hq + head] : INFINITY;
+      const float l = ok ? a.lse[r * a.hq + head] : INFINITY;
       // rows nothing sees have lse = -inf: their P must be 0, not exp(+inf)
-      s_lse[tid] = (l == -INFINITY) ? INFINITY : l * 1.4426950408889634f;
-      s_dv[tid] = ok ? a.dvec[(int64_t)r * a.hq + head] : 0.f;
+      lse_reg = (l == -INFINITY) ? INFINITY : l * 1.4426950408889634f;
+      d_reg = ok ? a.dvec[r * a.hq + head] : 0.f;
     }
-    __syncthreads();
-    if (step + 1 < n_steps) issue(step + 1);
+  };
+  auto publish = [&](int st) {
+    if (tid < kDkvRows) {
+      s_lse[st % 3][tid] = lse_reg;
+      s_dv[st % 3][tid] = d_reg;
+    }
+  };
+  if (n_steps == 0) goto epilogue;
+  issue(0);
+  publish(0);
+  dma_barrier();
 
-    // ---- S = Q K^T and dP = dO V^T : [64 q x 32 keys] as two 32-row blocks
-    f32x16 s[2], dp[2];
+  if (producer) {
+    for (int st = 0; st <= n_steps; ++st) {
+      if (st < n_steps) {
+        if (st + 1 < n_steps) issue(st + 1);
+        const DevEntry ent = a.entries[e_begin + st / a.grp];
+        const char* qt = smem + kQOff + (st % 3) * T::kBytes;
+        const char* ot = smem + kOOff + (st & 1) * T::kBytes;
+        float* xch = reinterpret_cast<float*>(smem + kXOff + ((st & 1) * 4 + pair) * kXchg);
+
+        // S = Q K^T : [64 q x 32 keys] as two 32-row blocks
+        f32x16 s[2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      s[qb] = f32x16{};
-      dp[qb] = f32x16{};
+        for (int qb = 0; qb < 2; ++qb) {
+          s[qb] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int o = (32 * qb + n) * St::kRmStr + 16 * ks + 8 * hh;
-        s[qb] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(q_rm + o), kf[ks], s[qb]);
-        dp[qb] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(o_rm + o), vf[ks], dp[qb]);
+          for (int ks = 0; ks < KS; ++ks) s[qb] = mfma_32x32x16(T::row8(qt, lrow, 32 * qb, 2 * ks), frag[ks], s[qb]);
+        }
+        // P; element (qb, v) is row 32qb + 8(v/4) + 4hh + v%4, key `key`
+        int lo = 0, hi = kDkvRows;
+        if (ent.meta & 1) {
+          const DevSlice sl = a.slices[ent.meta >> 1];
+          key_rows(sl, key, &lo, &hi);
+          lo -= ent.tile * kDkvRows;
+          hi -= ent.tile * kDkvRows;
+        }
+        u32x4 pw[4];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const int rbase = 32 * qb + 8 * v4 + 4 * hh;
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&s_lse[st % 3][rbase]);
+            f32x4 px;
+            float p4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float th;
+              const float t = score_to_t<SOFTCAP>(a, s[qb][4 * v4 + i], &th);
+              float p = fast_exp2(t - l4[i]);
+              if (rbase + i < lo || rbase + i >= hi) p = 0.f;
+              p4[i] = p;
+              px[i] = SOFTCAP ? p * (1.0f - th * th) : p;
+            }
+            *reinterpret_cast<f32x4*>(xch + ((qb * 4 + v4) * 64 + lane) * 4) = px;
+            pw[2 * qb + (v4 >> 1)][2 * (v4 & 1)] = pack_bf16x2(p4[0], p4[1]);
+            pw[2 * qb + (v4 >> 1)][2 * (v4 & 1) + 1] = pack_bf16x2(p4[2], p4[3]);
+          }
+        // dV^T += dO^T P : contraction over the 64 rows
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int t4 = 0; t4 < 4; ++t4)
+            acc[db] = mfma_32x32x16(tr8<D>(ot, tro, db, t4), __builtin_bit_cast(bf16x8, pw[t4]), acc[db]);
+        if (st + 1 < n_steps) publish(st + 1);
       }
+      dma_barrier();
     }
-
-    // ---- P and dS, element (qb, v) is row 32qb + 8(v/4) + 4hh + v%4, key `key`
-    int lo = 0, hi = kDkvRows;
-    if (ent.meta & 1) {
-      const DevSlice sl = a.slices[ent.meta >> 1];
-      key_rows(sl, key, &lo, &hi);
-      lo -= q0;
-      hi -= q0;
-    }
+  } else {
+    f32x16 dp[2];
+    for (int st = 0; st <= n_steps; ++st) {
+      if (st + 1 < n_steps) issue(st + 1);
+      if (st > 0) {
+        // dS of step st - 1 from the producer's P and the dP kept from then
+        const int sp = st - 1;
+        const char* qt = smem + kQOff + (sp % 3) * T::kBytes;
+        const float* xch = reinterpret_cast<const float*>(smem + kXOff + ((sp & 1) * 4 + pair) * kXchg);
+        u32x4 dw[4];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+        for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        const int rbase = 32 * qb + 8 * v4 + 4 * hh;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(s_lse + rbase);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(s_dv + rbase);
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const int rbase = 32 * qb + 8 * v4 + 4 * hh;
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&s_dv[sp % 3][rbase]);
+            const f32x4 px = *reinterpret_cast<const f32x4*>(xch + ((qb * 4 + v4) * 64 + lane) * 4);
+            float ds[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int v = 4 * v4 + i;
-          float th;
-          const float t = score_to_t<SOFTCAP>(a, s[qb][v], &th);
-          float p = fast_exp2(t - l4[i]);
-          if (rbase + i < lo || rbase + i >= hi) p = 0.f;
-          float ds = p * (dp[qb][v] - d4[i]);
-          if constexpr (SOFTCAP) ds *= 1.0f - th * th;
-          s[qb][v] = p;
-          dp[qb][v] = ds;
+            for (int i = 0; i < 4; ++i) ds[i] = px[i] * (dp[qb][4 * v4 + i] - d4[i]);
+            dw[2 * qb + (v4 >> 1)][2 * (v4 & 1)] = pack_bf16x2(ds[0], ds[1]);
+            dw[2 * qb + (v4 >> 1)][2 * (v4 & 1) + 1] = pack_bf16x2(ds[2], ds[3]);
+          }
+        // dK^T += Q^T dS
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int t4 = 0; t4 < 4; ++t4)
+            acc[db] = mfma_32x32x16(tr8<D>(qt, tro, db, t4), __builtin_bit_cast(bf16x8, dw[t4]), acc[db]);
+      }
+      if (st < n_steps) {
+        // dP = dO V^T of this step, used next step
+        const char* ot = smem + kOOff + (st & 1) * T::kBytes;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          dp[qb] = f32x16{};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) dp[qb] = mfma_32x32x16(T::row8(ot, lrow, 32 * qb, 2 * ks), frag[ks], dp[qb]);
         }
       }
-
-    // ---- dV^T += dO^T P and dK^T += Q^T dS : contraction over the 64 rows
-    bf16x8 pf[4], df[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int qb = t >> 1, h8 = (t & 1) * 8;
-#pragma unroll
-      for (int e8 = 0; e8 < 8; ++e8) {
-        pf[t][e8] = (__bf16)s[qb][h8 + e8];
-        df[t][e8] = (__bf16)dp[qb][h8 + e8];
-      }
+      dma_barrier();
     }
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int base = 32 * (t >> 1) + 16 * (t & 1) + 4 * hh;
-        dv_acc[db] = mfma_32x32x16(read_t8(o_t, 32 * db + n, St::kTStr, base), pf[t], dv_acc[db]);
-        dk_acc[db] = mfma_32x32x16(read_t8(q_t, 32 * db + n, St::kTStr, base), df[t], dk_acc[db]);
-      }
   }
 
-  // ---- epilogue: accumulator column n is key `key`, rows are head dims
+epilogue:
+  // accumulator column n is key `key`, rows are head dims
   if (key < a.Tk) {
     const int64_t off = ((int64_t)key * a.hkv + g) * D;
+    __bf16* dst = producer ? a.dv : a.dk;
+    const float mul = producer ? 1.0f : a.scale;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int d0 = 32 * db + 8 * j + 4 * hh;
-        u32x2 wv, wk;
-        wv[0] = pack_bf16x2(dv_acc[db][4 * j + 0], dv_acc[db][4 * j + 1]);
-        wv[1] = pack_bf16x2(dv_acc[db][4 * j + 2], dv_acc[db][4 * j + 3]);
-        wk[0] = pack_bf16x2(a.scale * dk_acc[db][4 * j + 0], a.scale * dk_acc[db][4 * j + 1]);
-        wk[1] = pack_bf16x2(a.scale * dk_acc[db][4 * j + 2], a.scale * dk_acc[db][4 * j + 3]);
-        *reinterpret_cast<u32x2*>(a.dv + off + d0) = wv;
-        *reinterpret_cast<u32x2*>(a.dk + off + d0) = wk;
+        u32x2 wv;
+        wv[0] = pack_bf16x2(mul * acc[db][4 * j + 0], mul * acc[db][4 * j + 1]);
+        wv[1] = pack_bf16x2(mul * acc[db][4 * j + 2], mul * acc[db][4 * j + 3]);
+        *reinterpret_cast<u32x2*>(dst + off + 32 * db + 8 * j + 4 * hh) = wv;
       }
   }
 }
@@ -339,20 +419,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 constexpr int kDqRows = 128;  // q rows per workgroup (32 per wave)
 constexpr int kDqKeys = 64;   // keys per k tile
 
-template <int D>
-struct DqSmem {
-  using St = Stage<kDqKeys, D>;
-  static constexpr int kElems = 2 * St::kRm + St::kT;  // K row-major + transposed, V row-major
-};
-
 template <int D, bool SOFTCAP>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
-  using St = Stage<kDqKeys, D>;
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
+  using T = ColTile<D>;
   constexpr int KS = D / 16, DB = D / 32;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[DqSmem<D>::kElems];
-  __bf16* k_rm = smem;
-  __bf16* k_t = k_rm + St::kRm;
-  __bf16* v_rm = k_t + St::kT;
+  constexpr int kBuf = 2 * T::kBytes;  // K and V of one k tile
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kBuf];
 
   // work item: (q tile, head), q heads of one kv head on one XCD
   const int wg = blockIdx.x;
@@ -394,35 +466,38 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
 
   const int e_begin = a.row_ptr[qt], e_end = a.row_ptr[qt + 1];
-  St sk, sv;
-  auto issue = [&](int e) {
+  const int tro = tr_lane_offset<D>(lane);
+  const int lrow = T::off(n, hh);
+  auto issue = [&](int e, int b) {
     const int64_t k0 = (int64_t)a.entries[e].tile * kDqKeys;
     const int64_t off = (k0 * a.hkv + g) * D;
     const int64_t valid = ((int64_t)a.Tk - k0) * kv_row_bytes - (int64_t)g * D * 2;
-    sk.load(make_rsrc(a.k + off, valid), kv_row_bytes, tid);
-    sv.load(make_rsrc(a.v + off, valid), kv_row_bytes, tid);
+    char* buf = smem + b * kBuf;
+    T::load(make_rsrc(a.k + off, valid), (uint32_t)kv_row_bytes, buf, w, lane);
+    T::load(make_rsrc(a.v + off, valid), (uint32_t)kv_row_bytes, buf + T::kBytes, w, lane);
   };
-  if (e_begin < e_end) issue(e_begin);
+  if (e_begin < e_end) {
+    issue(e_begin, 0);
+    dma_barrier();
+  }
 
   for (int e = e_begin; e < e_end; ++e) {
+    const int b = (e - e_begin) & 1;
     const DevEntry ent = a.entries[e];
-    __syncthreads();
-    sk.store(k_rm, k_t, tid);
-    sv.store(v_rm, nullptr, tid);
-    __syncthreads();
-    if (e + 1 < e_end) issue(e + 1);
+    if (e + 1 < e_end) issue(e + 1, b ^ 1);
+    const char* kt = smem + b * kBuf;
+    const char* vt = kt + T::kBytes;
 
     // ---- S^T = K Q^T and dP^T = V dO^T : [64 keys x 32 q]
     f32x16 s[2], dp[2];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      s[b] = f32x16{};
-      dp[b] = f32x16{};
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int o = (32 * b + n) * St::kRmStr + 16 * ks + 8 * hh;
-        s[b] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(k_rm + o), qf[ks], s[b]);
-        dp[b] = mfma_32x32x16(*reinterpret_cast<const bf16x8*>(v_rm + o), of[ks], dp[b]);
+        s[kb] = mfma_32x32x16(T::row8(kt, lrow, 32 * kb, 2 * ks), qf[ks], s[kb]);
+        dp[kb] = mfma_32x32x16(T::row8(vt, lrow, 32 * kb, 2 * ks), of[ks], dp[kb]);
       }
     }
 
@@ -433,35 +508,34 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
       lo -= ent.tile * kDqKeys + 4 * hh;
       hi -= ent.tile * kDqKeys + 4 * hh;
     }
+    u32x4 dw[4];
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int t4 = 0; t4 < 4; ++t4) {
+      const int kb = t4 >> 1, h8 = (t4 & 1) * 8;
+      float d8[8];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int off = 32 * b + 8 * (v >> 2) + (v & 3);
+      for (int e8 = 0; e8 < 8; ++e8) {
+        const int v = h8 + e8;
+        const int off = 32 * kb + 8 * (v >> 2) + (v & 3);
         float th;
-        const float t = score_to_t<SOFTCAP>(a, s[b][v], &th);
+        const float t = score_to_t<SOFTCAP>(a, s[kb][v], &th);
         float p = fast_exp2(t - lse2);
         if (off < lo || off >= hi) p = 0.f;
-        float ds = p * (dp[b][v] - dval);
+        float ds = p * (dp[kb][v] - dval);
         if constexpr (SOFTCAP) ds *= 1.0f - th * th;
-        s[b][v] = ds;
+        d8[e8] = ds;
       }
+      dw[t4] = pack8(d8);
+    }
 
     // ---- dQ^T += K^T dS^T : contraction over the 64 keys
-    bf16x8 df[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int b = t >> 1, h8 = (t & 1) * 8;
-#pragma unroll
-      for (int e8 = 0; e8 < 8; ++e8) df[t][e8] = (__bf16)s[b][h8 + e8];
-    }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int base = 32 * (t >> 1) + 16 * (t & 1) + 4 * hh;
-        acc[db] = mfma_32x32x16(read_t8(k_t, 32 * db + n, St::kTStr, base), df[t], acc[db]);
-      }
+      for (int t4 = 0; t4 < 4; ++t4)
+        acc[db] = mfma_32x32x16(tr8<D>(kt, tro, db, t4), __builtin_bit_cast(bf16x8, dw[t4]), acc[db]);
+
+    dma_barrier();
   }
 
   if (row < a.Tq) {
@@ -522,7 +596,7 @@ hipError_t launch_bwd_t(const BwdLaunch& p, hipStream_t stream) {
   const int64_t n_kt = (p.Tk + kDkvKeys - 1) / kDkvKeys;
   a.n_units = (int32_t)(n_kt * p.hkv);
   if (a.n_units > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, SC>), dim3((unsigned)a.n_units), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, SC>), dim3((unsigned)a.n_units), dim3(kDkvThreads), 0, stream, a);
   // dQ: one workgroup per (q tile, head)
   a.row_ptr = p.q_row_ptr;
   a.entries = reinterpret_cast<const DevEntry*>(p.q_entries);
