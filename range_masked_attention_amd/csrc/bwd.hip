@@ -217,23 +217,42 @@ __device__ __forceinline__ u32x4 pack8(const float* p) {
 // waves fit on each SIMD and one's exponentials overlap the other's matrix
 // work.  Q tiles are triple buffered (the consumer reads tile j - 1 while
 // the producer reads tile j and tile j + 1 is in flight), dO tiles double
-// buffered; one barrier per step.
+// buffered; one barrier per step.  Each buffer is its own LDS object and the
+// step loops are unrolled six times so that every access names its buffer
+// at compile time: the compiler then knows a read of one buffer does not
+// depend on a fetch into another and does not wait for it.
 constexpr int kDkvKeys = 128;    // keys per workgroup (32 per wave pair)
 constexpr int kDkvRows = 64;     // q rows per step
 constexpr int kDkvThreads = 512;
+
+template <int R>
+using IC = std::integral_constant<int, R>;
 
 template <int D, bool SOFTCAP>
 __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using T = ColTile<D>;
   constexpr int KS = D / 16, DB = D / 32;
-  constexpr int kXchg = kDkvRows * 32 * 4;  // fp32 P of one pair and step
-  constexpr int kQOff = 0, kOOff = 3 * T::kBytes, kXOff = 5 * T::kBytes;
-  __shared__ __attribute__((aligned(1024))) char smem[5 * T::kBytes + 2 * 4 * kXchg];
+  constexpr int kXchg = kDkvRows * 32;  // fp32 P of one pair and step (floats)
+  __shared__ __attribute__((aligned(1024))) char q_s0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char q_s1[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char q_s2[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char o_s0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char o_s1[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) float xchg[2][4][kXchg];
   __shared__ float s_lse[3][kDkvRows], s_dv[3][kDkvRows];
+  auto qbuf = [&](auto r) -> char* {
+    if constexpr (decltype(r)::value % 3 == 0) return q_s0;
+    else if constexpr (decltype(r)::value % 3 == 1) return q_s1;
+    else return q_s2;
+  };
+  auto obuf = [&](auto r) -> char* {
+    if constexpr (decltype(r)::value % 2 == 0) return o_s0;
+    else return o_s1;
+  };
 
   const int u = blockIdx.x;
   if (u >= a.n_units) return;
-  const int kt = a.order[u / a.hkv], g = u % a.hkv;
+  const int kt = plan_i32(a.order, u / a.hkv), g = u % a.hkv;
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, hh = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pair = w & 3;
@@ -260,144 +279,175 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
 
-  const int e_begin = a.row_ptr[kt], e_end = a.row_ptr[kt + 1];
+  const int e_begin = plan_i32(a.row_ptr, kt), e_end = plan_i32(a.row_ptr, kt + 1);
   const int n_steps = (e_end - e_begin) * a.grp;
   const int tro = tr_lane_offset<D>(lane);
   const int lrow = T::off(n, hh);
 
   // step st = (entry e, q head): producers fetch the Q tile, consumers the
-  // dO tile; wave 0 also fetches the step's lse (exp2 units) and D
-  float lse_reg = 0.f, d_reg = 0.f;
-  auto issue = [&](int st) {
+  // dO tile; wave 0 also fetches the step's lse and D (first, so that a
+  // wait for them never waits for the tile fetches behind them)
+  float lse_raw = 0.f, d_raw = 0.f;
+  auto issue = [&](int st, char* dst) {
     const int e = e_begin + st / a.grp;
     const int head = g * a.grp + st % a.grp;
-    const int64_t q0 = (int64_t)a.entries[e].tile * kDkvRows;
-    const int64_t off = (q0 * a.hq + head) * D;
-    const int64_t valid = ((int64_t)a.Tq - q0) * q_row_bytes - (int64_t)head * D * 2;
-    char* dst = producer ? smem + kQOff + (st % 3) * T::kBytes : smem + kOOff + (st & 1) * T::kBytes;
-    T::load(make_rsrc((producer ? a.q : a.dout) + off, valid), (uint32_t)q_row_bytes, dst, pair, lane);
+    const int64_t q0 = (int64_t)plan_entry(a.entries, e).tile * kDkvRows;
     if (tid < kDkvRows) {
       const int64_t r = q0 + tid;
-      const bool ok = r < a.Tq;
-      const float l = ok ? a.lse[r * a.hq + head] : INFINITY;
-      // rows nothing sees have lse = -inf: their P must be 0, not exp(+inf)
-      lse_reg = (l == -INFINITY) ? INFINITY : l * 1.4426950408889634f;
-      d_reg = ok ? a.dvec[r * a.hq + head] : 0.f;
+      lse_raw = INFINITY;
+      d_raw = 0.f;
+      if (r < a.Tq) {
+        lse_raw = a.lse[r * a.hq + head];
+        d_raw = a.dvec[r * a.hq + head];
+      }
     }
+    const int64_t off = (q0 * a.hq + head) * D;
+    const int64_t valid = ((int64_t)a.Tq - q0) * q_row_bytes - (int64_t)head * D * 2;
+    T::load(make_rsrc((producer ? a.q : a.dout) + off, valid), (uint32_t)q_row_bytes, dst, pair, lane);
   };
   auto publish = [&](int st) {
     if (tid < kDkvRows) {
-      s_lse[st % 3][tid] = lse_reg;
-      s_dv[st % 3][tid] = d_reg;
+      // lse in exp2 units; rows nothing sees have lse = -inf and their P
+      // must be 0, not exp(+inf)
+      s_lse[st % 3][tid] = (lse_raw == -INFINITY) ? INFINITY : lse_raw * 1.4426950408889634f;
+      s_dv[st % 3][tid] = d_raw;
     }
   };
-  if (n_steps == 0) goto epilogue;
-  issue(0);
-  publish(0);
-  dma_barrier();
 
-  if (producer) {
-    for (int st = 0; st <= n_steps; ++st) {
-      if (st < n_steps) {
-        if (st + 1 < n_steps) issue(st + 1);
-        const DevEntry ent = a.entries[e_begin + st / a.grp];
-        const char* qt = smem + kQOff + (st % 3) * T::kBytes;
-        const char* ot = smem + kOOff + (st & 1) * T::kBytes;
-        float* xch = reinterpret_cast<float*>(smem + kXOff + ((st & 1) * 4 + pair) * kXchg);
+  // producer step st (st == n_steps: nothing left but the barrier)
+  auto pstep = [&](int st, auto r) {
+    if (st < n_steps) {
+      if (st + 1 < n_steps) issue(st + 1, qbuf(IC<decltype(r)::value + 1>{}));
+      const DevEntry ent = plan_entry(a.entries, e_begin + st / a.grp);
+      const char* qt = qbuf(r);
+      const char* ot = obuf(r);
+      float* xch = xchg[st & 1][pair];
 
-        // S = Q K^T : [64 q x 32 keys] as two 32-row blocks
-        f32x16 s[2];
+      // S = Q K^T : [64 q x 32 keys] as two 32-row blocks
+      f32x16 s[2];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          s[qb] = f32x16{};
+      for (int qb = 0; qb < 2; ++qb) {
+        s[qb] = f32x16{};
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) s[qb] = mfma_32x32x16(T::row8(qt, lrow, 32 * qb, 2 * ks), frag[ks], s[qb]);
-        }
-        // P; element (qb, v) is row 32qb + 8(v/4) + 4hh + v%4, key `key`
-        int lo = 0, hi = kDkvRows;
-        if (ent.meta & 1) {
-          const DevSlice sl = a.slices[ent.meta >> 1];
-          key_rows(sl, key, &lo, &hi);
-          lo -= ent.tile * kDkvRows;
-          hi -= ent.tile * kDkvRows;
-        }
-        u32x4 pw[4];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4) {
-            const int rbase = 32 * qb + 8 * v4 + 4 * hh;
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&s_lse[st % 3][rbase]);
-            f32x4 px;
-            float p4[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              float th;
-              const float t = score_to_t<SOFTCAP>(a, s[qb][4 * v4 + i], &th);
-              float p = fast_exp2(t - l4[i]);
-              if (rbase + i < lo || rbase + i >= hi) p = 0.f;
-              p4[i] = p;
-              px[i] = SOFTCAP ? p * (1.0f - th * th) : p;
-            }
-            *reinterpret_cast<f32x4*>(xch + ((qb * 4 + v4) * 64 + lane) * 4) = px;
-            pw[2 * qb + (v4 >> 1)][2 * (v4 & 1)] = pack_bf16x2(p4[0], p4[1]);
-            pw[2 * qb + (v4 >> 1)][2 * (v4 & 1) + 1] = pack_bf16x2(p4[2], p4[3]);
-          }
-        // dV^T += dO^T P : contraction over the 64 rows
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int t4 = 0; t4 < 4; ++t4)
-            acc[db] = mfma_32x32x16(tr8<D>(ot, tro, db, t4), __builtin_bit_cast(bf16x8, pw[t4]), acc[db]);
-        if (st + 1 < n_steps) publish(st + 1);
+        for (int ks = 0; ks < KS; ++ks) s[qb] = mfma_32x32x16(T::row8(qt, lrow, 32 * qb, 2 * ks), frag[ks], s[qb]);
       }
-      dma_barrier();
+      // P; element (qb, v) is row 32qb + 8(v/4) + 4hh + v%4, key `key`
+      int lo = 0, hi = kDkvRows;
+      if (ent.meta & 1) {
+        const DevSlice sl = plan_slice(a.slices, ent.meta >> 1);
+        key_rows(sl, key, &lo, &hi);
+        lo -= ent.tile * kDkvRows;
+        hi -= ent.tile * kDkvRows;
+      }
+      u32x4 pw[4];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const int rbase = 32 * qb + 8 * v4 + 4 * hh;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&s_lse[st % 3][rbase]);
+          f32x4 px;
+          float p4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float th;
+            const float t = score_to_t<SOFTCAP>(a, s[qb][4 * v4 + i], &th);
+            float p = fast_exp2(t - l4[i]);
+            if (rbase + i < lo || rbase + i >= hi) p = 0.f;
+            p4[i] = p;
+            px[i] = SOFTCAP ? p * (1.0f - th * th) : p;
+          }
+          *reinterpret_cast<f32x4*>(xch + ((qb * 4 + v4) * 64 + lane) * 4) = px;
+          pw[2 * qb + (v4 >> 1)][2 * (v4 & 1)] = pack_bf16x2(p4[0], p4[1]);
+          pw[2 * qb + (v4 >> 1)][2 * (v4 & 1) + 1] = pack_bf16x2(p4[2], p4[3]);
+        }
+      // dV^T += dO^T P : contraction over the 64 rows
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4)
+          acc[db] = mfma_32x32x16(tr8<D>(ot, tro, db, t4), __builtin_bit_cast(bf16x8, pw[t4]), acc[db]);
+      if (st + 1 < n_steps) publish(st + 1);
     }
-  } else {
-    f32x16 dp[2];
-    for (int st = 0; st <= n_steps; ++st) {
-      if (st + 1 < n_steps) issue(st + 1);
-      if (st > 0) {
-        // dS of step st - 1 from the producer's P and the dP kept from then
-        const int sp = st - 1;
-        const char* qt = smem + kQOff + (sp % 3) * T::kBytes;
-        const float* xch = reinterpret_cast<const float*>(smem + kXOff + ((sp & 1) * 4 + pair) * kXchg);
-        u32x4 dw[4];
+    dma_barrier();
+  };
+
+  // consumer step st: dS, dK of step st - 1, then dP of step st
+  f32x16 dp[2];
+  auto cstep = [&](int st, auto r) {
+    if (st + 1 < n_steps) issue(st + 1, obuf(IC<decltype(r)::value + 1>{}));
+    if (st > 0) {
+      const float* xch = xchg[(st - 1) & 1][pair];
+      const char* qt = qbuf(IC<decltype(r)::value + 5>{});  // tile st - 1
+      u32x4 dw[4];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4) {
-            const int rbase = 32 * qb + 8 * v4 + 4 * hh;
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(&s_dv[sp % 3][rbase]);
-            const f32x4 px = *reinterpret_cast<const f32x4*>(xch + ((qb * 4 + v4) * 64 + lane) * 4);
-            float ds[4];
+        for (int v4 = 0; v4 < 4; ++v4) {
+          const int rbase = 32 * qb + 8 * v4 + 4 * hh;
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&s_dv[(st - 1) % 3][rbase]);
+          const f32x4 px = *reinterpret_cast<const f32x4*>(xch + ((qb * 4 + v4) * 64 + lane) * 4);
+          float ds[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ds[i] = px[i] * (dp[qb][4 * v4 + i] - d4[i]);
-            dw[2 * qb + (v4 >> 1)][2 * (v4 & 1)] = pack_bf16x2(ds[0], ds[1]);
-            dw[2 * qb + (v4 >> 1)][2 * (v4 & 1) + 1] = pack_bf16x2(ds[2], ds[3]);
-          }
-        // dK^T += Q^T dS
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int t4 = 0; t4 < 4; ++t4)
-            acc[db] = mfma_32x32x16(tr8<D>(qt, tro, db, t4), __builtin_bit_cast(bf16x8, dw[t4]), acc[db]);
-      }
-      if (st < n_steps) {
-        // dP = dO V^T of this step, used next step
-        const char* ot = smem + kOOff + (st & 1) * T::kBytes;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          dp[qb] = f32x16{};
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) dp[qb] = mfma_32x32x16(T::row8(ot, lrow, 32 * qb, 2 * ks), frag[ks], dp[qb]);
+          for (int i = 0; i < 4; ++i) ds[i] = px[i] * (dp[qb][4 * v4 + i] - d4[i]);
+          dw[2 * qb + (v4 >> 1)][2 * (v4 & 1)] = pack_bf16x2(ds[0], ds[1]);
+          dw[2 * qb + (v4 >> 1)][2 * (v4 & 1) + 1] = pack_bf16x2(ds[2], ds[3]);
         }
+      // dK^T += Q^T dS
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int t4 = 0; t4 < 4; ++t4)
+          acc[db] = mfma_32x32x16(tr8<D>(qt, tro, db, t4), __builtin_bit_cast(bf16x8, dw[t4]), acc[db]);
+    }
+    if (st < n_steps) {
+      const char* ot = obuf(r);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        dp[qb] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) dp[qb] = mfma_32x32x16(T::row8(ot, lrow, 32 * qb, 2 * ks), frag[ks], dp[qb]);
       }
-      dma_barrier();
+    }
+    dma_barrier();
+  };
+
+  if (n_steps > 0) {
+    issue(0, producer ? qbuf(IC<0>{}) : obuf(IC<0>{}));
+    publish(0);
+    dma_barrier();
+    // n_steps + 1 steps in both roles, so both pass the same barriers
+    if (producer) {
+      for (int st = 0; st <= n_steps; st += 6) {
+        pstep(st, IC<0>{});
+        if (st + 1 > n_steps) break;
+        pstep(st + 1, IC<1>{});
+        if (st + 2 > n_steps) break;
+        pstep(st + 2, IC<2>{});
+        if (st + 3 > n_steps) break;
+        pstep(st + 3, IC<3>{});
+        if (st + 4 > n_steps) break;
+        pstep(st + 4, IC<4>{});
+        if (st + 5 > n_steps) break;
+        pstep(st + 5, IC<5>{});
+      }
+    } else {
+      for (int st = 0; st <= n_steps; st += 6) {
+        cstep(st, IC<0>{});
+        if (st + 1 > n_steps) break;
+        cstep(st + 1, IC<1>{});
+        if (st + 2 > n_steps) break;
+        cstep(st + 2, IC<2>{});
+        if (st + 3 > n_steps) break;
+        cstep(st + 3, IC<3>{});
+        if (st + 4 > n_steps) break;
+        cstep(st + 4, IC<4>{});
+        if (st + 5 > n_steps) break;
+        cstep(st + 5, IC<5>{});
+      }
     }
   }
 
-epilogue:
   // accumulator column n is key `key`, rows are head dims
   if (key < a.Tk) {
     const int64_t off = ((int64_t)key * a.hkv + g) * D;
@@ -416,6 +466,8 @@ epilogue:
 }
 
 // ---------------------------------------------------------------- bwd_dq
+// K and V tiles double buffered in four LDS objects, loop unrolled twice so
+// each access names its buffer at compile time (see the dK/dV kernel).
 constexpr int kDqRows = 128;  // q rows per workgroup (32 per wave)
 constexpr int kDqKeys = 64;   // keys per k tile
 
@@ -423,8 +475,10 @@ template <int D, bool SOFTCAP>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   using T = ColTile<D>;
   constexpr int KS = D / 16, DB = D / 32;
-  constexpr int kBuf = 2 * T::kBytes;  // K and V of one k tile
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kBuf];
+  __shared__ __attribute__((aligned(1024))) char k_s0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char k_s1[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char v_s0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char v_s1[T::kBytes];
 
   // work item: (q tile, head), q heads of one kv head on one XCD
   const int wg = blockIdx.x;
@@ -432,9 +486,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const int r = slot % a.grp;
   const int u = (slot / a.grp) * 8 + xcd;
   if (u >= a.n_units) return;
-  const int qt = a.order[u / a.hkv], g = u % a.hkv, head = g * a.grp + r;
+  const int qt = plan_i32(a.order, u / a.hkv), g = u % a.hkv, head = g * a.grp + r;
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, n = lane & 31, hh = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q0 = qt * kDqRows;
   const int row = q0 + 32 * w + n;
   const int64_t q_row_bytes = (int64_t)a.hq * D * 2;
@@ -465,28 +520,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
 
-  const int e_begin = a.row_ptr[qt], e_end = a.row_ptr[qt + 1];
+  const int e_begin = plan_i32(a.row_ptr, qt), e_end = plan_i32(a.row_ptr, qt + 1);
   const int tro = tr_lane_offset<D>(lane);
   const int lrow = T::off(n, hh);
-  auto issue = [&](int e, int b) {
-    const int64_t k0 = (int64_t)a.entries[e].tile * kDqKeys;
+  auto issue = [&](int e, char* kd, char* vd) {
+    const int64_t k0 = (int64_t)plan_entry(a.entries, e).tile * kDqKeys;
     const int64_t off = (k0 * a.hkv + g) * D;
     const int64_t valid = ((int64_t)a.Tk - k0) * kv_row_bytes - (int64_t)g * D * 2;
-    char* buf = smem + b * kBuf;
-    T::load(make_rsrc(a.k + off, valid), (uint32_t)kv_row_bytes, buf, w, lane);
-    T::load(make_rsrc(a.v + off, valid), (uint32_t)kv_row_bytes, buf + T::kBytes, w, lane);
+    T::load(make_rsrc(a.k + off, valid), (uint32_t)kv_row_bytes, kd, w, lane);
+    T::load(make_rsrc(a.v + off, valid), (uint32_t)kv_row_bytes, vd, w, lane);
   };
-  if (e_begin < e_end) {
-    issue(e_begin, 0);
-    dma_barrier();
-  }
 
-  for (int e = e_begin; e < e_end; ++e) {
-    const int b = (e - e_begin) & 1;
-    const DevEntry ent = a.entries[e];
-    if (e + 1 < e_end) issue(e + 1, b ^ 1);
-    const char* kt = smem + b * kBuf;
-    const char* vt = kt + T::kBytes;
+  auto step = [&](int e, const char* kt, const char* vt, char* kn, char* vn) {
+    const DevEntry ent = plan_entry(a.entries, e);
+    if (e + 1 < e_end) issue(e + 1, kn, vn);
 
     // ---- S^T = K Q^T and dP^T = V dO^T : [64 keys x 32 q]
     f32x16 s[2], dp[2];
@@ -503,7 +550,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 
     int lo = 0, hi = kDqKeys;
     if (ent.meta & 1) {
-      const DevSlice sl = a.slices[ent.meta >> 1];
+      const DevSlice sl = plan_slice(a.slices, ent.meta >> 1);
       row_keys(sl, row, &lo, &hi);
       lo -= ent.tile * kDqKeys + 4 * hh;
       hi -= ent.tile * kDqKeys + 4 * hh;
@@ -536,6 +583,16 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         acc[db] = mfma_32x32x16(tr8<D>(kt, tro, db, t4), __builtin_bit_cast(bf16x8, dw[t4]), acc[db]);
 
     dma_barrier();
+  };
+
+  if (e_begin < e_end) {
+    issue(e_begin, k_s0, v_s0);
+    dma_barrier();
+    for (int e = e_begin; e < e_end; e += 2) {
+      step(e, k_s0, v_s0, k_s1, v_s1);
+      if (e + 1 >= e_end) break;
+      step(e + 1, k_s1, v_s1, k_s0, v_s0);
+    }
   }
 
   if (row < a.Tq) {

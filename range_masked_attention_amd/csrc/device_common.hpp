@@ -50,6 +50,23 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
   return __builtin_bit_cast(u32x4, x);
 }
 
+// The plan (offsets, entries, slices, order) stays unchanged while a kernel
+// runs.  Reading it through the constant address space lets the compiler use
+// scalar loads for wave-uniform indices: those count on lgkmcnt, so waiting
+// for an entry never also waits for the tile fetches in flight on vmcnt.
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+template <typename V>
+__device__ __forceinline__ V const_load(const void* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) V*)(p))[i];
+}
+__device__ __forceinline__ int32_t plan_i32(const int32_t* p, int64_t i) { return const_load<int32_t>(p, i); }
+__device__ __forceinline__ DevEntry plan_entry(const DevEntry* p, int64_t i) {
+  return __builtin_bit_cast(DevEntry, const_load<u32x2>(p, i));
+}
+__device__ __forceinline__ DevSlice plan_slice(const DevSlice* p, int64_t i) {
+  return __builtin_bit_cast(DevSlice, const_load<i32x8>(p, i));
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }

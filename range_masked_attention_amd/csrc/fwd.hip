@@ -82,7 +82,7 @@ __device__ __forceinline__ bool decode_item(const FwdArgs& a, int* qt, int* head
   const int r = slot % a.grp;
   const int u = (slot / a.grp) * 8 + xcd;
   if (u >= a.n_units) return false;
-  *qt = a.order[u / a.hkv];
+  *qt = plan_i32(a.order, u / a.hkv);
   *g = u % a.hkv;
   *head = *g * a.grp + r;
   return true;
@@ -213,14 +213,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   constexpr int KS = D / 16;  // k steps of the QK^T contraction
   constexpr int DB = D / 32;  // 32-wide blocks of the head dim in O^T
   constexpr int kTileElems = Smem::kTileBytes / 2;
-  __shared__ __attribute__((aligned(1024))) __bf16 smem[Smem::kElems];
-  // K[0], K[1], V[0], V[1]
+  // K and V double buffers as separate LDS objects: the compiler can then
+  // tell a direct-to-LDS fetch into one buffer from reads of another and
+  // does not make those reads wait for the fetch
+  __shared__ __attribute__((aligned(1024))) __bf16 kb0[kTileElems];
+  __shared__ __attribute__((aligned(1024))) __bf16 kb1[kTileElems];
+  __shared__ __attribute__((aligned(1024))) __bf16 vb0[kTileElems];
+  __shared__ __attribute__((aligned(1024))) __bf16 vb1[kTileElems];
 
   int qt, head, g;
   if (!decode_item(a, &qt, &head, &g)) return;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, n = lane & 31, hh = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, n = lane & 31, hh = lane >> 5;
   const int q0 = qt * kBM;
   const int row = q0 + w * 32 + n;  // the query row this lane's column holds
   const int64_t q_row_bytes = (int64_t)a.hq * D * 2;
@@ -237,7 +242,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
       qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(n * q_row_bytes + (16 * ks + 8 * hh) * 2)));
   }
 
-  const int e_begin = a.row_ptr[qt], e_end = a.row_ptr[qt + 1];
+  const int e_begin = plan_i32(a.row_ptr, qt), e_end = plan_i32(a.row_ptr, qt + 1);
   const int n_tiles = e_end - e_begin;
 
   f32x16 o[DB];
@@ -256,14 +261,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   if (n_tiles > 0) {
     TileDma<D> dma;
     dma.init(a, lane);
-    __bf16* const kb0 = smem;
-    __bf16* const kb1 = smem + kTileElems;
-    __bf16* const vb0 = smem + 2 * kTileElems;
-    __bf16* const vb1 = smem + 3 * kTileElems;
     // ---- prologue: K0, V0 and K1 in LDS; S0 and its row max
-    dma.load_k(a, a.entries[e_begin].tile, g, kb0, w);
-    dma.load_v(a, a.entries[e_begin].tile, g, vb0, w);
-    if (n_tiles > 1) dma.load_k(a, a.entries[e_begin + 1].tile, g, kb1, w);
+    dma.load_k(a, plan_entry(a.entries, e_begin).tile, g, kb0, w);
+    dma.load_v(a, plan_entry(a.entries, e_begin).tile, g, vb0, w);
+    if (n_tiles > 1) dma.load_k(a, plan_entry(a.entries, e_begin + 1).tile, g, kb1, w);
     dma_barrier();
     f32x16 sa[2], sb[2];
     qk_tile<D>(kb0, qf, n, hh, sa);
@@ -280,13 +281,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
       const int e = e_begin + j;
       if constexpr (MORE) {
         // direct loads for later tiles: K two ahead, V one ahead
-        if (j + 2 < n_tiles) dma.load_k(a, a.entries[e + 2].tile, g, kcur, w);
-        dma.load_v(a, a.entries[e + 1].tile, g, vnext, w);
+        if (j + 2 < n_tiles) dma.load_k(a, plan_entry(a.entries, e + 2).tile, g, kcur, w);
+        dma.load_v(a, plan_entry(a.entries, e + 1).tile, g, vnext, w);
       }
       // ---- tile j: mask (PARTIAL only) and the running max
-      const DevEntry ent = a.entries[e];
+      const DevEntry ent = plan_entry(a.entries, e);
       if (ent.meta & 1) {
-        mask_tile(a.slices[ent.meta >> 1], ent.tile, row, hh, s_cur);
+        mask_tile(plan_slice(a.slices, ent.meta >> 1), ent.tile, row, hh, s_cur);
         mx_cur = tile_max(s_cur);
       }
       // move the running max only when this tile's max exceeds it by more
