@@ -332,7 +332,8 @@ const char* ffa_build_info(void) {
     std::string s = "arch=gfx950 fwd_tile=" + std::to_string(ffa::fwd_tile_rows()) + "x" +
                     std::to_string(ffa::fwd_tile_cols()) + " bwd_kv_tile=" +
                     std::to_string(ffa::bwd_kv_tile_rows()) + "x" + std::to_string(ffa::bwd_kv_tile_cols()) +
-                    " head_dims=64,128 softcap=tanh compiler=" + __VERSION__;
+                    " bwd_q_tile=" + std::to_string(ffa::bwd_q_tile_rows()) + "x" +
+                    std::to_string(ffa::bwd_q_tile_cols()) + " head_dims=64,128 softcap=tanh compiler=" + __VERSION__;
     return s;
   }();
   return info.c_str();

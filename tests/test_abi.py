@@ -35,7 +35,10 @@ def test_exports_every_declared_symbol(lib):
 
 def test_build_info(lib):
     info = ffa.ffa_build_info()
-    assert "gfx950" in info and "128x64" in info
+    assert "arch=gfx950" in info
+    # every tile shape the planner is asked for is reported
+    for key in ("fwd_tile=", "bwd_kv_tile=", "bwd_q_tile="):
+        assert key in info, info
 
 
 def _fwd(lib, Tq=16, Tk=16, hq=2, hkv=1, d=64, qr=((0, 16),), kr=((0, 16),), ty=(0,),
