@@ -286,10 +286,13 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   // step st = (entry e, q head): producers fetch the Q tile, consumers the
   // dO tile; wave 0 also fetches the step's lse and D (first, so that a
-  // wait for them never waits for the tile fetches behind them)
+  // wait for them never waits for the tile fetches behind them).  Entries
+  // are walked last to first: key tiles of one causal sequence then all
+  // start at the sequence's last q tile and move down together, so the
+  // workgroups resident at the same time read the same Q/dO tiles from L2.
   float lse_raw = 0.f, d_raw = 0.f;
   auto issue = [&](int st, char* dst) {
-    const int e = e_begin + st / a.grp;
+    const int e = e_end - 1 - st / a.grp;
     const int head = g * a.grp + st % a.grp;
     const int64_t q0 = (int64_t)plan_entry(a.entries, e).tile * kDkvRows;
     if (tid < kDkvRows) {
@@ -318,7 +321,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   auto pstep = [&](int st, auto r) {
     if (st < n_steps) {
       if (st + 1 < n_steps) issue(st + 1, qbuf(IC<decltype(r)::value + 1>{}));
-      const DevEntry ent = plan_entry(a.entries, e_begin + st / a.grp);
+      const DevEntry ent = plan_entry(a.entries, e_end - 1 - st / a.grp);
       const char* qt = qbuf(r);
       const char* ot = obuf(r);
       float* xch = xchg[st & 1][pair];
