@@ -122,7 +122,10 @@ int ffa_bwd(const void* q, const void* k, const void* v,
  * row_ptr    [n_tiles + 1] CSR offsets (may be NULL)
  * entries    [cap][3] int32 (other_tile, r, kind), sorted within each tile
  *            by other_tile and then by the slice's bounds (may be NULL)
- * order      [n_tiles] tiles by descending entry count (may be NULL)
+ * order      [n_tiles] the order the kernels take tiles in (may be NULL):
+ *            tiles are grouped by the smallest slice start row (qs) among
+ *            the slices in their list, groups by descending longest list,
+ *            tiles within a group by descending entry count, then by index
  * Returns the number of entries (>= 0, even when cap is too small: call with
  * cap = 0 to size the buffers) or a negative FFA_ERR_*.
  */

@@ -3,6 +3,8 @@
 
 #include <algorithm>
 #include <numeric>
+#include <map>
+#include <limits>
 #include <tuple>
 
 namespace ffa {
@@ -122,11 +124,30 @@ void build_plan(const std::vector<Slice>& slices, int64_t Tq, int64_t Tk, int bm
   }
   for (int64_t t = 0; t < plan->n_tiles; ++t) plan->row_ptr[t + 1] += plan->row_ptr[t];
 
-  // longest-processing-time-first order of tiles (ties: lower tile first)
-  plan->order.resize(static_cast<size_t>(plan->n_tiles));
+  // Order of tiles.  Tiles are grouped by the first query row of the slices
+  // their lists meet (for a packed batch: one document), groups go by their
+  // longest list, tiles inside a group by their own length (ties: lower tile
+  // first).  Longest-first keeps the kernels' tail short; keeping a
+  // document's tiles together means the workgroups resident on one XCD at the
+  // same time walk the same K/V (or Q/dO) tiles and share them in L2.
+  const int64_t nt = plan->n_tiles;
+  std::vector<int64_t> key(static_cast<size_t>(nt), std::numeric_limits<int64_t>::max());
+  std::vector<int32_t> len(static_cast<size_t>(nt));
+  for (int64_t t = 0; t < nt; ++t) {
+    len[t] = plan->row_ptr[t + 1] - plan->row_ptr[t];
+    for (int32_t e = plan->row_ptr[t]; e < plan->row_ptr[t + 1]; ++e)
+      key[t] = std::min<int64_t>(key[t], slices[plan->entries[e].slice].qs);
+  }
+  std::map<int64_t, int32_t> group_len;  // key -> longest list in the group
+  for (int64_t t = 0; t < nt; ++t) {
+    int32_t& m = group_len[key[t]];
+    m = std::max(m, len[t]);
+  }
+  plan->order.resize(static_cast<size_t>(nt));
   std::iota(plan->order.begin(), plan->order.end(), 0);
-  std::stable_sort(plan->order.begin(), plan->order.end(), [&](int32_t x, int32_t y) {
-    return (plan->row_ptr[x + 1] - plan->row_ptr[x]) > (plan->row_ptr[y + 1] - plan->row_ptr[y]);
+  std::sort(plan->order.begin(), plan->order.end(), [&](int32_t x, int32_t y) {
+    const int32_t gx = group_len[key[x]], gy = group_len[key[y]];
+    return std::make_tuple(-gx, key[x], -len[x], x) < std::make_tuple(-gy, key[y], -len[y], y);
   });
 }
 

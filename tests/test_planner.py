@@ -32,9 +32,19 @@ def _check_structure(row_ptr, ent, order, qr, kr):
     n = len(row_ptr) - 1
     assert row_ptr[0] == 0 and np.all(np.diff(row_ptr) >= 0) and row_ptr[-1] == len(ent)
     counts = np.diff(row_ptr)
-    # longest list first, ties by tile index
+    # order: a permutation; tiles grouped by the smallest slice start row in
+    # their list (empty tiles form one group), each group contiguous, groups
+    # by descending longest list, inside a group by descending count, then index
     assert sorted(order.tolist()) == list(range(n))
-    assert all((counts[a], -a) >= (counts[b], -b) for a, b in zip(order[:-1], order[1:]))
+    key = [min((int(qr[e[1]][0]) for e in ent[row_ptr[t]:row_ptr[t + 1]]), default=None) for t in range(n)]
+    seq = [key[t] for t in order]
+    starts = [i for i in range(n) if i == 0 or seq[i] != seq[i - 1]]
+    assert len(starts) == len(set(seq)), "groups must be contiguous"
+    heads = [counts[order[i]] for i in starts]
+    assert heads == sorted(heads, reverse=True)
+    for a, b in zip(order[:-1], order[1:]):
+        if key[a] == key[b]:
+            assert (counts[a], -a) >= (counts[b], -b)
     # within a tile: sorted by the other tile, then by slice bounds
     for t in range(n):
         keys = [(int(e[0]), *qr[e[1]].tolist(), *kr[e[1]].tolist()) for e in ent[row_ptr[t]:row_ptr[t + 1]]]
