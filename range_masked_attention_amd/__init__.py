@@ -287,45 +287,33 @@ def ffa_bwd_planned(plan, q, k, v, out, lse, dout, scale: float, softcap: float 
     return dq, dk, dv
 
 
-def _autograd_fn():
-    import torch
-
-    class _FlexAttn(torch.autograd.Function):
-        @staticmethod
-        def forward(ctx, q, k, v, qr, kr, ty, scale, softcap):
-            out, lse = ffa_fwd(q, k, v, qr, kr, ty, scale, softcap)
-            ctx.save_for_backward(q, k, v, out, lse)
-            ctx.slices = (qr, kr, ty)
-            ctx.scale, ctx.softcap = scale, softcap
-            ctx.mark_non_differentiable(lse)
-            return out, lse
-
-        @staticmethod
-        def backward(ctx, dout, dlse):
-            q, k, v, out, lse = ctx.saved_tensors
-            dq, dk, dv = ffa_bwd(q, k, v, out, lse, dout.contiguous(), *ctx.slices,
-                                 ctx.scale, ctx.softcap)
-            return dq, dk, dv, None, None, None, None, None
-
-    return _FlexAttn
-
-
-_FN = None
-
-
 def flex_flash_attn_func(q, k, v, q_ranges, k_ranges, attn_type_map,
                          max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
                          softmax_scale: Optional[float] = None, softcap: float = 0.0):
-    """Range-masked attention with autograd.  Returns (out, lse).
+    """Range-masked attention with autograd.  Returns (out, lse); lse carries no gradient.
 
-    ``max_seqlen_q`` / ``max_seqlen_k`` are accepted for call compatibility and
-    unused: the host planner derives the tiling from the ranges themselves.
-    Slice tensors on the GPU are copied to the host (one synchronisation).
+    Runs through the ``ffa_amd::fwd`` / ``ffa_amd::bwd`` custom operators
+    (``torch_op``), so it also works inside ``torch.compile``: pad the slice
+    lists with empty ``[x, x]`` slices to a fixed count and one compiled graph
+    serves them all.  ``max_seqlen_q`` / ``max_seqlen_k`` are accepted for call
+    compatibility and unused: the host planner derives the tiling from the
+    ranges themselves.  Slice tensors on the GPU are copied to the host inside
+    the operator (one synchronisation).
     """
-    global _FN
-    if _FN is None:
-        _FN = _autograd_fn()
+    import torch
+
+    def as_tensor(x):
+        return x if isinstance(x, torch.Tensor) else torch.as_tensor(np.asarray(x, dtype=np.int32))
+
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(q.shape[-1])
-    qr, kr, ty = _host_slices(q_ranges, k_ranges, attn_type_map)
-    return _FN.apply(q, k, v, qr, kr, ty, float(softmax_scale), float(softcap))
+    return torch.ops.ffa_amd.fwd(q, k, v, as_tensor(q_ranges), as_tensor(k_ranges),
+                                 as_tensor(attn_type_map), float(softmax_scale), float(softcap))
+
+
+# Register the custom operators (ffa_amd::fwd, ffa_amd::bwd) on import, so
+# compiled code never has to import anything.
+try:
+    from . import torch_op  # noqa: F401,E402
+except ImportError:  # torch missing: the ctypes-level functions still work
+    pass

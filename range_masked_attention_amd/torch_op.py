@@ -1,0 +1,71 @@
+"""PyTorch custom operators over the C ABI, so the path runs under torch.compile.
+
+The MagiAttention issue on dummy/padded attention slices is about exactly this
+use: ``flex_flash_attn_func`` inside ``torch.compile`` with static shapes,
+obtained by padding the slice list with empty ``[x, x]`` slices up to a fixed
+count.  The flash-attention pull request "Add torch.compile support to flash
+attention 3" shows the mechanism: register the kernels as custom operators with
+fake implementations (output shapes only) and an autograd formula.
+
+Here ``ffa_amd::fwd`` returns ``(out, lse)`` and ``ffa_amd::bwd`` returns
+``(dq, dk, dv)``.  The compiler treats both as opaque; their fake
+implementations depend only on tensor shapes, so one compiled graph serves every
+slice list of the same padded length.  The real implementations call the C ABI
+through the ctypes binding (slice tensors on the GPU are copied to the host
+there: one synchronisation).  ``lse`` is returned without a gradient, as in the
+eager autograd path.
+"""
+from __future__ import annotations
+
+from typing import Tuple
+
+import torch
+
+from . import ffa_bwd as _ffa_bwd
+from . import ffa_fwd as _ffa_fwd
+
+NAMESPACE = "ffa_amd"
+
+
+@torch.library.custom_op(f"{NAMESPACE}::fwd", mutates_args=(), device_types="cuda")
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_ranges: torch.Tensor,
+        k_ranges: torch.Tensor, attn_type_map: torch.Tensor, scale: float,
+        softcap: float) -> Tuple[torch.Tensor, torch.Tensor]:
+    return _ffa_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, scale, softcap)
+
+
+@fwd.register_fake
+def _fwd_fake(q, k, v, q_ranges, k_ranges, attn_type_map, scale, softcap):
+    torch._check(q.dim() == 3 and k.dim() == 3 and v.dim() == 3, lambda: "q, k, v must be [T, heads, d]")
+    return torch.empty_like(q), q.new_empty((q.shape[0], q.shape[1]), dtype=torch.float32)
+
+
+@torch.library.custom_op(f"{NAMESPACE}::bwd", mutates_args=(), device_types="cuda")
+def bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+        lse: torch.Tensor, q_ranges: torch.Tensor, k_ranges: torch.Tensor,
+        attn_type_map: torch.Tensor, scale: float,
+        softcap: float) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    return _ffa_bwd(q, k, v, out, lse, dout.contiguous(), q_ranges, k_ranges, attn_type_map,
+                    scale, softcap)
+
+
+@bwd.register_fake
+def _bwd_fake(dout, q, k, v, out, lse, q_ranges, k_ranges, attn_type_map, scale, softcap):
+    return torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+
+def _setup_context(ctx, inputs, output):
+    q, k, v, q_ranges, k_ranges, attn_type_map, scale, softcap = inputs
+    out, lse = output
+    ctx.save_for_backward(q, k, v, out, lse, q_ranges, k_ranges, attn_type_map)
+    ctx.scale, ctx.softcap = scale, softcap
+    ctx.mark_non_differentiable(lse)
+
+
+def _backward(ctx, dout, dlse):
+    q, k, v, out, lse, q_ranges, k_ranges, attn_type_map = ctx.saved_tensors
+    dq, dk, dv = bwd(dout, q, k, v, out, lse, q_ranges, k_ranges, attn_type_map, ctx.scale, ctx.softcap)
+    return dq, dk, dv, None, None, None, None, None
+
+
+fwd.register_autograd(_backward, setup_context=_setup_context)
