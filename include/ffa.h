@@ -171,8 +171,75 @@ int ffa_bwd_planned(ffa_plan_t plan,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Release a plan: its device memory is freed in order on `stream`, after the
- * work already enqueued there.  NULL is a no-op. */
+ * work already enqueued there (a plan from ffa_plan_create_device lives in
+ * the caller's workspace, which is left alone).  NULL is a no-op. */
 int ffa_plan_destroy(ffa_plan_t plan, void* stream);
+
+/*
+ * Plans built on the device.  The slice arrays of flex_flash_attn_func are
+ * device tensors in the MagiAttention issue on dummy/padded slices (padded
+ * to a fixed count for torch.compile).  ffa_plan_create_device builds the
+ * same plan as ffa_plan_create (the same entries in the same order, and the
+ * same tile order) with kernels that read those arrays in device memory: no
+ * host copy, no synchronisation, no allocation.  ffa_plan_refresh re-runs
+ * the build on the current contents of the same arrays, so a sequence
+ * "refresh, forward, backward" can be captured once in a HIP graph and
+ * replayed for every new slice list of the same length.
+ *
+ * q_ranges [R][2], k_ranges [R][2], attn_type_map [R]: DEVICE int32 arrays,
+ *            4-byte aligned, read by every build; they must stay valid
+ *            (and keep their address) until the plan is destroyed.
+ * R          0 .. 4096 slices (FFA_ERR_INVALID_ARG above).
+ * max_entries  capacity of each of the plan's two block lists, in entries
+ *            (0 .. 2^30 - 1).  A list needs one entry per (tile, other tile,
+ *            slice) triple with a visible cell; ffa_plan_host gives the
+ *            exact count for a slice list.  A build that needs more leaves
+ *            the plan empty and sets FFA_PLAN_CAPACITY in its status.
+ * workspace  device memory of at least ffa_plan_device_workspace_size()
+ *            bytes, 256-byte aligned, owned by the caller, holding the plan;
+ *            it must outlive the plan and not be shared with another plan.
+ * Validation of Tq, Tk, R, max_entries and the pointers is synchronous (the
+ * usual FFA_ERR_* codes).  The slice values are only seen by the kernels: a
+ * slice with start > end, a range outside [0, T) or a type other than 0/1
+ * leaves the plan empty and sets FFA_PLAN_BAD_SLICE.  An empty plan makes
+ * the attention calls write out = 0, lse = -inf, zero gradients.  Slices
+ * must not overlap, as for ffa_fwd (not checked on the device).
+ * The build is enqueued on `stream`; use the plan on that stream.
+ */
+enum {
+  FFA_PLAN_BAD_SLICE = 1, /* a slice failed validation */
+  FFA_PLAN_CAPACITY = 2   /* a block list needed more than max_entries */
+};
+
+int ffa_plan_device_workspace_size(int64_t Tq, int64_t Tk, int R, int64_t max_entries,
+                                   size_t* bytes);
+
+int ffa_plan_create_device(int64_t Tq, int64_t Tk,
+                           const int32_t* q_ranges, const int32_t* k_ranges,
+                           const int32_t* attn_type_map, int R, int64_t max_entries,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream, ffa_plan_t* plan);
+
+/* Re-run the device build of a plan from ffa_plan_create_device on the
+ * current contents of its slice arrays (enqueue only; capturable).
+ * FFA_ERR_INVALID_ARG for a plan built on the host. */
+int ffa_plan_refresh(ffa_plan_t plan, void* stream);
+
+/* Status bits (FFA_PLAN_*) of the last device build; 0 if it succeeded or
+ * if the plan was built on the host.  Synchronises with `stream`. */
+int ffa_plan_status(ffa_plan_t plan, void* stream, int* status);
+
+/*
+ * ffa_plan_export -- copy one block list of a plan back to the host, in the
+ * format of ffa_plan_host: which = 0 the forward list (per q tile), 1 the
+ * key-side list of dK/dV, 2 the q-tile list of the dQ pass.  *n_tiles
+ * receives the number of tiles; row_ptr [n_tiles + 1], entries [cap][3]
+ * (other_tile, caller's slice index, kind), order [n_tiles]; any pointer may
+ * be NULL (call once with NULLs to size the buffers).  Returns the number of
+ * entries or a negative FFA_ERR_*.  Synchronises with `stream`.
+ */
+int64_t ffa_plan_export(ffa_plan_t plan, int which, int64_t* n_tiles, int64_t* row_ptr,
+                        int32_t* entries, int64_t cap, int32_t* order, void* stream);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* ffa_last_error(void);

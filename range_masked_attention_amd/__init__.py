@@ -26,7 +26,8 @@ __all__ = [
     "FULL", "CAUSAL", "FfaError", "lib_path", "load_library", "ffa_fwd", "ffa_bwd",
     "ffa_bwd_workspace_size", "ffa_plan_host", "ffa_last_error", "ffa_build_info",
     "ffa_plan_create", "ffa_fwd_planned", "ffa_bwd_planned", "ffa_plan_destroy",
-    "flex_flash_attn_func",
+    "ffa_plan_device_workspace_size", "ffa_plan_create_device", "ffa_plan_refresh", "ffa_plan_status",
+    "ffa_plan_export", "FFA_PLAN_BAD_SLICE", "FFA_PLAN_CAPACITY", "flex_flash_attn_func",
 ]
 
 FULL = 0
@@ -81,6 +82,18 @@ def load_library():
     lib.ffa_bwd_planned.restype = ctypes.c_int
     lib.ffa_plan_destroy.argtypes = [vp, vp]
     lib.ffa_plan_destroy.restype = ctypes.c_int
+    lib.ffa_plan_device_workspace_size.argtypes = [i64, i64, i32, i64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.ffa_plan_device_workspace_size.restype = ctypes.c_int
+    lib.ffa_plan_create_device.argtypes = [i64, i64, vp, vp, vp, i32, i64, vp, ctypes.c_size_t, vp,
+                                           ctypes.POINTER(vp)]
+    lib.ffa_plan_create_device.restype = ctypes.c_int
+    lib.ffa_plan_refresh.argtypes = [vp, vp]
+    lib.ffa_plan_refresh.restype = ctypes.c_int
+    lib.ffa_plan_status.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int)]
+    lib.ffa_plan_status.restype = ctypes.c_int
+    lib.ffa_plan_export.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                                    ip32, i64, ip32, vp]
+    lib.ffa_plan_export.restype = ctypes.c_int64
     lib.ffa_last_error.restype = ctypes.c_char_p
     lib.ffa_build_info.restype = ctypes.c_char_p
     _LIB = lib
@@ -242,6 +255,88 @@ def ffa_plan_destroy(plan, device=None) -> None:
         return
     dev_ = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
     _check(load_library().ffa_plan_destroy(plan, torch.cuda.current_stream(dev_).cuda_stream))
+
+
+FFA_PLAN_BAD_SLICE = 1
+FFA_PLAN_CAPACITY = 2
+
+
+def _cur_stream(device=None) -> int:
+    import torch
+    dev_ = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    return torch.cuda.current_stream(dev_).cuda_stream
+
+
+def ffa_plan_device_workspace_size(Tq: int, Tk: int, R: int, max_entries: int) -> int:
+    """C ABI ``ffa_plan_device_workspace_size``: bytes of workspace a device-built plan needs."""
+    n = ctypes.c_size_t(0)
+    _check(load_library().ffa_plan_device_workspace_size(Tq, Tk, R, max_entries, ctypes.byref(n)))
+    return int(n.value)
+
+
+def default_plan_capacity(Tq: int, Tk: int, R: int) -> int:
+    """A generous entry capacity for device-built plans: every (row tile, key
+    tile) pair of the 128 x 64 grid met by up to min(R, 16) slices."""
+    return int(min((1 << 30) - 1, -(-Tq // 128) * -(-Tk // 64) * max(1, min(R, 16))))
+
+
+def ffa_plan_create_device(Tq: int, Tk: int, q_ranges, k_ranges, attn_type_map,
+                           max_entries: Optional[int] = None, workspace=None):
+    """C ABI ``ffa_plan_create_device`` on device int32 tensors ([R,2], [R,2], [R]).
+
+    Returns ``(plan, workspace)``; the workspace (allocated here if None) and
+    the three slice tensors must stay alive, unmoved, until ffa_plan_destroy.
+    """
+    import torch
+    for nm, t, nd in (("q_ranges", q_ranges, 2), ("k_ranges", k_ranges, 2), ("attn_type_map", attn_type_map, 1)):
+        if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.int32 or t.dim() != nd \
+                or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous int32 GPU tensor with {nd} dims")
+    R = attn_type_map.shape[0]
+    if tuple(q_ranges.shape) != (R, 2) or tuple(k_ranges.shape) != (R, 2):
+        raise ValueError("q_ranges and k_ranges must be [R, 2] with attn_type_map [R]")
+    if max_entries is None:
+        max_entries = default_plan_capacity(Tq, Tk, R)
+    need = ffa_plan_device_workspace_size(Tq, Tk, R, max_entries)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_ranges.device)
+    h = ctypes.c_void_p()
+    _check(load_library().ffa_plan_create_device(
+        Tq, Tk, q_ranges.data_ptr(), k_ranges.data_ptr(), attn_type_map.data_ptr(), R, max_entries,
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _cur_stream(q_ranges.device), ctypes.byref(h)))
+    return h.value, workspace
+
+
+def ffa_plan_refresh(plan, device=None) -> None:
+    """C ABI ``ffa_plan_refresh`` on the current stream (capturable)."""
+    _check(load_library().ffa_plan_refresh(plan, _cur_stream(device)))
+
+
+def ffa_plan_status(plan, device=None) -> int:
+    """C ABI ``ffa_plan_status``: FFA_PLAN_* bits of the last device build (synchronises)."""
+    st = ctypes.c_int(0)
+    _check(load_library().ffa_plan_status(plan, _cur_stream(device), ctypes.byref(st)))
+    return int(st.value)
+
+
+def ffa_plan_export(plan, which: int, device=None):
+    """C ABI ``ffa_plan_export``: (row_ptr, entries [E,3], order) of list `which`
+    (0 forward, 1 key-side dK/dV, 2 dQ), as ffa_plan_host returns them."""
+    lib = load_library()
+    s = _cur_stream(device)
+    nt = ctypes.c_int64(0)
+    n = lib.ffa_plan_export(plan, which, ctypes.byref(nt), None, None, 0, None, s)
+    if n < 0:
+        raise FfaError(int(n), ffa_last_error())
+    row_ptr = np.zeros(nt.value + 1, dtype=np.int64)
+    entries = np.zeros((max(n, 1), 3), dtype=np.int32)
+    order = np.zeros(max(nt.value, 1), dtype=np.int32)
+    n2 = lib.ffa_plan_export(plan, which, None, row_ptr.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                             _iptr(entries), n, _iptr(order), s)
+    if n2 != n:
+        raise FfaError(int(n2), ffa_last_error())
+    return row_ptr, entries[:n], order[:nt.value]
 
 
 def ffa_fwd_planned(plan, q, k, v, scale: float, softcap: float = 0.0, out=None, lse=None):

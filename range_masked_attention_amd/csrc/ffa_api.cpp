@@ -172,6 +172,12 @@ struct ffa_plan_s {
   PlanPart fwd, kv, dq;  // forward q tiles; per key tile (dK/dV); dQ q tiles
   unsigned char* dev = nullptr;
   size_t bytes = 0;
+  // host-built plans: the caller's index of each slice in the device table
+  std::vector<int32_t> slice_index;
+  // plans built on the device: the planner's arguments (re-run by
+  // ffa_plan_refresh) and its status word; `dev` is the caller's workspace
+  bool on_device = false;
+  ffa::PlanDeviceLaunch dl{};
 };
 
 namespace {
@@ -194,6 +200,13 @@ int plan_create(int64_t Tq, int64_t Tk, const int32_t* qr, const int32_t* kr, co
   p->Tk = Tk;
   p->want = want;
   p->n_slices = slices.size();
+  try {
+    p->slice_index.resize(slices.size());
+  } catch (const std::bad_alloc&) {
+    delete p;
+    return fail(FFA_ERR_NOMEM, "out of host memory");
+  }
+  for (size_t i = 0; i < slices.size(); ++i) p->slice_index[i] = slices[i].r;
   std::vector<unsigned char> img;
   try {
     img.resize(align16((slices.size() + 1) * sizeof(ffa::HostDevSlice)), 0);
@@ -248,7 +261,7 @@ int plan_create(int64_t Tq, int64_t Tk, const int32_t* qr, const int32_t* kr, co
 int plan_destroy(ffa_plan_s* p, hipStream_t stream) {
   if (!p) return FFA_OK;
   hipError_t e = hipSuccess;
-  if (p->dev) e = hipFreeAsync(p->dev, stream);
+  if (p->dev && !p->on_device) e = hipFreeAsync(p->dev, stream);
   delete p;
   if (e != hipSuccess) return hip_fail(e, "hipFreeAsync(plan)");
   return FFA_OK;
@@ -319,6 +332,57 @@ int bwd_planned(const ffa_plan_s* p, const void* q, const void* k, const void* v
   if (ws != workspace) (void)hipFreeAsync(ws, stream);
   if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
   return FFA_OK;
+}
+
+// Layout of a device-built plan inside the caller's workspace (256-byte
+// aligned pieces): slice table, slice ranks, status word, then per list
+// row_ptr, entries, order and three scratch arrays.
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct DeviceLayout {
+  size_t slices, rank, status, total;
+  struct Part {
+    int64_t n_tiles;
+    size_t row_ptr, entries, order, count, key, glen;
+  } part[2];
+};
+
+DeviceLayout device_layout(int64_t Tq, int64_t Tk, int R, int64_t cap) {
+  DeviceLayout L{};
+  size_t off = 0;
+  L.slices = off;
+  off += align256(size_t(std::max(R, 1)) * sizeof(ffa::HostDevSlice));
+  L.rank = off;
+  off += align256(size_t(std::max(R, 1)) * 4);
+  L.status = off;
+  off += 256;
+  const int64_t n_tiles[2] = {(Tq + ffa::fwd_tile_rows() - 1) / ffa::fwd_tile_rows(),
+                              (Tk + ffa::bwd_kv_tile_cols() - 1) / ffa::bwd_kv_tile_cols()};
+  for (int i = 0; i < 2; ++i) {
+    const size_t n = size_t(n_tiles[i]);
+    DeviceLayout::Part& P = L.part[i];
+    P.n_tiles = n_tiles[i];
+    P.row_ptr = off; off += align256((n + 1) * 4);
+    P.entries = off; off += align256(size_t(std::max<int64_t>(cap, 1)) * sizeof(ffa::HostDevEntry));
+    P.order = off;   off += align256(std::max<size_t>(n, 1) * 4);
+    P.count = off;   off += align256(std::max<size_t>(n, 1) * 4);
+    P.key = off;     off += align256(std::max<size_t>(n, 1) * 4);
+    P.glen = off;    off += align256(std::max<size_t>(n, 1) * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+std::string check_device_plan_args(int64_t Tq, int64_t Tk, int R, int64_t max_entries) {
+  std::string m = check_sizes(Tq, Tk);
+  if (!m.empty()) return m;
+  if (R < 0) return "R must be >= 0";
+  if (R > ffa::plan_device_max_slices())
+    return "the device planner takes at most " + std::to_string(ffa::plan_device_max_slices()) + " slices";
+  if (max_entries < 0 || max_entries >= (int64_t(1) << 30)) return "max_entries must be in [0, 2^30)";
+  if (ffa::bwd_q_tile_rows() != ffa::fwd_tile_rows() || ffa::bwd_q_tile_cols() != ffa::fwd_tile_cols())
+    return "device planner expects the dQ pass to share the forward tiles";
+  return "";
 }
 
 }  // namespace
@@ -461,6 +525,158 @@ int ffa_bwd(const void* q, const void* k, const void* v, const void* out, const 
   const int rc2 = plan_destroy(p, st);
   if (rc != FFA_OK) return fail(rc, err);
   return rc2;
+}
+
+int ffa_plan_device_workspace_size(int64_t Tq, int64_t Tk, int R, int64_t max_entries, size_t* bytes) {
+  g_err.clear();
+  if (!bytes) return fail(FFA_ERR_INVALID_ARG, "bytes must not be NULL");
+  const std::string m = check_device_plan_args(Tq, Tk, R, max_entries);
+  if (!m.empty()) return fail(FFA_ERR_INVALID_ARG, m);
+  *bytes = device_layout(Tq, Tk, R, max_entries).total;
+  return FFA_OK;
+}
+
+int ffa_plan_create_device(int64_t Tq, int64_t Tk, const int32_t* q_ranges, const int32_t* k_ranges,
+                           const int32_t* attn_type_map, int R, int64_t max_entries, void* workspace,
+                           size_t workspace_bytes, void* stream, ffa_plan_t* plan) {
+  g_err.clear();
+  if (!plan) return fail(FFA_ERR_INVALID_ARG, "plan must not be NULL");
+  *plan = nullptr;
+  const std::string m = check_device_plan_args(Tq, Tk, R, max_entries);
+  if (!m.empty()) return fail(FFA_ERR_INVALID_ARG, m);
+  if (R > 0 && (!q_ranges || !k_ranges || !attn_type_map))
+    return fail(FFA_ERR_INVALID_ARG, "slice arrays must not be NULL");
+  if ((reinterpret_cast<uintptr_t>(q_ranges) | reinterpret_cast<uintptr_t>(k_ranges) |
+       reinterpret_cast<uintptr_t>(attn_type_map)) & 3)
+    return fail(FFA_ERR_INVALID_ARG, "slice arrays must be 4-byte aligned");
+  const DeviceLayout L = device_layout(Tq, Tk, R, max_entries);
+  if (!workspace) return fail(FFA_ERR_INVALID_ARG, "workspace must not be NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255)
+    return fail(FFA_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail(FFA_ERR_INVALID_ARG, "workspace is smaller than ffa_plan_device_workspace_size()");
+  ffa_plan_s* p = new (std::nothrow) ffa_plan_s;
+  if (!p) return fail(FFA_ERR_NOMEM, "out of host memory");
+  auto* base = static_cast<unsigned char*>(workspace);
+  p->Tq = Tq;
+  p->Tk = Tk;
+  p->want = kWantFwd | kWantBwd;
+  p->n_slices = size_t(R);
+  p->off_slices = L.slices;
+  p->dev = base;
+  p->bytes = L.total;
+  p->on_device = true;
+  PlanPart* parts[2] = {&p->fwd, &p->kv};
+  ffa::PlanDeviceLaunch& D = p->dl;
+  D.q_ranges = q_ranges;
+  D.k_ranges = k_ranges;
+  D.types = attn_type_map;
+  D.R = R;
+  D.Tq = Tq;
+  D.Tk = Tk;
+  D.slices = base + L.slices;
+  D.rank = reinterpret_cast<int32_t*>(base + L.rank);
+  D.status = reinterpret_cast<int32_t*>(base + L.status);
+  D.n_parts = 2;
+  for (int i = 0; i < 2; ++i) {
+    const DeviceLayout::Part& LP = L.part[i];
+    parts[i]->n_tiles = LP.n_tiles;
+    parts[i]->off_row_ptr = LP.row_ptr;
+    parts[i]->off_entries = LP.entries;
+    parts[i]->off_order = LP.order;
+    ffa::PlanDevicePart& P = D.part[i];
+    P.n_tiles = LP.n_tiles;
+    P.bm = i == 0 ? ffa::fwd_tile_rows() : ffa::bwd_kv_tile_rows();
+    P.bn = i == 0 ? ffa::fwd_tile_cols() : ffa::bwd_kv_tile_cols();
+    P.transpose = i == 1;
+    P.cap = max_entries;
+    P.count = reinterpret_cast<int32_t*>(base + LP.count);
+    P.key = reinterpret_cast<int32_t*>(base + LP.key);
+    P.glen = reinterpret_cast<int32_t*>(base + LP.glen);
+    P.row_ptr = reinterpret_cast<int32_t*>(base + LP.row_ptr);
+    P.entries = base + LP.entries;
+    P.order = reinterpret_cast<int32_t*>(base + LP.order);
+  }
+  p->dq = p->fwd;  // the dQ pass walks the forward lists
+  hipError_t e = ffa::launch_plan_device(D, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    delete p;
+    return hip_fail(e, "device planner launch");
+  }
+  *plan = p;
+  return FFA_OK;
+}
+
+int ffa_plan_refresh(ffa_plan_t plan, void* stream) {
+  g_err.clear();
+  if (!plan) return fail(FFA_ERR_INVALID_ARG, "plan must not be NULL");
+  if (!plan->on_device) return fail(FFA_ERR_INVALID_ARG, "plan was not built by ffa_plan_create_device");
+  hipError_t e = ffa::launch_plan_device(plan->dl, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "device planner launch");
+  return FFA_OK;
+}
+
+int ffa_plan_status(ffa_plan_t plan, void* stream, int* status) {
+  g_err.clear();
+  if (!plan || !status) return fail(FFA_ERR_INVALID_ARG, "plan and status must not be NULL");
+  *status = 0;
+  if (!plan->on_device) return FFA_OK;
+  int32_t word = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(&word, plan->dl.status, sizeof(word), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "reading the planner status");
+  *status = word;
+  return FFA_OK;
+}
+
+int64_t ffa_plan_export(ffa_plan_t plan, int which, int64_t* n_tiles, int64_t* row_ptr, int32_t* entries,
+                        int64_t cap, int32_t* order, void* stream) {
+  g_err.clear();
+  if (!plan) return fail(FFA_ERR_INVALID_ARG, "plan must not be NULL");
+  if (which < 0 || which > 2) return fail(FFA_ERR_INVALID_ARG, "which must be 0, 1 or 2");
+  const int need = which == 0 ? kWantFwd : kWantBwd;
+  if (!(plan->want & need)) return fail(FFA_ERR_INVALID_ARG, "the plan has no such list");
+  const PlanPart& P = which == 0 ? plan->fwd : which == 1 ? plan->kv : plan->dq;
+  if (n_tiles) *n_tiles = P.n_tiles;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<int32_t> rp, od;
+  std::vector<ffa::HostDevEntry> en;
+  try {
+    rp.resize(size_t(P.n_tiles) + 1);
+    od.resize(size_t(std::max<int64_t>(P.n_tiles, 1)));
+  } catch (const std::bad_alloc&) {
+    return fail(FFA_ERR_NOMEM, "out of host memory");
+  }
+  hipError_t e = hipMemcpyAsync(rp.data(), plan->dev + P.off_row_ptr, rp.size() * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess && P.n_tiles > 0)
+    e = hipMemcpyAsync(od.data(), plan->dev + P.off_order, size_t(P.n_tiles) * 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "reading the plan");
+  const int64_t n = rp.back();
+  try {
+    en.resize(size_t(std::max<int64_t>(n, 1)));
+  } catch (const std::bad_alloc&) {
+    return fail(FFA_ERR_NOMEM, "out of host memory");
+  }
+  if (n > 0) {
+    e = hipMemcpyAsync(en.data(), plan->dev + P.off_entries, size_t(n) * sizeof(ffa::HostDevEntry),
+                       hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "reading the plan");
+  }
+  if (row_ptr)
+    for (size_t i = 0; i < rp.size(); ++i) row_ptr[i] = rp[i];
+  if (order)
+    for (int64_t i = 0; i < P.n_tiles; ++i) order[i] = od[size_t(i)];
+  if (entries)
+    for (int64_t i = 0; i < std::min(n, cap); ++i) {
+      const int32_t slice = en[size_t(i)].meta >> 1;
+      entries[3 * i + 0] = en[size_t(i)].tile;
+      entries[3 * i + 1] = plan->on_device ? slice : plan->slice_index[size_t(slice)];
+      entries[3 * i + 2] = en[size_t(i)].meta & 1;
+    }
+  return n;
 }
 
 }  // extern "C"

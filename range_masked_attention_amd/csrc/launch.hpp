@@ -59,6 +59,38 @@ int fwd_tile_rows();
 int fwd_tile_cols();
 hipError_t launch_fwd(const FwdLaunch& p, hipStream_t stream);
 
+// Device-side planner (plan_device.hip).  Status bits in the device word.
+enum : int32_t { kPlanBadSlice = 1, kPlanCapacity = 2 };  // FFA_PLAN_* in ffa.h
+
+struct PlanDevicePart {
+  int64_t n_tiles;
+  int bm, bn;      // row-tile rows, key-tile keys
+  bool transpose;  // tiles are key tiles, entries name row tiles
+  int64_t cap;     // entry capacity
+  int32_t* count;  // scratch [n_tiles]
+  int32_t* key;    // scratch [n_tiles]
+  int32_t* glen;   // scratch [n_tiles]
+  int32_t* row_ptr;  // [n_tiles + 1]
+  void* entries;     // HostDevEntry[cap]
+  int32_t* order;    // [n_tiles]
+};
+
+struct PlanDeviceLaunch {
+  const int32_t* q_ranges;  // device [R][2]
+  const int32_t* k_ranges;  // device [R][2]
+  const int32_t* types;     // device [R]
+  int R;
+  int64_t Tq, Tk;
+  void* slices;     // HostDevSlice[R], indexed by the caller's slice index
+  int32_t* rank;    // scratch [R]
+  int32_t* status;  // device word: kPlan* bits of the last build
+  int n_parts;
+  PlanDevicePart part[2];
+};
+
+int plan_device_max_slices();
+hipError_t launch_plan_device(const PlanDeviceLaunch& L, hipStream_t stream);
+
 int bwd_kv_tile_rows();  // q rows per step of the dK/dV kernel
 int bwd_kv_tile_cols();  // keys per dK/dV workgroup
 int bwd_q_tile_rows();   // q rows per dQ workgroup
