@@ -186,6 +186,24 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    # the device-side planner on the same slices (outside the timed steps):
+    # HIP events around repeated ffa_plan_refresh on the launch stream
+    sl_dev = [torch.as_tensor(np.ascontiguousarray(a, dtype=np.int32), device=dev) for a in (qr, kr, ty)]
+    dplan, dws = ffa.ffa_plan_create_device(w.Tq, w.Tk, *sl_dev)
+    for _ in range(3):
+        ffa.ffa_plan_refresh(dplan)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(20):
+        ffa.ffa_plan_refresh(dplan)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    plan_device_ms = e0.elapsed_time(e1) / 20
+    if ffa.ffa_plan_status(dplan) != 0:
+        raise RuntimeError("device planner reported a bad status on the bench slices")
+    ffa.ffa_plan_destroy(dplan)
+    del dws
+
     fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) if do_bwd else None
     ms_step = 1e3 * wall / args.steps
@@ -216,6 +234,7 @@ def main():
         "bwd_ms": round(bwd_ms, 4) if do_bwd else None,
         "bwd_tflops": round(bwd_tflops, 2) if do_bwd else None,
         "plan_ms": round(1e3 * plan_s / args.steps, 4),
+        "plan_device_ms": round(plan_device_ms, 4),
         "step_tflops": round((fwd_flop + (bwd_flop if do_bwd else 0.0)) / (ms_step * 1e-3) / 1e12, 2),
     }
     algo_bytes = 2.0 * (w.Tq * w.hq * w.d * 2 + 2 * w.Tk * w.hkv * w.d) + 4.0 * w.Tq * w.hq
