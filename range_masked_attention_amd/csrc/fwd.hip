@@ -106,21 +106,27 @@ struct TileDma {
   // per-lane part and a wave-uniform part.
   uint32_t lane_row_bytes;  // (L / kChunks) * row_bytes
   int lane_slot, lane_row;  // L % kChunks, L / kChunks
+  uint32_t row_bytes, tile_bytes;
+  // this workgroup's kv head: first row of K and V, and the bytes from there
+  // to the end of the tensor; a tile's resource starts at its first row
+  const char* kbase;
+  const char* vbase;
+  int64_t bytes;
 
-  __device__ __forceinline__ void init(const FwdArgs& a, int lane) {
+  __device__ __forceinline__ void init(const FwdArgs& a, int g, int lane) {
     lane_slot = lane % Smem::kChunks;
     lane_row = lane / Smem::kChunks;
-    lane_row_bytes = (uint32_t)lane_row * ((uint32_t)a.hkv * D * 2);
-  }
-  __device__ __forceinline__ static __amdgpu_buffer_rsrc_t rsrc(const FwdArgs& a, const __bf16* t, int ktile, int g) {
-    const int64_t row_bytes = (int64_t)a.hkv * D * 2;
-    const int64_t k0 = (int64_t)ktile * kBN;
-    return make_rsrc(t + (k0 * a.hkv + g) * D, ((int64_t)a.Tk - k0) * row_bytes - (int64_t)g * D * 2);
+    row_bytes = (uint32_t)a.hkv * D * 2;
+    tile_bytes = kBN * row_bytes;
+    lane_row_bytes = (uint32_t)lane_row * row_bytes;
+    kbase = reinterpret_cast<const char*>(a.k + (int64_t)g * D);
+    vbase = reinterpret_cast<const char*>(a.v + (int64_t)g * D);
+    bytes = (int64_t)a.Tk * row_bytes - (int64_t)g * D * 2;
   }
   template <bool IS_K>
-  __device__ __forceinline__ void load(const FwdArgs& a, const __bf16* t, int ktile, int g, __bf16* dst, int w) const {
-    const __amdgpu_buffer_rsrc_t r = rsrc(a, t, ktile, g);
-    const uint32_t row_bytes = (uint32_t)a.hkv * D * 2;
+  __device__ __forceinline__ void load(int ktile, __bf16* dst, int w) const {
+    const int64_t t0 = (int64_t)(uint32_t)ktile * tile_bytes;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc((IS_K ? kbase : vbase) + t0, bytes - t0);
 #pragma unroll
     for (int c = 0; c < kPerThread; ++c) {
       const int row0 = (w * kPerThread + c) * kRowsPerLoad;  // wave-uniform
@@ -131,12 +137,8 @@ struct TileDma {
           r, (__attribute__((address_space(3))) void*)(dst + (w * kPerThread + c) * 512), 16, off, 0, 0, 0);
     }
   }
-  __device__ __forceinline__ void load_k(const FwdArgs& a, int ktile, int g, __bf16* dst, int w) const {
-    load<true>(a, a.k, ktile, g, dst, w);
-  }
-  __device__ __forceinline__ void load_v(const FwdArgs& a, int ktile, int g, __bf16* dst, int w) const {
-    load<false>(a, a.v, ktile, g, dst, w);
-  }
+  __device__ __forceinline__ void load_k(int ktile, __bf16* dst, int w) const { load<true>(ktile, dst, w); }
+  __device__ __forceinline__ void load_v(int ktile, __bf16* dst, int w) const { load<false>(ktile, dst, w); }
 };
 
 // Wait for this wave's direct-to-LDS loads, then for the whole workgroup.
@@ -260,11 +262,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
 
   if (n_tiles > 0) {
     TileDma<D> dma;
-    dma.init(a, lane);
+    dma.init(a, g, lane);
     // ---- prologue: K0, V0 and K1 in LDS; S0 and its row max
-    dma.load_k(a, plan_entry(a.entries, e_begin).tile, g, kb0, w);
-    dma.load_v(a, plan_entry(a.entries, e_begin).tile, g, vb0, w);
-    if (n_tiles > 1) dma.load_k(a, plan_entry(a.entries, e_begin + 1).tile, g, kb1, w);
+    dma.load_k(plan_entry(a.entries, e_begin).tile, kb0, w);
+    dma.load_v(plan_entry(a.entries, e_begin).tile, vb0, w);
+    if (n_tiles > 1) dma.load_k(plan_entry(a.entries, e_begin + 1).tile, kb1, w);
     dma_barrier();
     f32x16 sa[2], sb[2];
     qk_tile<D>(kb0, qf, n, hh, sa);
@@ -281,8 +283,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
       const int e = e_begin + j;
       if constexpr (MORE) {
         // direct loads for later tiles: K two ahead, V one ahead
-        if (j + 2 < n_tiles) dma.load_k(a, plan_entry(a.entries, e + 2).tile, g, kcur, w);
-        dma.load_v(a, plan_entry(a.entries, e + 1).tile, g, vnext, w);
+        if (j + 2 < n_tiles) dma.load_k(plan_entry(a.entries, e + 2).tile, kcur, w);
+        dma.load_v(plan_entry(a.entries, e + 1).tile, vnext, w);
       }
       // ---- tile j: mask (PARTIAL only) and the running max
       const DevEntry ent = plan_entry(a.entries, e);
