@@ -281,11 +281,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
                     const __bf16* vcur, __bf16* vnext, auto more_tag) {
       constexpr bool MORE = decltype(more_tag)::value;
       const int e = e_begin + j;
-      if constexpr (MORE) {
-        // direct loads for later tiles: K two ahead, V one ahead
-        if (j + 2 < n_tiles) dma.load_k(plan_entry(a.entries, e + 2).tile, kcur, w);
-        dma.load_v(plan_entry(a.entries, e + 1).tile, vnext, w);
-      }
       // ---- tile j: mask (PARTIAL only) and the running max
       const DevEntry ent = plan_entry(a.entries, e);
       if (ent.meta & 1) {
@@ -310,7 +305,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
 
       // ---- A: S_{j+1} = K_{j+1} Q^T on the matrix cores, while
       //      B: the VALU turns tile j into exp2 weights
-      if constexpr (MORE) qk_tile<D>(knext, qf, n, hh, s_next);
+      if constexpr (MORE) {
+        // direct loads for later tiles, K two ahead and V one ahead, issued
+        // among the QK products (the schedule below spreads them); past the
+        // last tile the K fetch reloads the last tile into a buffer nobody
+        // reads again, so every step issues the same loads
+        dma.load_k(plan_entry(a.entries, e_begin + min(j + 2, n_tiles - 1)).tile, kcur, w);
+        dma.load_v(plan_entry(a.entries, e + 1).tile, vnext, w);
+        qk_tile<D>(knext, qf, n, hh, s_next);
+      }
       u32x4 pw[4];
       float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -356,6 +359,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          if (i < 2 * TileDma<D>::kPerThread)
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // direct-to-LDS fetch
           if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, SOFTCAP ? 5 : 7, 0);  // VALU
         }
