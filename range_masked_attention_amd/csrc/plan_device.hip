@@ -303,33 +303,61 @@ __global__ __launch_bounds__(kBlock) void fill_kernel(PartArgs a) {
   }
 }
 
+// The all-pairs passes below stream the per-tile arrays through LDS in
+// chunks; every thread of a block then reads the same element (a broadcast).
+constexpr int kChunk = 1024;
+
 // Longest list in each tile's group (tiles with the same key).
 __global__ __launch_bounds__(kBlock) void group_kernel(PartArgs a) {
+  __shared__ int32_t c_key[kChunk], c_len[kChunk];
   const int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (t >= a.n_tiles) return;
-  const int32_t k = a.key[t];
+  const bool mine = t < a.n_tiles;
+  const int32_t k = mine ? a.key[t] : 0;
   int32_t m = 0;
-  for (int64_t i = 0; i < a.n_tiles; ++i)
-    if (a.key[i] == k) m = max(m, a.row_ptr[i + 1] - a.row_ptr[i]);
-  a.glen[t] = m;
+  for (int64_t base = 0; base < a.n_tiles; base += kChunk) {
+    const int cnt = (int)min<int64_t>(kChunk, a.n_tiles - base);
+    __syncthreads();
+    for (int i = threadIdx.x; i < cnt; i += kBlock) {
+      c_key[i] = a.key[base + i];
+      c_len[i] = a.row_ptr[base + i + 1] - a.row_ptr[base + i];
+    }
+    __syncthreads();
+    if (mine)
+      for (int i = 0; i < cnt; ++i)
+        if (c_key[i] == k) m = max(m, c_len[i]);
+  }
+  if (mine) a.glen[t] = m;
 }
 
 // Position of each tile in the order (-group length, key, -length, index).
 __global__ __launch_bounds__(kBlock) void order_kernel(PartArgs a) {
+  __shared__ int32_t c_g[kChunk], c_key[kChunk], c_len[kChunk];
   const int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (t >= a.n_tiles) return;
-  const int32_t g = a.glen[t], k = a.key[t], l = a.row_ptr[t + 1] - a.row_ptr[t];
+  const bool mine = t < a.n_tiles;
+  const int32_t g = mine ? a.glen[t] : 0, k = mine ? a.key[t] : 0;
+  const int32_t l = mine ? a.row_ptr[t + 1] - a.row_ptr[t] : 0;
   int64_t pos = 0;
-  for (int64_t i = 0; i < a.n_tiles; ++i) {
-    const int32_t gi = a.glen[i], ki = a.key[i], li = a.row_ptr[i + 1] - a.row_ptr[i];
-    bool before;
-    if (gi != g) before = gi > g;
-    else if (ki != k) before = ki < k;
-    else if (li != l) before = li > l;
-    else before = i < t;
-    pos += before;
+  for (int64_t base = 0; base < a.n_tiles; base += kChunk) {
+    const int cnt = (int)min<int64_t>(kChunk, a.n_tiles - base);
+    __syncthreads();
+    for (int i = threadIdx.x; i < cnt; i += kBlock) {
+      c_g[i] = a.glen[base + i];
+      c_key[i] = a.key[base + i];
+      c_len[i] = a.row_ptr[base + i + 1] - a.row_ptr[base + i];
+    }
+    __syncthreads();
+    if (mine)
+      for (int i = 0; i < cnt; ++i) {
+        const int32_t gi = c_g[i], ki = c_key[i], li = c_len[i];
+        bool before;
+        if (gi != g) before = gi > g;
+        else if (ki != k) before = ki < k;
+        else if (li != l) before = li > l;
+        else before = base + i < t;
+        pos += before;
+      }
   }
-  a.order[pos] = (int32_t)t;
+  if (mine) a.order[pos] = (int32_t)t;
 }
 
 hipError_t build_part(const PlanDeviceLaunch& L, const PlanDevicePart& P, hipStream_t stream) {
