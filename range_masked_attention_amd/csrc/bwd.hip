@@ -291,9 +291,21 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // start at the sequence's last q tile and move down together, so the
   // workgroups resident at the same time read the same Q/dO tiles from L2.
   float lse_raw = 0.f, d_raw = 0.f;
-  auto issue = [&](int st, char* dst) {
-    const int e = e_end - 1 - st / a.grp;
-    const int head = g * a.grp + st % a.grp;
+  // Steps go head-minor: step st is entry e_end - 1 - st / grp, head
+  // g * grp + st % grp.  Counters advanced once per step stand in for the
+  // divisions: (f_e, f_h) for the next step to fetch, (p_e, p_h) for the
+  // producer's current step.
+  int f_e = e_end - 1, f_h = 0, p_e = e_end - 1, p_h = 0;
+  auto advance = [&](int& e_, int& h_) {
+    if (++h_ == a.grp) {
+      h_ = 0;
+      --e_;
+    }
+  };
+  auto issue = [&](char* dst) {
+    const int e = f_e;
+    const int head = g * a.grp + f_h;
+    advance(f_e, f_h);
     const int64_t q0 = (int64_t)plan_entry(a.entries, e).tile * kDkvRows;
     if (tid < kDkvRows) {
       const int64_t r = q0 + tid;
@@ -308,20 +320,24 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     const int64_t valid = ((int64_t)a.Tq - q0) * q_row_bytes - (int64_t)head * D * 2;
     T::load(make_rsrc((producer ? a.q : a.dout) + off, valid), (uint32_t)q_row_bytes, dst, pair, lane);
   };
-  auto publish = [&](int st) {
+  // the step loops run six steps per turn from st = 0, so a step's slot in
+  // the 3- and 2-deep buffers is fixed by its position R in the turn
+  auto publish = [&](int slot) {
     if (tid < kDkvRows) {
       // lse in exp2 units; rows nothing sees have lse = -inf and their P
       // must be 0, not exp(+inf)
-      s_lse[st % 3][tid] = (lse_raw == -INFINITY) ? INFINITY : lse_raw * 1.4426950408889634f;
-      s_dv[st % 3][tid] = d_raw;
+      s_lse[slot][tid] = (lse_raw == -INFINITY) ? INFINITY : lse_raw * 1.4426950408889634f;
+      s_dv[slot][tid] = d_raw;
     }
   };
 
   // producer step st (st == n_steps: nothing left but the barrier)
   auto pstep = [&](int st, auto r) {
     if (st < n_steps) {
-      if (st + 1 < n_steps) issue(st + 1, qbuf(IC<decltype(r)::value + 1>{}));
-      const DevEntry ent = plan_entry(a.entries, e_end - 1 - st / a.grp);
+      constexpr int R = decltype(r)::value;
+      if (st + 1 < n_steps) issue(qbuf(IC<R + 1>{}));
+      const DevEntry ent = plan_entry(a.entries, p_e);
+      advance(p_e, p_h);
       const char* qt = qbuf(r);
       const char* ot = obuf(r);
       float* xch = xchg[st & 1][pair];
@@ -370,7 +386,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int t4 = 0; t4 < 4; ++t4)
           acc[db] = mfma_32x32x16(tr8<D>(ot, tro, db, t4), __builtin_bit_cast(bf16x8, pw[t4]), acc[db]);
-      if (st + 1 < n_steps) publish(st + 1);
+      if (st + 1 < n_steps) publish((st + 1) % 3);
     }
     dma_barrier();
   };
@@ -378,7 +394,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // consumer step st: dS, dK of step st - 1, then dP of step st
   f32x16 dp[2];
   auto cstep = [&](int st, auto r) {
-    if (st + 1 < n_steps) issue(st + 1, obuf(IC<decltype(r)::value + 1>{}));
+    constexpr int R = decltype(r)::value;
+    if (st + 1 < n_steps) issue(obuf(IC<R + 1>{}));
     if (st > 0) {
       const float* xch = xchg[(st - 1) & 1][pair];
       const char* qt = qbuf(IC<decltype(r)::value + 5>{});  // tile st - 1
@@ -416,7 +433,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   };
 
   if (n_steps > 0) {
-    issue(0, producer ? qbuf(IC<0>{}) : obuf(IC<0>{}));
+    issue(producer ? qbuf(IC<0>{}) : obuf(IC<0>{}));
     publish(0);
     dma_barrier();
     // n_steps + 1 steps in both roles, so both pass the same barriers
