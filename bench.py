@@ -140,7 +140,7 @@ def main():
     out = torch.empty_like(qd)
     lse = torch.empty((w.Tq, w.hq), dtype=torch.float32, device=dev)
     dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
-    ws = torch.empty(max(ffa.ffa_bwd_workspace_size(w.Tq, w.hq), 16), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(ffa.ffa_bwd_workspace_size(w.Tq, w.Tk, w.hq, w.hkv, w.d), 16), dtype=torch.uint8, device=dev)
     qr, kr, ty = w.slices()
     pairs = visible_pairs(w)
     fwd_flop = 4.0 * w.d * w.hq * pairs

@@ -83,10 +83,15 @@ int ffa_fwd(const void* q, const void* k, const void* v,
             void* stream);
 
 /*
- * ffa_bwd_workspace_size -- bytes of device workspace ffa_bwd needs
- * (the fp32 row term D = rowsum(dO * out), [Tq][hq]).
+ * ffa_bwd_workspace_size -- bytes of device workspace ffa_bwd and
+ * ffa_bwd_planned need for these sizes (0 for invalid sizes or Tq == Tk == 0):
+ * the fp32 row term D = rowsum(dO * out) [Tq][hq], the dK/dV work list, and
+ * fp32 partial sums for key tiles whose list is cut into several runs (at
+ * most 512 runs x kv heads of 128 keys x d x 2: 64 MiB at d = 128, 32 MiB at
+ * d = 64, present whenever Tk > 0).  The contents need no initialisation and
+ * are scratch after the call.
  */
-size_t ffa_bwd_workspace_size(int64_t Tq, int hq);
+size_t ffa_bwd_workspace_size(int64_t Tq, int64_t Tk, int hq, int hkv, int d);
 
 /*
  * ffa_bwd -- backward pass of ffa_fwd for upstream gradient `dout`.
@@ -95,8 +100,10 @@ size_t ffa_bwd_workspace_size(int64_t Tq, int hq);
  * with the same slices, scale and softcap.  Writes dq [Tq][hq][d] and dk, dv
  * [Tk][hkv][d] (bf16) in full, zeros where a row or key takes part in no
  * visible cell.  dk and dv of a kv head sum over the q heads that read it.
- * `workspace` is device memory of ffa_bwd_workspace_size(Tq, hq) bytes
- * (or NULL: then the library allocates it on `stream`).  Deterministic.
+ * `workspace` is 16-byte aligned device memory of
+ * ffa_bwd_workspace_size(Tq, Tk, hq, hkv, d) bytes (or NULL: then the
+ * library allocates it on `stream`).  Deterministic: the same inputs give
+ * the same bits, whatever the order in which workgroups run.
  */
 int ffa_bwd(const void* q, const void* k, const void* v,
             const void* out, const float* lse, const void* dout,

@@ -68,7 +68,7 @@ def load_library():
     lib.ffa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, ip32, ip32, ip32,
                             i32, f32, f32, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.ffa_bwd.restype = ctypes.c_int
-    lib.ffa_bwd_workspace_size.argtypes = [i64, i32]
+    lib.ffa_bwd_workspace_size.argtypes = [i64, i64, i32, i32, i32]
     lib.ffa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.ffa_plan_host.argtypes = [i64, i64, ip32, ip32, ip32, i32, i32, i32, i32,
                                   ctypes.POINTER(ctypes.c_int64), ip32, i64, ip32]
@@ -178,8 +178,9 @@ def ffa_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, scale: float, softcap: f
     return out, lse
 
 
-def ffa_bwd_workspace_size(Tq: int, hq: int) -> int:
-    return int(load_library().ffa_bwd_workspace_size(Tq, hq))
+def ffa_bwd_workspace_size(Tq: int, Tk: int, hq: int, hkv: int, d: int) -> int:
+    """C ABI ``ffa_bwd_workspace_size``: bytes of device workspace the backward needs."""
+    return int(load_library().ffa_bwd_workspace_size(Tq, Tk, hq, hkv, d))
 
 
 def ffa_bwd(q, k, v, out, lse, dout, q_ranges, k_ranges, attn_type_map, scale: float,
@@ -201,7 +202,7 @@ def ffa_bwd(q, k, v, out, lse, dout, q_ranges, k_ranges, attn_type_map, scale: f
         _check_tensor(nm, t, torch.bfloat16, 3)
         if tuple(t.shape) != tuple(ref.shape):
             raise ValueError(f"{nm} must be shaped like its input")
-    ws_bytes = ffa_bwd_workspace_size(Tq, hq)
+    ws_bytes = ffa_bwd_workspace_size(Tq, Tk, hq, hkv, d)
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -366,11 +367,11 @@ def ffa_bwd_planned(plan, q, k, v, out, lse, dout, scale: float, softcap: float 
         _check_tensor(nm, t, torch.bfloat16, 3)
     _check_tensor("lse", lse, torch.float32, 2)
     Tq, hq, d = q.shape
-    hkv = k.shape[1]
+    Tk, hkv = k.shape[0], k.shape[1]
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    ws_bytes = ffa_bwd_workspace_size(Tq, hq)
+    ws_bytes = ffa_bwd_workspace_size(Tq, Tk, hq, hkv, d)
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None

@@ -179,6 +179,10 @@ struct BwdArgs {
   const DevEntry* entries;
   const int32_t* order;
   const DevSlice* slices;
+  const i32x4* items;       // dK/dV work items (key tile, entries, slot)
+  const i32x4* splits;      // key tiles split over several items
+  const int32_t* counts;    // [0] items, [1] split tiles
+  float* partial;           // fp32 dK^T / dV^T of the items of split tiles
   int32_t Tq, Tk, hq, hkv, grp;
   int32_t n_units;
   float scale;
@@ -250,9 +254,12 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     else return o_s1;
   };
 
+  // work item: a run of one key tile's entries, for kv head g
   const int u = blockIdx.x;
-  if (u >= a.n_units) return;
-  const int kt = plan_i32(a.order, u / a.hkv), g = u % a.hkv;
+  const int item = u / a.hkv, g = u % a.hkv;
+  if (item >= plan_i32(a.counts, 0)) return;
+  const i32x4 it = const_load<i32x4>(a.items, item);
+  const int kt = it[0], e_begin = it[1], e_end = it[2], slot = it[3];
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, hh = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pair = w & 3;
@@ -279,7 +286,6 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
 
-  const int e_begin = plan_i32(a.row_ptr, kt), e_end = plan_i32(a.row_ptr, kt + 1);
   const int n_steps = (e_end - e_begin) * a.grp;
   const int tro = tr_lane_offset<D>(lane);
   const int lrow = T::off(n, hh);
@@ -469,7 +475,22 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   }
 
   // accumulator column n is key `key`, rows are head dims
-  if (key < a.Tk) {
+  if (slot >= 0) {
+    // one run of a split key tile: fp32 partial sums, [dK^T | dV^T][key][dim]
+    float* dst = a.partial + ((int64_t)slot * a.hkv + g) * (2 * kDkvKeys * D) +
+                 (producer ? kDkvKeys * D : 0) + (32 * pair + n) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 x;
+        x[0] = acc[db][4 * j + 0];
+        x[1] = acc[db][4 * j + 1];
+        x[2] = acc[db][4 * j + 2];
+        x[3] = acc[db][4 * j + 3];
+        *reinterpret_cast<f32x4*>(dst + 32 * db + 8 * j + 4 * hh) = x;
+      }
+  } else if (key < a.Tk) {
     const int64_t off = ((int64_t)key * a.hkv + g) * D;
     __bf16* dst = producer ? a.dv : a.dk;
     const float mul = producer ? 1.0f : a.scale;
@@ -482,6 +503,142 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         wv[1] = pack_bf16x2(mul * acc[db][4 * j + 2], mul * acc[db][4 * j + 3]);
         *reinterpret_cast<u32x2*>(dst + off + 32 * db + 8 * j + 4 * hh) = wv;
       }
+  }
+}
+
+// ---------------------------------------------------------------- split
+// A key tile's list is one serial chain in the dK/dV kernel, so a tile that
+// many q tiles see (a global "sink" that every block attends, a long causal
+// sequence shared by few heads) would set the kernel's duration by itself.
+// bwd_split cuts every list longer than `ec` entries into runs of at most
+// ec entries, with ec chosen so that all runs over all kv heads number about
+// kBalanceItems (twice the 256 CUs): no run is then longer than half of one
+// CU's share of the work.  Runs of a split tile write fp32 partial sums and
+// bwd_dkdv_reduce adds them in run order, so the result does not depend on
+// timing.  Item and split counts are bounded on the host side:
+//   items  <= n_kt + E / ec <= n_kt + kBalanceItems / hkv
+//   splits <  E / ec        <= kBalanceItems / hkv
+// (E = entries of all key tiles); partial buffers are capped at
+// kMaxSlotHeads (runs of split tiles times kv heads) by doubling ec.
+constexpr int kSplitThreads = 1024;
+constexpr int kBalanceItems = 512;
+constexpr int kMinItemSteps = 32;   // (entry, q head) steps: never split below this
+constexpr int kMaxSlotHeads = 512;
+
+// Inclusive prefix sums of three values over the 1024 threads.
+__device__ __forceinline__ void block_scan3(int v[3], int (*s_wave)[16]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int y = __shfl_up(v[j], d, 64);
+      if (lane >= d) v[j] += y;
+    }
+  if (lane == 63)
+    for (int j = 0; j < 3; ++j) s_wave[j][w] = v[j];
+  __syncthreads();
+  for (int j = 0; j < 3; ++j) {
+    int off = 0;
+    for (int i = 0; i < w; ++i) off += s_wave[j][i];
+    v[j] += off;
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kSplitThreads) void bwd_split_kernel(const int32_t* __restrict__ row_ptr,
+                                                                  const int32_t* __restrict__ order,
+                                                                  int n_kt, int grp, int hkv, i32x4* items,
+                                                                  int items_cap, i32x4* splits, int splits_cap,
+                                                                  int32_t* counts) {
+  __shared__ int s_wave[3][16];
+  __shared__ int s_tot[3];
+  __shared__ long long s_slots;
+  const int tid = threadIdx.x;
+  const long long E = (long long)row_ptr[n_kt] - row_ptr[0];
+  long long ec = max((long long)((kMinItemSteps + grp - 1) / grp),
+                     (E * hkv + kBalanceItems - 1) / kBalanceItems);
+  if (ec < 1) ec = 1;
+  // runs of split tiles (one partial buffer each per kv head) for this ec
+  for (;;) {
+    if (tid == 0) s_slots = 0;
+    __syncthreads();
+    long long part = 0;
+    for (int u = tid; u < n_kt; u += kSplitThreads) {
+      const int kt = order[u];
+      const long long len = (long long)row_ptr[kt + 1] - row_ptr[kt];
+      if (len > ec) part += (len + ec - 1) / ec;
+    }
+    if (part) atomicAdd(reinterpret_cast<unsigned long long*>(&s_slots), (unsigned long long)part);
+    __syncthreads();
+    const long long slots = s_slots;
+    __syncthreads();
+    if (slots * hkv <= kMaxSlotHeads) break;
+    ec *= 2;
+  }
+
+  int base_item = 0, base_slot = 0, base_split = 0;
+  for (int u0 = 0; u0 < n_kt; u0 += kSplitThreads) {
+    const int u = u0 + tid;
+    int kt = 0, lo = 0, len = 0, ns = 0;
+    if (u < n_kt) {
+      kt = order[u];
+      lo = row_ptr[kt];
+      len = row_ptr[kt + 1] - lo;
+      ns = len > ec ? (int)((len + ec - 1) / ec) : 1;
+    }
+    const bool sp = ns > 1;
+    int v[3] = {ns, sp ? ns : 0, sp ? 1 : 0};
+    block_scan3(v, s_wave);
+    if (u < n_kt) {
+      const int item0 = base_item + v[0] - ns;
+      const int slot0 = base_slot + v[1] - (sp ? ns : 0);
+      const int ce = (len + ns - 1) / ns;
+      for (int c = 0; c < ns; ++c) {
+        const int e_lo = lo + min(len, c * ce), e_hi = lo + min(len, (c + 1) * ce);
+        if (item0 + c < items_cap) items[item0 + c] = i32x4{kt, e_lo, e_hi, sp ? slot0 + c : -1};
+      }
+      const int si = base_split + v[2] - 1;
+      if (sp && si < splits_cap) splits[si] = i32x4{kt, slot0, ns, 0};
+    }
+    if (tid == kSplitThreads - 1)
+      for (int j = 0; j < 3; ++j) s_tot[j] = v[j];
+    __syncthreads();
+    base_item += s_tot[0];
+    base_slot += s_tot[1];
+    base_split += s_tot[2];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    counts[0] = min(base_item, items_cap);
+    counts[1] = min(base_split, splits_cap);
+  }
+}
+
+// Sum of the partial dK^T / dV^T of a split tile's runs, in run order, to
+// bf16 dK (times the softmax scale) and dV.
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_reduce_kernel(BwdArgs a) {
+  const int u = blockIdx.x;
+  const int s = u / a.hkv, g = u % a.hkv;
+  if (s >= plan_i32(a.counts, 1)) return;
+  const i32x4 sp = const_load<i32x4>(a.splits, s);
+  const int kt = sp[0], slot0 = sp[1], ns = sp[2];
+  constexpr int kSlot = 2 * kDkvKeys * D;  // floats per (run, kv head)
+  for (int i = 4 * threadIdx.x; i < kSlot; i += 4 * kThreads) {
+    f32x4 sum = f32x4{};
+    for (int c = 0; c < ns; ++c)
+      sum += *reinterpret_cast<const f32x4*>(a.partial + ((int64_t)(slot0 + c) * a.hkv + g) * kSlot + i);
+    const bool is_v = i >= kDkvKeys * D;
+    const int r = is_v ? i - kDkvKeys * D : i;
+    const int key = kt * kDkvKeys + r / D, dim = r % D;
+    if (key < a.Tk) {
+      const float mul = is_v ? 1.0f : a.scale;
+      u32x2 w;
+      w[0] = pack_bf16x2(mul * sum[0], mul * sum[1]);
+      w[1] = pack_bf16x2(mul * sum[2], mul * sum[3]);
+      *reinterpret_cast<u32x2*>((is_v ? a.dv : a.dk) + ((int64_t)key * a.hkv + g) * D + dim) = w;
+    }
   }
 }
 
@@ -635,7 +792,6 @@ void fill_args(const BwdLaunch& p, BwdArgs* a) {
   a->v = static_cast<const __bf16*>(p.v);
   a->dout = static_cast<const __bf16*>(p.dout);
   a->lse = p.lse;
-  a->dvec = p.dvec;
   a->dq = static_cast<__bf16*>(p.dq);
   a->dk = static_cast<__bf16*>(p.dk);
   a->dv = static_cast<__bf16*>(p.dv);
@@ -659,21 +815,37 @@ void fill_args(const BwdLaunch& p, BwdArgs* a) {
 
 template <int D, bool SC>
 hipError_t launch_bwd_t(const BwdLaunch& p, hipStream_t stream) {
+  const BwdWorkspaceLayout L = bwd_workspace_layout(p.Tq, p.Tk, p.hq, p.hkv, p.d);
+  unsigned char* ws = static_cast<unsigned char*>(p.workspace);
   const int64_t rows = p.Tq * p.hq;
+  BwdArgs a;
+  fill_args(p, &a);
+  float* dvec = reinterpret_cast<float*>(ws + L.dvec);
+  a.dvec = dvec;
+  a.counts = reinterpret_cast<const int32_t*>(ws + L.counts);
+  a.items = reinterpret_cast<const i32x4*>(ws + L.items);
+  a.splits = reinterpret_cast<const i32x4*>(ws + L.splits);
+  a.partial = reinterpret_cast<float*>(ws + L.partial);
   if (rows > 0)
     hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + kThreads - 1) / kThreads)),
                        dim3(kThreads), 0, stream, static_cast<const __bf16*>(p.out),
-                       static_cast<const __bf16*>(p.dout), p.dvec, rows);
-  BwdArgs a;
-  fill_args(p, &a);
-  // dK, dV: one workgroup per (key tile, kv head), every key tile listed
+                       static_cast<const __bf16*>(p.dout), dvec, rows);
+  // dK, dV: key tiles cut into runs, one workgroup per (run, kv head), then
+  // the sums over the runs of split tiles
   a.row_ptr = p.kv_row_ptr;
   a.entries = reinterpret_cast<const DevEntry*>(p.kv_entries);
   a.order = p.kv_order;
   const int64_t n_kt = (p.Tk + kDkvKeys - 1) / kDkvKeys;
-  a.n_units = (int32_t)(n_kt * p.hkv);
-  if (a.n_units > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, SC>), dim3((unsigned)a.n_units), dim3(kDkvThreads), 0, stream, a);
+  if (n_kt > 0) {
+    hipLaunchKernelGGL(bwd_split_kernel, dim3(1), dim3(kSplitThreads), 0, stream, p.kv_row_ptr, p.kv_order,
+                       (int)n_kt, a.grp, a.hkv, reinterpret_cast<i32x4*>(ws + L.items), (int)L.items_cap,
+                       reinterpret_cast<i32x4*>(ws + L.splits), (int)L.splits_cap,
+                       reinterpret_cast<int32_t*>(ws + L.counts));
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, SC>), dim3((unsigned)(L.items_cap * p.hkv)), dim3(kDkvThreads), 0,
+                       stream, a);
+    hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<D>), dim3((unsigned)(L.splits_cap * p.hkv)), dim3(kThreads), 0,
+                       stream, a);
+  }
   // dQ: one workgroup per (q tile, head)
   a.row_ptr = p.q_row_ptr;
   a.entries = reinterpret_cast<const DevEntry*>(p.q_entries);
@@ -692,6 +864,30 @@ int bwd_kv_tile_rows() { return kDkvRows; }
 int bwd_kv_tile_cols() { return kDkvKeys; }
 int bwd_q_tile_rows() { return kDqRows; }
 int bwd_q_tile_cols() { return kDqKeys; }
+
+static size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+BwdWorkspaceLayout bwd_workspace_layout(int64_t Tq, int64_t Tk, int hq, int hkv, int d) {
+  BwdWorkspaceLayout L{};
+  const int64_t n_kt = Tk > 0 ? (Tk + kDkvKeys - 1) / kDkvKeys : 0;
+  const int64_t per_head = hkv > 0 ? kBalanceItems / hkv : 0;
+  L.items_cap = n_kt + per_head;
+  L.splits_cap = per_head > 0 ? per_head : 1;
+  const int64_t slot_heads = kMaxSlotHeads;
+  size_t off = 0;
+  L.dvec = off;
+  off += round256((size_t)(Tq > 0 ? Tq : 0) * (size_t)(hq > 0 ? hq : 0) * sizeof(float));
+  L.counts = off;
+  off += 256;
+  L.items = off;
+  off += round256((size_t)L.items_cap * 16);
+  L.splits = off;
+  off += round256((size_t)L.splits_cap * 16);
+  L.partial = off;
+  if (n_kt > 0) off += (size_t)slot_heads * 2 * kDkvKeys * (size_t)d * sizeof(float);
+  L.total = off;
+  return L;
+}
 
 hipError_t launch_bwd(const BwdLaunch& p, hipStream_t stream) {
   const bool sc = p.softcap > 0.f;

@@ -305,7 +305,7 @@ int bwd_planned(const ffa_plan_s* p, const void* q, const void* k, const void* v
       (rc = check_ptr(v, has_k, "v")) || (rc = check_ptr(dk, has_k, "dk")) ||
       (rc = check_ptr(dv, has_k, "dv")))
     return rc;
-  const size_t need = ffa_bwd_workspace_size(p->Tq, hq);
+  const size_t need = ffa_bwd_workspace_size(p->Tq, p->Tk, hq, hkv, d);
   if (workspace && workspace_bytes < need)
     return fail(FFA_ERR_INVALID_ARG, "workspace is smaller than ffa_bwd_workspace_size()");
   if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 15))
@@ -318,7 +318,7 @@ int bwd_planned(const ffa_plan_s* p, const void* q, const void* k, const void* v
   }
   ffa::BwdLaunch L;
   L.q = q; L.k = k; L.v = v; L.out = out; L.lse = lse; L.dout = dout;
-  L.dq = dq; L.dk = dk; L.dv = dv; L.dvec = static_cast<float*>(ws);
+  L.dq = dq; L.dk = dk; L.dv = dv; L.workspace = ws;
   L.Tq = p->Tq; L.Tk = p->Tk; L.hq = hq; L.hkv = hkv; L.d = d;
   L.scale = scale; L.softcap = softcap;
   L.kv_row_ptr = reinterpret_cast<const int32_t*>(p->dev + p->kv.off_row_ptr);
@@ -489,9 +489,10 @@ int ffa_fwd(const void* q, const void* k, const void* v, int64_t Tq, int64_t Tk,
   return rc2;
 }
 
-size_t ffa_bwd_workspace_size(int64_t Tq, int hq) {
-  if (Tq <= 0 || hq <= 0) return 0;
-  return align16(static_cast<size_t>(Tq) * static_cast<size_t>(hq) * sizeof(float));
+size_t ffa_bwd_workspace_size(int64_t Tq, int64_t Tk, int hq, int hkv, int d) {
+  if (Tq < 0 || Tk < 0 || hq <= 0 || hkv <= 0 || (d != 64 && d != 128)) return 0;
+  if (Tq == 0 && Tk == 0) return 0;
+  return ffa::bwd_workspace_layout(Tq, Tk, hq, hkv, d).total;
 }
 
 int ffa_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
@@ -512,7 +513,7 @@ int ffa_bwd(const void* q, const void* k, const void* v, const void* out, const 
       (rc = check_ptr(v, has_k, "v")) || (rc = check_ptr(dk, has_k, "dk")) ||
       (rc = check_ptr(dv, has_k, "dv")))
     return rc;
-  if (workspace && workspace_bytes < ffa_bwd_workspace_size(Tq, hq))
+  if (workspace && workspace_bytes < ffa_bwd_workspace_size(Tq, Tk, hq, hkv, d))
     return fail(FFA_ERR_INVALID_ARG, "workspace is smaller than ffa_bwd_workspace_size()");
   if (Tq == 0 && Tk == 0) return FFA_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);

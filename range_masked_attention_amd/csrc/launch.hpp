@@ -40,7 +40,7 @@ struct BwdLaunch {
   void* dq;
   void* dk;
   void* dv;
-  float* dvec;  // device workspace [Tq * hq]
+  void* workspace;  // device memory laid out by bwd_workspace_layout()
   int64_t Tq, Tk;
   int hq, hkv, d;
   float scale, softcap;
@@ -96,5 +96,14 @@ int bwd_kv_tile_cols();  // keys per dK/dV workgroup
 int bwd_q_tile_rows();   // q rows per dQ workgroup
 int bwd_q_tile_cols();   // keys per dQ step
 hipError_t launch_bwd(const BwdLaunch& p, hipStream_t stream);
+
+// Byte offsets of the backward workspace pieces (each 256-byte aligned):
+// the row term D [Tq][hq] fp32, two counters, the dK/dV work items and the
+// split-tile records (capacities in records), and the fp32 partial sums.
+struct BwdWorkspaceLayout {
+  size_t dvec, counts, items, splits, partial, total;
+  int64_t items_cap, splits_cap;
+};
+BwdWorkspaceLayout bwd_workspace_layout(int64_t Tq, int64_t Tk, int hq, int hkv, int d);
 
 }  // namespace ffa

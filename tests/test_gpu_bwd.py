@@ -77,6 +77,52 @@ def test_random_slices_full_compare(case):
             _cmp(n, g, r, f"{case} trial {trial}", m)
 
 
+def _sink_slices(T, blk, sink, window):
+    """Blocks of `blk` rows: each sees keys [0, sink) (FULL) and a causal window."""
+    qr, kr, ty = [], [], []
+    for b in range(T // blk):
+        s, e = b * blk, (b + 1) * blk
+        if b == 0:
+            qr.append((s, e)); kr.append((0, e)); ty.append(O.CAUSAL)
+            continue
+        qr.append((s, e)); kr.append((0, sink)); ty.append(O.FULL)
+        qr.append((s, e)); kr.append((max(sink, e - window), e)); ty.append(O.CAUSAL)
+    return (np.array(qr, np.int32), np.array(kr, np.int32), np.array(ty, np.int32))
+
+
+# Key tiles whose lists are cut into several runs (dK/dV partial sums added by
+# a separate pass).  "sink": the 128-key sink tile is seen by all 64 q tiles
+# and is cut into 8 runs, most window tiles into 2.  "cap": 40 key tiles x 8 kv
+# heads, each seen by 64 q tiles: runs of 40 entries would need 640 partial
+# buffers, over the 512 the workspace holds, so the run length doubles and no
+# tile is split (the run-length rule's fallback).
+SPLIT_CASES = [
+    ("sink", 4096, 4096, 4, 1, 64, 0.0),
+    ("sink", 4096, 4096, 8, 2, 128, 30.0),
+    ("cap", 4096, 5120, 8, 8, 64, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[f"{c[0]}_h{c[3]}:{c[4]}_d{c[5]}_cap{c[6]}" for c in SPLIT_CASES])
+def test_split_key_tiles_full_compare(case):
+    kind, Tq, Tk, hq, hkv, dd, cap = case
+    say(f"bwd split key tiles {case}")
+    if kind == "sink":
+        qr, kr, ty = _sink_slices(Tq, 512, 128, 1024)
+    else:
+        qr, kr, ty = (np.array([[0, Tq]], np.int32), np.array([[0, Tk]], np.int32), np.array([O.FULL], np.int32))
+    q, k, v, do = W.make_tensors(Tq, Tk, hq, hkv, dd, seed=11)
+    scale = dd ** -0.5
+    dq, dk, dv = _bwd_gpu(q, k, v, do, qr, kr, ty, scale, cap, dev())
+    again = _bwd_gpu(q, k, v, do, qr, kr, ty, scale, cap, dev())
+    for n, a, b in zip(("dq", "dk", "dv"), (dq, dk, dv), again):
+        assert torch.equal(a, b), f"{case}: {n} differs between two identical calls"
+    rq, rk, rv, mags = O.attention_bwd(to64(q), to64(k), to64(v), to64(do), qr, kr, ty, scale, cap,
+                                       magnitudes=True)
+    e = [_cmp(n, g, r, str(case), m) for (n, g, r), m in zip((("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)), mags)]
+    say(f"  dq/dk/dv max-abs {e[0]:.3e} {e[1]:.3e} {e[2]:.3e}")
+
+
 def _visible_rows(qr, kr, ty, Tq, Tk):
     """Rows that see at least one key (slices are disjoint rectangles)."""
     sl = O.normalise_slices(qr, kr, ty, Tq, Tk)

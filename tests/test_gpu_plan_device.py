@@ -142,7 +142,7 @@ def test_graph_capture_replays_new_slice_lists():
     out = torch.empty_like(qd)
     lse = torch.empty((w.Tq, w.hq), dtype=torch.float32, device=d)
     dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
-    bws = torch.empty(max(ffa.ffa_bwd_workspace_size(w.Tq, w.hq), 16), dtype=torch.uint8, device=d)
+    bws = torch.empty(max(ffa.ffa_bwd_workspace_size(w.Tq, w.Tk, w.hq, w.hkv, w.d), 16), dtype=torch.uint8, device=d)
 
     def body():
         ffa.ffa_plan_refresh(plan)
