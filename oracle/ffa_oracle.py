@@ -25,6 +25,14 @@ What is computed, and where the pages define it:
 * Scores: ``u = scale * q . k``; optional softcap ``s = c * tanh(u / c)``
   (softcapping limits logit growth: FlexAttention paper summary, section 2,
   attention variants); masked cells are -inf after the cap.
+* Optional distance bias (ALiBi): the pages list ALiBi as a variant that
+  adds a bias depending on the distance between query and key positions
+  (FlexAttention paper summary, section 2, attention variants; section 3.1,
+  a position-dependent score bias) and give no formula.  Read here as the
+  linear form ``s += slope[h] * (j - i)`` with one slope per q head, i and j
+  the token indices along the q and k axes, added after the softcap and
+  before the mask.  With slope > 0 on a causal mask (j <= i) it is the usual
+  ALiBi penalty ``-slope * (i - j)``.
 * Output and log-sum-exp per row (natural log).  A row that sees no key gets
   out = 0 and lse = -inf.
 * GQA: q head h reads kv head ``h // (hq // hkv)`` (repro script: 8 q heads,
@@ -105,7 +113,7 @@ def visible_count(slices, Tq: int, Tk: int, block: int = 1024) -> int:
 # --------------------------------------------------------------------------
 # forward
 # --------------------------------------------------------------------------
-def _row_block_attention(q, k, v, slices, scale, softcap, rows, Tk):
+def _row_block_attention(q, k, v, slices, scale, softcap, rows, Tk, alibi_slopes=None):
     """Scores, probabilities, output and lse for one block of rows.
 
     Returns (cols, vis, s, p, out, lse) per q head, where ``cols`` are the key
@@ -130,6 +138,8 @@ def _row_block_attention(q, k, v, slices, scale, softcap, rows, Tk):
             continue
         u = scale * (q[rows, h, :] @ k[cols, g, :].T)
         s = softcap * np.tanh(u / softcap) if softcap > 0 else u
+        if alibi_slopes is not None:
+            s = s + alibi_slopes[h] * (cols[None, :] - rows[:, None]).astype(np.float64)
         s = np.where(vis, s, -np.inf)
         m = s.max(axis=1)
         has = np.isfinite(m)
@@ -143,12 +153,22 @@ def _row_block_attention(q, k, v, slices, scale, softcap, rows, Tk):
     return cols, vis, res
 
 
+def _slopes(alibi_slopes, hq):
+    if alibi_slopes is None:
+        return None
+    a = np.asarray(alibi_slopes, dtype=np.float64).reshape(-1)
+    if a.size != hq:
+        raise ValueError("alibi_slopes needs one slope per q head")
+    return a
+
+
 def attention_fwd(q, k, v, q_ranges, k_ranges, types, scale, softcap=0.0,
-                  rows=None, block=256):
+                  rows=None, block=256, alibi_slopes=None):
     """Forward pass: ``out [n, hq, d]`` and ``lse [n, hq]`` for ``rows``.
 
     ``q`` is [Tq, hq, d], ``k`` and ``v`` are [Tk, hkv, d] (float64 arrays).
     ``rows`` selects which query rows to compute (all rows when None).
+    ``alibi_slopes`` ([hq] or None): the distance bias described above.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -160,12 +180,13 @@ def attention_fwd(q, k, v, q_ranges, k_ranges, types, scale, softcap=0.0,
     if softcap < 0:
         raise ValueError("softcap must be >= 0")
     slices = normalise_slices(q_ranges, k_ranges, types, Tq, Tk)
+    slopes = _slopes(alibi_slopes, hq)
     rows = np.arange(Tq) if rows is None else np.asarray(rows, dtype=np.int64)
     out = np.zeros((rows.size, hq, d))
     lse = np.full((rows.size, hq), -np.inf)
     for b0 in range(0, rows.size, block):
         rb = rows[b0:b0 + block]
-        _, _, res = _row_block_attention(q, k, v, slices, scale, softcap, rb, Tk)
+        _, _, res = _row_block_attention(q, k, v, slices, scale, softcap, rb, Tk, slopes)
         for h, r in enumerate(res):
             if r is None:
                 continue
@@ -178,13 +199,15 @@ def attention_fwd(q, k, v, q_ranges, k_ranges, types, scale, softcap=0.0,
 # backward
 # --------------------------------------------------------------------------
 def attention_bwd(q, k, v, dout, q_ranges, k_ranges, types, scale, softcap=0.0,
-                  rows=None, keys=None, block=256, magnitudes=False):
+                  rows=None, keys=None, block=256, magnitudes=False, alibi_slopes=None):
     """Gradients of ``sum(dout * out)``: dq at ``rows``, dk and dv at ``keys``.
 
     Chain rule through the forward above, in the usual flash-attention form:
     ``P = softmax(s)``, ``dV = P^T dO``, ``dP = dO V^T``,
     ``D = rowsum(dO * out)``, ``dS = P * (dP - D)``, the softcap derivative
-    ``1 - tanh^2 = 1 - (s / c)^2``, ``dQ = scale * dU K``, ``dK = scale * dU^T Q``.
+    ``1 - tanh^2(u / c)``, ``dQ = scale * dU K``, ``dK = scale * dU^T Q``.  The
+    distance bias is a constant added to the scores: it changes P and nothing
+    else in these formulas.
     GQA: dk and dv of a kv head sum over the q heads that read it.
     Returns (dq [len(rows), hq, d], dk [len(keys), hkv, d], dv [len(keys), hkv, d]).
 
@@ -203,6 +226,7 @@ def attention_bwd(q, k, v, dout, q_ranges, k_ranges, types, scale, softcap=0.0,
     Tk, hkv, _ = k.shape
     grp = hq // hkv
     slices = normalise_slices(q_ranges, k_ranges, types, Tq, Tk)
+    slopes = _slopes(alibi_slopes, hq)
     rows = np.arange(Tq) if rows is None else np.asarray(rows, dtype=np.int64)
     keys = np.arange(Tk) if keys is None else np.asarray(keys, dtype=np.int64)
 
@@ -227,7 +251,7 @@ def attention_bwd(q, k, v, dout, q_ranges, k_ranges, types, scale, softcap=0.0,
         dq_m, dk_m, dv_m = np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv)
     for b0 in range(0, work.size, block):
         rb = work[b0:b0 + block]
-        cols, vis, res = _row_block_attention(q, k, v, slices, scale, softcap, rb, Tk)
+        cols, vis, res = _row_block_attention(q, k, v, slices, scale, softcap, rb, Tk, slopes)
         if cols.size == 0:
             continue
         kp = key_pos[cols]
@@ -242,7 +266,7 @@ def attention_bwd(q, k, v, dout, q_ranges, k_ranges, types, scale, softcap=0.0,
             dP = do @ v[cols, g, :].T
             dS = p * (dP - D[:, None])
             if softcap > 0:
-                dU = dS * (1.0 - (np.where(vis, s, 0.0) / softcap) ** 2)
+                dU = dS * (1.0 - np.tanh(u / softcap) ** 2)
             else:
                 dU = dS
             if dq_mask.any():

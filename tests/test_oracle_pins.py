@@ -434,3 +434,85 @@ def test_backward_term_magnitudes_bound_the_gradients():
     # dO >= 0 and P >= 0: dv is a sum of non-negative terms, so it equals its magnitude
     _, _, dv2, (_, _, mv2) = O.attention_bwd(q, k, v, np.abs(do), qr, kr, ty, 0.4, magnitudes=True)
     np.testing.assert_allclose(dv2, mv2, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- distance bias (ALiBi)
+def test_alibi_closed_form_zero_queries():
+    """q = 0: every score is the bias m (j - i), so over keys [0, n) the weights
+    are e^{m j} / sum_j e^{m j} for every row, and
+    lse_i = -m i + log((e^{m n} - 1) / (e^m - 1))."""
+    rng = np.random.default_rng(40)
+    Tq, n, d = 9, 13, 4
+    slopes = np.array([0.25, -0.125, 0.5])
+    q = np.zeros((Tq, 3, d))
+    k, v = _rand((n, 1, d), rng), _rand((n, 1, d), rng)
+    out, lse = O.attention_fwd(q, k, v, [[0, Tq]], [[0, n]], [O.FULL], 0.7, alibi_slopes=slopes)
+    for h, m in enumerate(slopes):
+        w = np.array([math.exp(m * j) for j in range(n)])
+        w /= w.sum()
+        for i in range(Tq):
+            assert abs(lse[i, h] - (-m * i + math.log(math.expm1(m * n) / math.expm1(m)))) < 1e-12
+            np.testing.assert_allclose(out[i, h], w @ v[:, 0], rtol=0, atol=1e-13)
+
+
+def test_alibi_causal_matches_sdpa_float_mask():
+    """One causal slice over the whole sequence with ALiBi slopes 2^(-8h/H):
+    torch SDPA with the bias (and -inf above the diagonal) as a float mask."""
+    rng = np.random.default_rng(41)
+    T, hq, hkv, d = 70, 4, 2, 16
+    slopes = np.array([2.0 ** (-8.0 * (h + 1) / hq) for h in range(hq)])
+    q, k, v = _rand((T, hq, d), rng), _rand((T, hkv, d), rng), _rand((T, hkv, d), rng)
+    out, lse = O.attention_fwd(q, k, v, [[0, T]], [[0, T]], [O.CAUSAL], 0.3, alibi_slopes=slopes)
+    i = torch.arange(T, dtype=torch.float64)[:, None]
+    j = torch.arange(T, dtype=torch.float64)[None, :]
+    above = j > i
+    mask = torch.stack([torch.where(above, float("-inf"), float(m) * (j - i)) for m in slopes])[None]
+    kr = np.repeat(k, hq // hkv, axis=1)
+    vr = np.repeat(v, hq // hkv, axis=1)
+    np.testing.assert_allclose(out, _sdpa(q, kr, vr, 0.3, mask=mask), rtol=1e-10, atol=1e-12)
+    scores = 0.3 * np.einsum("ihc,jhc->hij", q, kr) + mask[0].numpy()
+    np.testing.assert_allclose(lse, logsumexp(scores, axis=-1).T, rtol=1e-12, atol=1e-12)
+
+
+def test_alibi_zero_slopes_change_nothing():
+    rng = np.random.default_rng(42)
+    T, d = 60, 8
+    qr, kr, ty = W.random_slices(rng, T, T, max_slices=5)
+    q, k, v = _rand((T, 2, d), rng), _rand((T, 1, d), rng), _rand((T, 1, d), rng)
+    a = O.attention_fwd(q, k, v, qr, kr, ty, 0.4, softcap=2.0)
+    b = O.attention_fwd(q, k, v, qr, kr, ty, 0.4, softcap=2.0, alibi_slopes=[0.0, 0.0])
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("cap", [0.0, 3.0])
+def test_alibi_backward_matches_autograd(cap):
+    """Bias added after the softcap: dense masked formula under torch autograd."""
+    rng = np.random.default_rng(43)
+    Tq, Tk, hq, hkv, d = 40, 52, 4, 2, 8
+    slopes = np.array([0.3, -0.2, 0.05, 0.0])
+    qr, kr, ty = W.random_slices(rng, Tq, Tk, max_slices=5, n_dummies=1)
+    q, k, v = _rand((Tq, hq, d), rng), _rand((Tk, hkv, d), rng), _rand((Tk, hkv, d), rng)
+    do = _rand((Tq, hq, d), rng)
+    dq, dk, dv = O.attention_bwd(q, k, v, do, qr, kr, ty, 0.5, softcap=cap, alibi_slopes=slopes)
+    vis = torch.from_numpy(O.visibility(O.normalise_slices(qr, kr, ty, Tq, Tk),
+                                        np.arange(Tq), np.arange(Tk)) > 0)
+    tq = torch.from_numpy(q).requires_grad_()
+    tk = torch.from_numpy(k).requires_grad_()
+    tv = torch.from_numpy(v).requires_grad_()
+    kk = tk.repeat_interleave(hq // hkv, dim=1)
+    vv = tv.repeat_interleave(hq // hkv, dim=1)
+    u = 0.5 * torch.einsum("ihc,jhc->hij", tq, kk)
+    s = cap * torch.tanh(u / cap) if cap else u
+    dist = (torch.arange(Tk, dtype=torch.float64)[None, :] - torch.arange(Tq, dtype=torch.float64)[:, None])
+    s = s + torch.from_numpy(slopes)[:, None, None] * dist[None]
+    s = s.masked_fill(~vis[None], float("-inf"))
+    has = vis.any(dim=1)
+    p = torch.softmax(torch.where(has[None, :, None], s, torch.zeros_like(s)), dim=-1)
+    p = torch.where(vis[None], p, torch.zeros_like(p))
+    out = torch.einsum("hij,jhc->ihc", p, vv)
+    (out * torch.from_numpy(do)).sum().backward()
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-10, atol=1e-11)
+    o_ref, _ = O.attention_fwd(q, k, v, qr, kr, ty, 0.5, softcap=cap, alibi_slopes=slopes)
+    np.testing.assert_allclose(o_ref, out.detach().numpy(), rtol=1e-10, atol=1e-12)
