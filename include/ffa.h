@@ -116,6 +116,39 @@ int ffa_bwd(const void* q, const void* k, const void* v,
             void* stream);
 
 /*
+ * Distance bias (ALiBi).  The FlexAttention paper summary lists ALiBi among
+ * the attention variants as a bias that depends on the distance between the
+ * query and key positions (section 2; section 3.1, a position-dependent score
+ * bias).  The _ex entry points take it as one fp32 slope per q head:
+ *   s_ij += alibi_slopes[h] * (j - i)      (after the softcap, before the mask)
+ * with i and j the token indices along the q and k axes.  With slope > 0 on a
+ * causal mask (j <= i) this is ALiBi's linear penalty on distance.
+ *   alibi_slopes  DEVICE pointer to hq finite fp32 values, 4-byte aligned,
+ *                 read by the kernels (left alone); NULL = no bias, which is
+ *                 exactly the entry point without _ex.
+ * lse includes the bias.  The bias is formed as slope * (j - i) in fp32 from
+ * the exact integer j - i; where every visible key of a row is far from it
+ * (|slope * (j - i)| in the thousands), lse itself is large and carries fp32
+ * rounding of that size.  Errors as for the entry points without _ex.
+ */
+int ffa_fwd_ex(const void* q, const void* k, const void* v,
+               int64_t Tq, int64_t Tk, int hq, int hkv, int d,
+               const int32_t* q_ranges, const int32_t* k_ranges,
+               const int32_t* attn_type_map, int R,
+               float scale, float softcap, const float* alibi_slopes,
+               void* out, float* lse, void* stream);
+
+int ffa_bwd_ex(const void* q, const void* k, const void* v,
+               const void* out, const float* lse, const void* dout,
+               int64_t Tq, int64_t Tk, int hq, int hkv, int d,
+               const int32_t* q_ranges, const int32_t* k_ranges,
+               const int32_t* attn_type_map, int R,
+               float scale, float softcap, const float* alibi_slopes,
+               void* dq, void* dk, void* dv,
+               void* workspace, size_t workspace_bytes,
+               void* stream);
+
+/*
  * ffa_plan_host -- the block-sparse plan, on the host only (no GPU call).
  *
  * For tiles of bm query rows by bn key columns, lists every (tile, other
@@ -176,6 +209,22 @@ int ffa_bwd_planned(ffa_plan_t plan,
                     int hq, int hkv, int d, float scale, float softcap,
                     void* dq, void* dk, void* dv,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ffa_fwd_planned / ffa_bwd_planned with the distance bias of ffa_fwd_ex
+ * (alibi_slopes: device, hq fp32 slopes, or NULL). */
+int ffa_fwd_planned_ex(ffa_plan_t plan,
+                       const void* q, const void* k, const void* v,
+                       int hq, int hkv, int d, float scale, float softcap,
+                       const float* alibi_slopes,
+                       void* out, float* lse, void* stream);
+
+int ffa_bwd_planned_ex(ffa_plan_t plan,
+                       const void* q, const void* k, const void* v,
+                       const void* out, const float* lse, const void* dout,
+                       int hq, int hkv, int d, float scale, float softcap,
+                       const float* alibi_slopes,
+                       void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* Release a plan: its device memory is freed in order on `stream`, after the
  * work already enqueued there (a plan from ffa_plan_create_device lives in

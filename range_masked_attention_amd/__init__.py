@@ -28,6 +28,7 @@ __all__ = [
     "ffa_plan_create", "ffa_fwd_planned", "ffa_bwd_planned", "ffa_plan_destroy",
     "ffa_plan_device_workspace_size", "ffa_plan_create_device", "ffa_plan_refresh", "ffa_plan_status",
     "ffa_plan_export", "FFA_PLAN_BAD_SLICE", "FFA_PLAN_CAPACITY", "flex_flash_attn_func",
+    "alibi_geometric_slopes", "ffa_fwd_ex", "ffa_bwd_ex", "ffa_fwd_planned_ex", "ffa_bwd_planned_ex",
 ]
 
 FULL = 0
@@ -68,6 +69,12 @@ def load_library():
     lib.ffa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, ip32, ip32, ip32,
                             i32, f32, f32, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.ffa_bwd.restype = ctypes.c_int
+    lib.ffa_fwd_ex.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, ip32, ip32, ip32, i32,
+                               f32, f32, vp, vp, vp, vp]
+    lib.ffa_fwd_ex.restype = ctypes.c_int
+    lib.ffa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, ip32, ip32, ip32,
+                               i32, f32, f32, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.ffa_bwd_ex.restype = ctypes.c_int
     lib.ffa_bwd_workspace_size.argtypes = [i64, i64, i32, i32, i32]
     lib.ffa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.ffa_plan_host.argtypes = [i64, i64, ip32, ip32, ip32, i32, i32, i32, i32,
@@ -80,6 +87,11 @@ def load_library():
     lib.ffa_bwd_planned.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, f32,
                                     vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.ffa_bwd_planned.restype = ctypes.c_int
+    lib.ffa_fwd_planned_ex.argtypes = [vp, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp, vp, vp]
+    lib.ffa_fwd_planned_ex.restype = ctypes.c_int
+    lib.ffa_bwd_planned_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, vp,
+                                       vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.ffa_bwd_planned_ex.restype = ctypes.c_int
     lib.ffa_plan_destroy.argtypes = [vp, vp]
     lib.ffa_plan_destroy.restype = ctypes.c_int
     lib.ffa_plan_device_workspace_size.argtypes = [i64, i64, i32, i64, ctypes.POINTER(ctypes.c_size_t)]
@@ -151,9 +163,36 @@ def _check_tensor(name, t, dtype, ndim):
         raise ValueError(f"{name} must be contiguous")
 
 
+def alibi_geometric_slopes(hq: int):
+    """ALiBi's geometric head slopes 2^(-8 h / hq), h = 1 .. hq, as a list.
+
+    Pass them (as an fp32 tensor on the GPU) to the ``alibi_slopes`` argument,
+    which adds ``slope[h] * (j - i)`` to the scores: with positive slopes on a
+    causal mask, a penalty growing linearly with the distance i - j.
+    """
+    return [2.0 ** (-8.0 * (h + 1) / hq) for h in range(hq)]
+
+
+def _slopes_ptr(slopes, hq: int, device):
+    """Device pointer of an fp32 [hq] slope tensor, or None."""
+    import torch
+    if slopes is None:
+        return None
+    if not isinstance(slopes, torch.Tensor):
+        raise TypeError("alibi_slopes must be a torch.Tensor (fp32 [hq] on the GPU)")
+    if slopes.dtype != torch.float32 or tuple(slopes.shape) != (hq,):
+        raise ValueError(f"alibi_slopes must be fp32 of shape ({hq},), got {slopes.dtype} {tuple(slopes.shape)}")
+    if not slopes.is_cuda or slopes.device != device or not slopes.is_contiguous():
+        raise ValueError("alibi_slopes must be a contiguous tensor on the inputs' GPU")
+    return slopes.data_ptr()
+
+
 def ffa_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, scale: float, softcap: float = 0.0,
-            out=None, lse=None):
-    """C ABI ``ffa_fwd`` on torch tensors.  Returns (out [Tq,hq,d] bf16, lse [Tq,hq] fp32)."""
+            out=None, lse=None, alibi_slopes=None):
+    """C ABI ``ffa_fwd`` (``ffa_fwd_ex`` with ``alibi_slopes``) on torch tensors.
+
+    Returns (out [Tq,hq,d] bf16, lse [Tq,hq] fp32).
+    """
     import torch
     lib = load_library()
     for nm, t in (("q", q), ("k", k), ("v", v)):
@@ -171,9 +210,11 @@ def ffa_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, scale: float, softcap: f
     if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (Tq, hq):
         raise ValueError("out must be shaped like q and lse [Tq, hq]")
     qr, kr, ty = _host_slices(q_ranges, k_ranges, attn_type_map)
-    rc = lib.ffa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), Tq, Tk, hq, hkv, d,
-                     _iptr(qr), _iptr(kr), _iptr(ty), qr.shape[0], float(scale), float(softcap),
-                     out.data_ptr(), lse.data_ptr(), _stream_handle(q))
+    sp = _slopes_ptr(alibi_slopes, hq, q.device)
+    head = (q.data_ptr(), k.data_ptr(), v.data_ptr(), Tq, Tk, hq, hkv, d,
+            _iptr(qr), _iptr(kr), _iptr(ty), qr.shape[0], float(scale), float(softcap))
+    tail = (out.data_ptr(), lse.data_ptr(), _stream_handle(q))
+    rc = lib.ffa_fwd(*head, *tail) if sp is None else lib.ffa_fwd_ex(*head, sp, *tail)
     _check(rc)
     return out, lse
 
@@ -184,8 +225,11 @@ def ffa_bwd_workspace_size(Tq: int, Tk: int, hq: int, hkv: int, d: int) -> int:
 
 
 def ffa_bwd(q, k, v, out, lse, dout, q_ranges, k_ranges, attn_type_map, scale: float,
-            softcap: float = 0.0, dq=None, dk=None, dv=None, workspace=None):
-    """C ABI ``ffa_bwd`` on torch tensors.  Returns (dq, dk, dv) in bf16."""
+            softcap: float = 0.0, dq=None, dk=None, dv=None, workspace=None, alibi_slopes=None):
+    """C ABI ``ffa_bwd`` (``ffa_bwd_ex`` with ``alibi_slopes``) on torch tensors.
+
+    Returns (dq, dk, dv) in bf16.
+    """
     import torch
     lib = load_library()
     for nm, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
@@ -208,10 +252,12 @@ def ffa_bwd(q, k, v, out, lse, dout, q_ranges, k_ranges, attn_type_map, scale: f
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     qr, kr, ty = _host_slices(q_ranges, k_ranges, attn_type_map)
-    rc = lib.ffa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                     dout.data_ptr(), Tq, Tk, hq, hkv, d, _iptr(qr), _iptr(kr), _iptr(ty),
-                     qr.shape[0], float(scale), float(softcap), dq.data_ptr(), dk.data_ptr(),
-                     dv.data_ptr(), ws_ptr, ws_len, _stream_handle(q))
+    sp = _slopes_ptr(alibi_slopes, hq, q.device)
+    head = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+            dout.data_ptr(), Tq, Tk, hq, hkv, d, _iptr(qr), _iptr(kr), _iptr(ty),
+            qr.shape[0], float(scale), float(softcap))
+    tail = (dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_len, _stream_handle(q))
+    rc = lib.ffa_bwd(*head, *tail) if sp is None else lib.ffa_bwd_ex(*head, sp, *tail)
     _check(rc)
     return dq, dk, dv
 
@@ -340,8 +386,9 @@ def ffa_plan_export(plan, which: int, device=None):
     return row_ptr, entries[:n], order[:nt.value]
 
 
-def ffa_fwd_planned(plan, q, k, v, scale: float, softcap: float = 0.0, out=None, lse=None):
-    """C ABI ``ffa_fwd_planned``: the forward kernel alone, on a prepared plan."""
+def ffa_fwd_planned(plan, q, k, v, scale: float, softcap: float = 0.0, out=None, lse=None,
+                    alibi_slopes=None):
+    """C ABI ``ffa_fwd_planned`` (``_ex`` with ``alibi_slopes``): the forward kernel alone."""
     import torch
     lib = load_library()
     for nm, t in (("q", q), ("k", k), ("v", v)):
@@ -352,15 +399,16 @@ def ffa_fwd_planned(plan, q, k, v, scale: float, softcap: float = 0.0, out=None,
     lse = torch.empty((Tq, hq), dtype=torch.float32, device=q.device) if lse is None else lse
     _check_tensor("out", out, torch.bfloat16, 3)
     _check_tensor("lse", lse, torch.float32, 2)
-    _check(lib.ffa_fwd_planned(plan, q.data_ptr(), k.data_ptr(), v.data_ptr(), hq, hkv, d,
-                               float(scale), float(softcap), out.data_ptr(), lse.data_ptr(),
-                               _stream_handle(q)))
+    sp = _slopes_ptr(alibi_slopes, hq, q.device)
+    head = (plan, q.data_ptr(), k.data_ptr(), v.data_ptr(), hq, hkv, d, float(scale), float(softcap))
+    tail = (out.data_ptr(), lse.data_ptr(), _stream_handle(q))
+    _check(lib.ffa_fwd_planned(*head, *tail) if sp is None else lib.ffa_fwd_planned_ex(*head, sp, *tail))
     return out, lse
 
 
 def ffa_bwd_planned(plan, q, k, v, out, lse, dout, scale: float, softcap: float = 0.0,
-                    dq=None, dk=None, dv=None, workspace=None):
-    """C ABI ``ffa_bwd_planned``: the backward kernels alone, on a prepared plan."""
+                    dq=None, dk=None, dv=None, workspace=None, alibi_slopes=None):
+    """C ABI ``ffa_bwd_planned`` (``_ex`` with ``alibi_slopes``): the backward kernels alone."""
     import torch
     lib = load_library()
     for nm, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
@@ -376,17 +424,49 @@ def ffa_bwd_planned(plan, q, k, v, out, lse, dout, scale: float, softcap: float 
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib.ffa_bwd_planned(plan, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                               lse.data_ptr(), dout.data_ptr(), hq, hkv, d, float(scale),
-                               float(softcap), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                               ws_ptr, ws_len, _stream_handle(q)))
+    sp = _slopes_ptr(alibi_slopes, hq, q.device)
+    head = (plan, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+            dout.data_ptr(), hq, hkv, d, float(scale), float(softcap))
+    tail = (dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_len, _stream_handle(q))
+    _check(lib.ffa_bwd_planned(*head, *tail) if sp is None else lib.ffa_bwd_planned_ex(*head, sp, *tail))
     return dq, dk, dv
+
+
+def ffa_fwd_ex(q, k, v, q_ranges, k_ranges, attn_type_map, scale: float, softcap: float,
+               alibi_slopes, out=None, lse=None):
+    """C ABI ``ffa_fwd_ex``: ``ffa_fwd`` with a distance bias (``alibi_slopes``: fp32 [hq] or None)."""
+    return ffa_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, scale, softcap, out=out, lse=lse,
+                   alibi_slopes=alibi_slopes)
+
+
+def ffa_bwd_ex(q, k, v, out, lse, dout, q_ranges, k_ranges, attn_type_map, scale: float,
+               softcap: float, alibi_slopes, dq=None, dk=None, dv=None, workspace=None):
+    """C ABI ``ffa_bwd_ex``: ``ffa_bwd`` with a distance bias (``alibi_slopes``: fp32 [hq] or None)."""
+    return ffa_bwd(q, k, v, out, lse, dout, q_ranges, k_ranges, attn_type_map, scale, softcap,
+                   dq=dq, dk=dk, dv=dv, workspace=workspace, alibi_slopes=alibi_slopes)
+
+
+def ffa_fwd_planned_ex(plan, q, k, v, scale: float, softcap: float, alibi_slopes, out=None, lse=None):
+    """C ABI ``ffa_fwd_planned_ex``: ``ffa_fwd_planned`` with a distance bias."""
+    return ffa_fwd_planned(plan, q, k, v, scale, softcap, out=out, lse=lse, alibi_slopes=alibi_slopes)
+
+
+def ffa_bwd_planned_ex(plan, q, k, v, out, lse, dout, scale: float, softcap: float, alibi_slopes,
+                       dq=None, dk=None, dv=None, workspace=None):
+    """C ABI ``ffa_bwd_planned_ex``: ``ffa_bwd_planned`` with a distance bias."""
+    return ffa_bwd_planned(plan, q, k, v, out, lse, dout, scale, softcap, dq=dq, dk=dk, dv=dv,
+                           workspace=workspace, alibi_slopes=alibi_slopes)
 
 
 def flex_flash_attn_func(q, k, v, q_ranges, k_ranges, attn_type_map,
                          max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
-                         softmax_scale: Optional[float] = None, softcap: float = 0.0):
+                         softmax_scale: Optional[float] = None, softcap: float = 0.0,
+                         alibi_slopes=None):
     """Range-masked attention with autograd.  Returns (out, lse); lse carries no gradient.
+
+    ``alibi_slopes`` (fp32 [hq] on the GPU, or None) adds ``slope[h] * (j - i)``
+    to every score after the softcap (``alibi_geometric_slopes(hq)`` gives ALiBi's
+    geometric slopes); the slopes carry no gradient.
 
     Runs through the ``ffa_amd::fwd`` / ``ffa_amd::bwd`` custom operators
     (``torch_op``), so it also works inside ``torch.compile``: pad the slice
@@ -404,7 +484,8 @@ def flex_flash_attn_func(q, k, v, q_ranges, k_ranges, attn_type_map,
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(q.shape[-1])
     return torch.ops.ffa_amd.fwd(q, k, v, as_tensor(q_ranges), as_tensor(k_ranges),
-                                 as_tensor(attn_type_map), float(softmax_scale), float(softcap))
+                                 as_tensor(attn_type_map), float(softmax_scale), float(softcap),
+                                 alibi_slopes)
 
 
 # Register the custom operators (ffa_amd::fwd, ffa_amd::bwd) on import, so

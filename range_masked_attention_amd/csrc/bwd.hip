@@ -5,6 +5,9 @@
 //   P = exp(s - lse),  dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * out),
 //   dS = P (dP - D) [* (1 - tanh^2) with softcap],  dQ = scale dS K,
 //   dK = scale dS^T Q.
+// With the optional distance bias (ALiBi: FlexAttention paper summary,
+// sections 2 and 3.1) the scores gain slope[head] * (j - i) after the
+// softcap; it only changes P, recomputed here exactly as in the forward.
 // The pages show this pass only through autograd (MagiAttention issue on
 // dummy slices: out.backward(do) gives q.grad, k.grad, v.grad) and leave the
 // varlen backward design open (CUTLASS issue #2192); this one is built for
@@ -183,6 +186,7 @@ struct BwdArgs {
   const i32x4* splits;      // key tiles split over several items
   const int32_t* counts;    // [0] items, [1] split tiles
   float* partial;           // fp32 dK^T / dV^T of the items of split tiles
+  const float* slopes;      // [hq] distance-bias slopes (biased kernels only)
   int32_t Tq, Tk, hq, hkv, grp;
   int32_t n_units;
   float scale;
@@ -232,7 +236,7 @@ constexpr int kDkvThreads = 512;
 template <int R>
 using IC = std::integral_constant<int, R>;
 
-template <int D, bool SOFTCAP>
+template <int D, bool SOFTCAP, bool BIAS>
 __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using T = ColTile<D>;
   constexpr int KS = D / 16, DB = D / 32;
@@ -296,7 +300,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // are walked last to first: key tiles of one causal sequence then all
   // start at the sequence's last q tile and move down together, so the
   // workgroups resident at the same time read the same Q/dO tiles from L2.
-  float lse_raw = 0.f, d_raw = 0.f;
+  float lse_raw = 0.f, d_raw = 0.f, bias_row = 0.f;
   // Steps go head-minor: step st is entry e_end - 1 - st / grp, head
   // g * grp + st % grp.  Counters advanced once per step stand in for the
   // divisions: (f_e, f_h) for the next step to fetch, (p_e, p_h) for the
@@ -321,6 +325,9 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         lse_raw = a.lse[r * a.hq + head];
         d_raw = a.dvec[r * a.hq + head];
       }
+      // the row's part of the bias, -slope (i - q0), moves into its lse:
+      // exp2(t + slope (j - i) - lse) = exp2(t + slope (j - q0) - (lse + slope (i - q0)))
+      if constexpr (BIAS) bias_row = const_load<float>(a.slopes, head) * 1.4426950408889634f * (float)tid;
     }
     const int64_t off = (q0 * a.hq + head) * D;
     const int64_t valid = ((int64_t)a.Tq - q0) * q_row_bytes - (int64_t)head * D * 2;
@@ -332,7 +339,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     if (tid < kDkvRows) {
       // lse in exp2 units; rows nothing sees have lse = -inf and their P
       // must be 0, not exp(+inf)
-      s_lse[slot][tid] = (lse_raw == -INFINITY) ? INFINITY : lse_raw * 1.4426950408889634f;
+      s_lse[slot][tid] = (lse_raw == -INFINITY) ? INFINITY : lse_raw * 1.4426950408889634f + bias_row;
       s_dv[slot][tid] = d_raw;
     }
   };
@@ -343,6 +350,11 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       constexpr int R = decltype(r)::value;
       if (st + 1 < n_steps) issue(qbuf(IC<R + 1>{}));
       const DevEntry ent = plan_entry(a.entries, p_e);
+      // the key's part of the bias, slope (j - q0), in exp2 units
+      float bias_key = 0.f;
+      if constexpr (BIAS)
+        bias_key = const_load<float>(a.slopes, g * a.grp + p_h) * 1.4426950408889634f *
+                   (float)(key - ent.tile * kDkvRows);
       advance(p_e, p_h);
       const char* qt = qbuf(r);
       const char* ot = obuf(r);
@@ -377,7 +389,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
           for (int i = 0; i < 4; ++i) {
             float th;
             const float t = score_to_t<SOFTCAP>(a, s[qb][4 * v4 + i], &th);
-            float p = fast_exp2(t - l4[i]);
+            float p = BIAS ? fast_exp2(t + (bias_key - l4[i])) : fast_exp2(t - l4[i]);
             if (rbase + i < lo || rbase + i >= hi) p = 0.f;
             p4[i] = p;
             px[i] = SOFTCAP ? p * (1.0f - th * th) : p;
@@ -648,7 +660,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_reduce_kernel(BwdArgs a) {
 constexpr int kDqRows = 128;  // q rows per workgroup (32 per wave)
 constexpr int kDqKeys = 64;   // keys per k tile
 
-template <int D, bool SOFTCAP>
+template <int D, bool SOFTCAP, bool BIAS>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   using T = ColTile<D>;
   constexpr int KS = D / 16, DB = D / 32;
@@ -693,6 +705,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     dval = a.dvec[(int64_t)row * a.hq + head];
   }
 
+  // distance bias in exp2 units: slope * (j - i) for key j
+  const float slope2 = BIAS ? const_load<float>(a.slopes, head) * 1.4426950408889634f : 0.f;
+
   f32x16 acc[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
@@ -732,6 +747,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
       lo -= ent.tile * kDqKeys + 4 * hh;
       hi -= ent.tile * kDqKeys + 4 * hh;
     }
+    // exp2 argument offset of the tile: slope (j0 - i) - lse, j0 = first key + 4 hh;
+    // register v adds slope * off
+    const float base = BIAS ? slope2 * (float)(ent.tile * kDqKeys + 4 * hh - row) - lse2 : 0.f;
     u32x4 dw[4];
 #pragma unroll
     for (int t4 = 0; t4 < 4; ++t4) {
@@ -743,7 +761,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         const int off = 32 * kb + 8 * (v >> 2) + (v & 3);
         float th;
         const float t = score_to_t<SOFTCAP>(a, s[kb][v], &th);
-        float p = fast_exp2(t - lse2);
+        float p = BIAS ? fast_exp2(t + __builtin_fmaf(slope2, (float)off, base)) : fast_exp2(t - lse2);
         if (off < lo || off >= hi) p = 0.f;
         float ds = p * (dp[kb][v] - dval);
         if constexpr (SOFTCAP) ds *= 1.0f - th * th;
@@ -813,7 +831,7 @@ void fill_args(const BwdLaunch& p, BwdArgs* a) {
   }
 }
 
-template <int D, bool SC>
+template <int D, bool SC, bool BIAS>
 hipError_t launch_bwd_t(const BwdLaunch& p, hipStream_t stream) {
   const BwdWorkspaceLayout L = bwd_workspace_layout(p.Tq, p.Tk, p.hq, p.hkv, p.d);
   unsigned char* ws = static_cast<unsigned char*>(p.workspace);
@@ -826,6 +844,7 @@ hipError_t launch_bwd_t(const BwdLaunch& p, hipStream_t stream) {
   a.items = reinterpret_cast<const i32x4*>(ws + L.items);
   a.splits = reinterpret_cast<const i32x4*>(ws + L.splits);
   a.partial = reinterpret_cast<float*>(ws + L.partial);
+  a.slopes = p.alibi_slopes;
   if (rows > 0)
     hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + kThreads - 1) / kThreads)),
                        dim3(kThreads), 0, stream, static_cast<const __bf16*>(p.out),
@@ -841,7 +860,7 @@ hipError_t launch_bwd_t(const BwdLaunch& p, hipStream_t stream) {
                        (int)n_kt, a.grp, a.hkv, reinterpret_cast<i32x4*>(ws + L.items), (int)L.items_cap,
                        reinterpret_cast<i32x4*>(ws + L.splits), (int)L.splits_cap,
                        reinterpret_cast<int32_t*>(ws + L.counts));
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, SC>), dim3((unsigned)(L.items_cap * p.hkv)), dim3(kDkvThreads), 0,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, SC, BIAS>), dim3((unsigned)(L.items_cap * p.hkv)), dim3(kDkvThreads), 0,
                        stream, a);
     hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<D>), dim3((unsigned)(L.splits_cap * p.hkv)), dim3(kThreads), 0,
                        stream, a);
@@ -854,7 +873,7 @@ hipError_t launch_bwd_t(const BwdLaunch& p, hipStream_t stream) {
   a.n_units = (int32_t)(n_qt * p.hkv);
   const int64_t n_wg = ((a.n_units + 7) / 8) * 8 * (int64_t)a.grp;
   if (n_wg > 0)
-    hipLaunchKernelGGL((bwd_dq_kernel<D, SC>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_kernel<D, SC, BIAS>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -889,10 +908,15 @@ BwdWorkspaceLayout bwd_workspace_layout(int64_t Tq, int64_t Tk, int hq, int hkv,
   return L;
 }
 
+template <int D>
+hipError_t launch_bwd_d(const BwdLaunch& p, hipStream_t stream) {
+  const bool sc = p.softcap > 0.f, bias = p.alibi_slopes != nullptr;
+  if (bias) return sc ? launch_bwd_t<D, true, true>(p, stream) : launch_bwd_t<D, false, true>(p, stream);
+  return sc ? launch_bwd_t<D, true, false>(p, stream) : launch_bwd_t<D, false, false>(p, stream);
+}
+
 hipError_t launch_bwd(const BwdLaunch& p, hipStream_t stream) {
-  const bool sc = p.softcap > 0.f;
-  if (p.d == 64) return sc ? launch_bwd_t<64, true>(p, stream) : launch_bwd_t<64, false>(p, stream);
-  return sc ? launch_bwd_t<128, true>(p, stream) : launch_bwd_t<128, false>(p, stream);
+  return p.d == 64 ? launch_bwd_d<64>(p, stream) : launch_bwd_d<128>(p, stream);
 }
 
 }  // namespace ffa

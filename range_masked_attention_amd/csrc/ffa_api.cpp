@@ -267,15 +267,22 @@ int plan_destroy(ffa_plan_s* p, hipStream_t stream) {
   return FFA_OK;
 }
 
+int check_slopes(const float* slopes) {
+  if (slopes && (reinterpret_cast<uintptr_t>(slopes) & 3))
+    return fail(FFA_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
+  return FFA_OK;
+}
+
 int fwd_planned(const ffa_plan_s* p, const void* q, const void* k, const void* v, int hq, int hkv,
-                int d, float scale, float softcap, void* out, float* lse, hipStream_t stream) {
+                int d, float scale, float softcap, const float* slopes, void* out, float* lse,
+                hipStream_t stream) {
   if (!(p->want & kWantFwd)) return fail(FFA_ERR_INVALID_ARG, "plan was built without the forward lists");
   int rc = check_heads(p->Tq, p->Tk, hq, hkv, d, scale, softcap);
   if (rc != FFA_OK) return rc;
   const bool has_q = p->Tq > 0, has_k = p->Tk > 0;
   if ((rc = check_ptr(q, has_q, "q")) || (rc = check_ptr(out, has_q, "out")) ||
       (rc = check_ptr(lse, has_q, "lse")) || (rc = check_ptr(k, has_k, "k")) ||
-      (rc = check_ptr(v, has_k, "v")))
+      (rc = check_ptr(v, has_k, "v")) || (rc = check_slopes(slopes)))
     return rc;
   if (p->Tq == 0) return FFA_OK;
   ffa::FwdLaunch L;
@@ -286,6 +293,7 @@ int fwd_planned(const ffa_plan_s* p, const void* q, const void* k, const void* v
   L.entries = p->dev + p->fwd.off_entries;
   L.order = reinterpret_cast<const int32_t*>(p->dev + p->fwd.off_order);
   L.slices = p->dev + p->off_slices;
+  L.alibi_slopes = slopes;
   hipError_t e = ffa::launch_fwd(L, stream);
   if (e != hipSuccess) return hip_fail(e, "forward kernel launch");
   return FFA_OK;
@@ -293,8 +301,8 @@ int fwd_planned(const ffa_plan_s* p, const void* q, const void* k, const void* v
 
 int bwd_planned(const ffa_plan_s* p, const void* q, const void* k, const void* v, const void* out,
                 const float* lse, const void* dout, int hq, int hkv, int d, float scale, float softcap,
-                void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                hipStream_t stream) {
+                const float* slopes, void* dq, void* dk, void* dv, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
   if (!(p->want & kWantBwd)) return fail(FFA_ERR_INVALID_ARG, "plan was built without the backward lists");
   int rc = check_heads(p->Tq, p->Tk, hq, hkv, d, scale, softcap);
   if (rc != FFA_OK) return rc;
@@ -303,7 +311,7 @@ int bwd_planned(const ffa_plan_s* p, const void* q, const void* k, const void* v
       (rc = check_ptr(lse, has_q, "lse")) || (rc = check_ptr(dout, has_q, "dout")) ||
       (rc = check_ptr(dq, has_q, "dq")) || (rc = check_ptr(k, has_k, "k")) ||
       (rc = check_ptr(v, has_k, "v")) || (rc = check_ptr(dk, has_k, "dk")) ||
-      (rc = check_ptr(dv, has_k, "dv")))
+      (rc = check_ptr(dv, has_k, "dv")) || (rc = check_slopes(slopes)))
     return rc;
   const size_t need = ffa_bwd_workspace_size(p->Tq, p->Tk, hq, hkv, d);
   if (workspace && workspace_bytes < need)
@@ -328,6 +336,7 @@ int bwd_planned(const ffa_plan_s* p, const void* q, const void* k, const void* v
   L.q_entries = p->dev + p->dq.off_entries;
   L.q_order = reinterpret_cast<const int32_t*>(p->dev + p->dq.off_order);
   L.slices = p->dev + p->off_slices;
+  L.alibi_slopes = slopes;
   hipError_t e = ffa::launch_bwd(L, stream);
   if (ws != workspace) (void)hipFreeAsync(ws, stream);
   if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
@@ -446,26 +455,49 @@ int ffa_plan_destroy(ffa_plan_t plan, void* stream) {
   return plan_destroy(plan, static_cast<hipStream_t>(stream));
 }
 
-int ffa_fwd_planned(ffa_plan_t plan, const void* q, const void* k, const void* v, int hq, int hkv,
-                    int d, float scale, float softcap, void* out, float* lse, void* stream) {
+int ffa_fwd_planned_ex(ffa_plan_t plan, const void* q, const void* k, const void* v, int hq, int hkv,
+                       int d, float scale, float softcap, const float* alibi_slopes, void* out,
+                       float* lse, void* stream) {
   g_err.clear();
   if (!plan) return fail(FFA_ERR_INVALID_ARG, "plan must not be NULL");
-  return fwd_planned(plan, q, k, v, hq, hkv, d, scale, softcap, out, lse, static_cast<hipStream_t>(stream));
+  return fwd_planned(plan, q, k, v, hq, hkv, d, scale, softcap, alibi_slopes, out, lse,
+                     static_cast<hipStream_t>(stream));
+}
+
+int ffa_fwd_planned(ffa_plan_t plan, const void* q, const void* k, const void* v, int hq, int hkv,
+                    int d, float scale, float softcap, void* out, float* lse, void* stream) {
+  return ffa_fwd_planned_ex(plan, q, k, v, hq, hkv, d, scale, softcap, nullptr, out, lse, stream);
+}
+
+int ffa_bwd_planned_ex(ffa_plan_t plan, const void* q, const void* k, const void* v, const void* out,
+                       const float* lse, const void* dout, int hq, int hkv, int d, float scale,
+                       float softcap, const float* alibi_slopes, void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!plan) return fail(FFA_ERR_INVALID_ARG, "plan must not be NULL");
+  return bwd_planned(plan, q, k, v, out, lse, dout, hq, hkv, d, scale, softcap, alibi_slopes, dq, dk,
+                     dv, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 int ffa_bwd_planned(ffa_plan_t plan, const void* q, const void* k, const void* v, const void* out,
                     const float* lse, const void* dout, int hq, int hkv, int d, float scale,
                     float softcap, void* dq, void* dk, void* dv, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  g_err.clear();
-  if (!plan) return fail(FFA_ERR_INVALID_ARG, "plan must not be NULL");
-  return bwd_planned(plan, q, k, v, out, lse, dout, hq, hkv, d, scale, softcap, dq, dk, dv,
-                     workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+  return ffa_bwd_planned_ex(plan, q, k, v, out, lse, dout, hq, hkv, d, scale, softcap, nullptr, dq, dk,
+                            dv, workspace, workspace_bytes, stream);
 }
 
 int ffa_fwd(const void* q, const void* k, const void* v, int64_t Tq, int64_t Tk, int hq, int hkv,
             int d, const int32_t* q_ranges, const int32_t* k_ranges, const int32_t* attn_type_map,
             int R, float scale, float softcap, void* out, float* lse, void* stream) {
+  return ffa_fwd_ex(q, k, v, Tq, Tk, hq, hkv, d, q_ranges, k_ranges, attn_type_map, R, scale, softcap,
+                    nullptr, out, lse, stream);
+}
+
+int ffa_fwd_ex(const void* q, const void* k, const void* v, int64_t Tq, int64_t Tk, int hq, int hkv,
+               int d, const int32_t* q_ranges, const int32_t* k_ranges, const int32_t* attn_type_map,
+               int R, float scale, float softcap, const float* alibi_slopes, void* out, float* lse,
+               void* stream) {
   g_err.clear();
   std::string m = check_sizes(Tq, Tk);
   if (!m.empty()) return fail(FFA_ERR_INVALID_ARG, m);
@@ -475,14 +507,14 @@ int ffa_fwd(const void* q, const void* k, const void* v, int64_t Tq, int64_t Tk,
   const bool has_q = Tq > 0, has_k = Tk > 0;
   if ((rc = check_ptr(q, has_q, "q")) || (rc = check_ptr(out, has_q, "out")) ||
       (rc = check_ptr(lse, has_q, "lse")) || (rc = check_ptr(k, has_k, "k")) ||
-      (rc = check_ptr(v, has_k, "v")))
+      (rc = check_ptr(v, has_k, "v")) || (rc = check_slopes(alibi_slopes)))
     return rc;
   if (Tq == 0) return FFA_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   ffa_plan_s* p = nullptr;
   rc = plan_create(Tq, Tk, q_ranges, k_ranges, attn_type_map, R, kWantFwd, st, &p);
   if (rc != FFA_OK) return rc;
-  rc = fwd_planned(p, q, k, v, hq, hkv, d, scale, softcap, out, lse, st);
+  rc = fwd_planned(p, q, k, v, hq, hkv, d, scale, softcap, alibi_slopes, out, lse, st);
   const std::string err = g_err;
   const int rc2 = plan_destroy(p, st);
   if (rc != FFA_OK) return fail(rc, err);
@@ -500,6 +532,15 @@ int ffa_bwd(const void* q, const void* k, const void* v, const void* out, const 
             const int32_t* q_ranges, const int32_t* k_ranges, const int32_t* attn_type_map, int R,
             float scale, float softcap, void* dq, void* dk, void* dv, void* workspace,
             size_t workspace_bytes, void* stream) {
+  return ffa_bwd_ex(q, k, v, out, lse, dout, Tq, Tk, hq, hkv, d, q_ranges, k_ranges, attn_type_map, R,
+                    scale, softcap, nullptr, dq, dk, dv, workspace, workspace_bytes, stream);
+}
+
+int ffa_bwd_ex(const void* q, const void* k, const void* v, const void* out, const float* lse,
+               const void* dout, int64_t Tq, int64_t Tk, int hq, int hkv, int d,
+               const int32_t* q_ranges, const int32_t* k_ranges, const int32_t* attn_type_map, int R,
+               float scale, float softcap, const float* alibi_slopes, void* dq, void* dk, void* dv,
+               void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   std::string m = check_sizes(Tq, Tk);
   if (!m.empty()) return fail(FFA_ERR_INVALID_ARG, m);
@@ -511,7 +552,7 @@ int ffa_bwd(const void* q, const void* k, const void* v, const void* out, const 
       (rc = check_ptr(lse, has_q, "lse")) || (rc = check_ptr(dout, has_q, "dout")) ||
       (rc = check_ptr(dq, has_q, "dq")) || (rc = check_ptr(k, has_k, "k")) ||
       (rc = check_ptr(v, has_k, "v")) || (rc = check_ptr(dk, has_k, "dk")) ||
-      (rc = check_ptr(dv, has_k, "dv")))
+      (rc = check_ptr(dv, has_k, "dv")) || (rc = check_slopes(alibi_slopes)))
     return rc;
   if (workspace && workspace_bytes < ffa_bwd_workspace_size(Tq, Tk, hq, hkv, d))
     return fail(FFA_ERR_INVALID_ARG, "workspace is smaller than ffa_bwd_workspace_size()");
@@ -520,8 +561,8 @@ int ffa_bwd(const void* q, const void* k, const void* v, const void* out, const 
   ffa_plan_s* p = nullptr;
   rc = plan_create(Tq, Tk, q_ranges, k_ranges, attn_type_map, R, kWantBwd, st, &p);
   if (rc != FFA_OK) return rc;
-  rc = bwd_planned(p, q, k, v, out, lse, dout, hq, hkv, d, scale, softcap, dq, dk, dv, workspace,
-                   workspace_bytes, st);
+  rc = bwd_planned(p, q, k, v, out, lse, dout, hq, hkv, d, scale, softcap, alibi_slopes, dq, dk, dv,
+                   workspace, workspace_bytes, st);
   const std::string err = g_err;
   const int rc2 = plan_destroy(p, st);
   if (rc != FFA_OK) return fail(rc, err);

@@ -24,6 +24,15 @@
 // -inf before the softmax (masking P in softmax, as recommended in CUTLASS
 // issue #2192 on ex77 varlen handling), and rows past the end of a tensor
 // are read as zeros through range-checked buffer loads and never stored.
+//
+// Optional distance bias (ALiBi: a bias that depends on the distance between
+// query and key positions, FlexAttention paper summary, section 2 and
+// section 3.1): score += slope[head] * (j - i) after the softcap.  Without
+// softcap the bias, in raw score units, is the initial value of the S^T
+// accumulator, so everything after the QK product is unchanged; with softcap
+// it is folded into the cap's final multiply.  j - i is formed in integers
+// (a per-lane base per tile plus a compile-time offset per register), so
+// the only rounding is that of slope * (j - i).
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -53,6 +62,8 @@ struct FwdArgs {
   float cap_in;             // softcap: 2*scale*log2(e)/softcap (tanh argument, see tanh_from_2xlog2e)
   float cap_out;            // softcap: softcap*log2(e)
   float rescale_thr;        // 8 exp2 units in the units of the running max
+  const float* slopes;      // [hq] distance-bias slopes (biased kernels only)
+  float bias_mult;          // slope to running-max units: 1/scale, or log2(e) with softcap
 };
 
 // LDS tiles are unpadded kBN x D bf16, filled by direct-to-LDS loads; 16-byte
@@ -156,15 +167,29 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const __bf16* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+// Key offset (from the tile's first key + 4 hh) of register v of block b
+// in the S^T layout: 32 b + 8 (v / 4) + v % 4.
+__device__ __forceinline__ constexpr int key_off(int b, int v) { return 32 * b + 8 * (v >> 2) + (v & 3); }
+
+// sigma * (j - i) for this lane's 32 cells of tile `ktile`: d0 = 4 hh - row.
+__device__ __forceinline__ void bias_tile(float sigma, int ktile, int d0, f32x16* s) {
+  const float base = sigma * (float)(ktile * kBN + d0);
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s[b][v] = __builtin_fmaf(sigma, (float)key_off(b, v), base);
+}
+
 // S^T = K Q^T for one 64-key tile: two 32-key blocks.  Lane (n, hh) reads
-// row 32b + n, logical chunk 2ks + hh.
-template <int D>
+// row 32b + n, logical chunk 2ks + hh.  With INIT the accumulators start
+// from s (the distance bias), else from zero.
+template <int D, bool INIT = false>
 __device__ __forceinline__ void qk_tile(const __bf16* kl, const bf16x8* qf, int n, int hh, f32x16* s) {
   using Smem = FwdSmem<D>;
   const int swz = Smem::k_swz(n);  // rows n and 32 + n share it
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
-    s[b] = f32x16{};
+    if constexpr (!INIT) s[b] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const int byte = (32 * b + n) * Smem::kRowBytes + (((2 * ks + hh) ^ swz) * 16);
@@ -174,12 +199,19 @@ __device__ __forceinline__ void qk_tile(const __bf16* kl, const bf16x8* qf, int 
   }
 }
 
-// Softcap in exp2 units: cap*log2(e) * tanh(scale * s / cap).
-__device__ __forceinline__ void softcap_tile(const FwdArgs& a, f32x16* s) {
+// Softcap in exp2 units: cap*log2(e) * tanh(scale * s / cap), plus with BIAS
+// sigma * (j - i) (sigma in exp2 units; see bias_tile).
+template <bool BIAS>
+__device__ __forceinline__ void softcap_tile(const FwdArgs& a, f32x16* s, float sigma, int ktile, int d0) {
+  const float base = BIAS ? sigma * (float)(ktile * kBN + d0) : 0.f;
 #pragma unroll
   for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) s[b][v] = a.cap_out * tanh_from_2xlog2e(s[b][v] * a.cap_in);
+    for (int v = 0; v < 16; ++v) {
+      const float th = tanh_from_2xlog2e(s[b][v] * a.cap_in);
+      s[b][v] = BIAS ? __builtin_fmaf(a.cap_out, th, __builtin_fmaf(sigma, (float)key_off(b, v), base))
+                     : a.cap_out * th;
+    }
 }
 
 // Row max over this lane's 32 scores and the other half-wave's 32.
@@ -209,7 +241,7 @@ __device__ __forceinline__ void mask_tile(const DevSlice& sl, int ktile, int row
     }
 }
 
-template <int D, bool SOFTCAP>
+template <int D, bool SOFTCAP, bool BIAS>
 __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   using Smem = FwdSmem<D>;
   constexpr int KS = D / 16;  // k steps of the QK^T contraction
@@ -246,6 +278,21 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
 
   const int e_begin = plan_i32(a.row_ptr, qt), e_end = plan_i32(a.row_ptr, qt + 1);
   const int n_tiles = e_end - e_begin;
+  // distance bias: slope of this head in running-max units, and j - i of
+  // this lane's first cell minus the tile's first key
+  const float sigma = BIAS ? const_load<float>(a.slopes, head) * a.bias_mult : 0.f;
+  const int d0 = 4 * hh - row;
+  // S^T of a tile: accumulators start from the bias (no softcap), or the
+  // bias joins the softcap
+  auto scores = [&](const __bf16* kl, int ktile, f32x16* s) {
+    if constexpr (BIAS && !SOFTCAP) {
+      bias_tile(sigma, ktile, d0, s);
+      qk_tile<D, true>(kl, qf, n, hh, s);
+    } else {
+      qk_tile<D>(kl, qf, n, hh, s);
+    }
+    if constexpr (SOFTCAP) softcap_tile<BIAS>(a, s, sigma, ktile, d0);
+  };
 
   f32x16 o[DB];
 #pragma unroll
@@ -269,8 +316,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
     if (n_tiles > 1) dma.load_k(plan_entry(a.entries, e_begin + 1).tile, kb1, w);
     dma_barrier();
     f32x16 sa[2], sb[2];
-    qk_tile<D>(kb0, qf, n, hh, sa);
-    if constexpr (SOFTCAP) softcap_tile(a, sa);
+    scores(kb0, plan_entry(a.entries, e_begin).tile, sa);
     float mx_cur = tile_max(sa);
     __syncthreads();  // K0's buffer is refilled in the first step
 
@@ -311,8 +357,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
         // last tile the K fetch reloads the last tile into a buffer nobody
         // reads again, so every step issues the same loads
         dma.load_k(plan_entry(a.entries, e_begin + min(j + 2, n_tiles - 1)).tile, kcur, w);
-        dma.load_v(plan_entry(a.entries, e + 1).tile, vnext, w);
-        qk_tile<D>(knext, qf, n, hh, s_next);
+        const int next_tile = plan_entry(a.entries, e + 1).tile;
+        dma.load_v(next_tile, vnext, w);
+        if constexpr (BIAS && !SOFTCAP) {
+          bias_tile(sigma, next_tile, d0, s_next);
+          qk_tile<D, true>(knext, qf, n, hh, s_next);
+        } else {
+          qk_tile<D>(knext, qf, n, hh, s_next);
+        }
       }
       u32x4 pw[4];
       float rs[4] = {0.f, 0.f, 0.f, 0.f};
@@ -349,7 +401,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
           o[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, pw[t]), o[db]);
         }
       if constexpr (MORE) {
-        if constexpr (SOFTCAP) softcap_tile(a, s_next);
+        if constexpr (SOFTCAP) softcap_tile<BIAS>(a, s_next, sigma, plan_entry(a.entries, e + 1).tile, d0);
         mx_cur = tile_max(s_next);
         // Instruction order for the block above: the K reads run 4 ahead of
         // the QK products, and the softmax VALU fills the shadow of each
@@ -415,7 +467,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   }
 }
 
-template <int D, bool SC>
+template <int D, bool SC, bool BIAS>
 hipError_t launch_fwd_t(const FwdLaunch& p, hipStream_t stream) {
   FwdArgs a;
   a.q = static_cast<const __bf16*>(p.q);
@@ -444,9 +496,11 @@ hipError_t launch_fwd_t(const FwdLaunch& p, hipStream_t stream) {
     a.cap_in = a.cap_out = 0.f;
   }
   a.rescale_thr = 8.0f / a.score_mult;
+  a.slopes = p.alibi_slopes;
+  a.bias_mult = SC ? log2e : 1.0f / p.scale;
   const int64_t n_wg = ((a.n_units + 7) / 8) * 8 * (int64_t)a.grp;
   if (n_wg == 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_kernel<D, SC>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<D, SC, BIAS>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -455,10 +509,15 @@ hipError_t launch_fwd_t(const FwdLaunch& p, hipStream_t stream) {
 int fwd_tile_rows() { return kBM; }
 int fwd_tile_cols() { return kBN; }
 
+template <int D>
+hipError_t launch_fwd_d(const FwdLaunch& p, hipStream_t stream) {
+  const bool sc = p.softcap > 0.f, bias = p.alibi_slopes != nullptr;
+  if (bias) return sc ? launch_fwd_t<D, true, true>(p, stream) : launch_fwd_t<D, false, true>(p, stream);
+  return sc ? launch_fwd_t<D, true, false>(p, stream) : launch_fwd_t<D, false, false>(p, stream);
+}
+
 hipError_t launch_fwd(const FwdLaunch& p, hipStream_t stream) {
-  const bool sc = p.softcap > 0.f;
-  if (p.d == 64) return sc ? launch_fwd_t<64, true>(p, stream) : launch_fwd_t<64, false>(p, stream);
-  return sc ? launch_fwd_t<128, true>(p, stream) : launch_fwd_t<128, false>(p, stream);
+  return p.d == 64 ? launch_fwd_d<64>(p, stream) : launch_fwd_d<128>(p, stream);
 }
 
 }  // namespace ffa

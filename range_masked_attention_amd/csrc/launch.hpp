@@ -28,6 +28,7 @@ struct FwdLaunch {
   const void* entries;     // device: HostDevEntry[]
   const int32_t* order;    // device: [n_qtiles]
   const void* slices;      // device: HostDevSlice[]
+  const float* alibi_slopes = nullptr;  // device: [hq], or null for no distance bias
 };
 
 struct BwdLaunch {
@@ -53,6 +54,7 @@ struct BwdLaunch {
   const void* q_entries;
   const int32_t* q_order;
   const void* slices;
+  const float* alibi_slopes = nullptr;  // device: [hq], or null for no distance bias
 };
 
 int fwd_tile_rows();

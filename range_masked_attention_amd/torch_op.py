@@ -13,11 +13,12 @@ implementations depend only on tensor shapes, so one compiled graph serves every
 slice list of the same padded length.  The real implementations call the C ABI
 through the ctypes binding (slice tensors on the GPU are copied to the host
 there: one synchronisation).  ``lse`` is returned without a gradient, as in the
-eager autograd path.
+eager autograd path.  The optional ``alibi_slopes`` (fp32 [hq] on the GPU: a
+distance bias ``slope[h] * (j - i)`` on the scores) takes no gradient either.
 """
 from __future__ import annotations
 
-from typing import Tuple
+from typing import Optional, Tuple
 
 import torch
 
@@ -30,12 +31,12 @@ NAMESPACE = "ffa_amd"
 @torch.library.custom_op(f"{NAMESPACE}::fwd", mutates_args=(), device_types="cuda")
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_ranges: torch.Tensor,
         k_ranges: torch.Tensor, attn_type_map: torch.Tensor, scale: float,
-        softcap: float) -> Tuple[torch.Tensor, torch.Tensor]:
-    return _ffa_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, scale, softcap)
+        softcap: float, alibi_slopes: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    return _ffa_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, scale, softcap, alibi_slopes=alibi_slopes)
 
 
 @fwd.register_fake
-def _fwd_fake(q, k, v, q_ranges, k_ranges, attn_type_map, scale, softcap):
+def _fwd_fake(q, k, v, q_ranges, k_ranges, attn_type_map, scale, softcap, alibi_slopes=None):
     torch._check(q.dim() == 3 and k.dim() == 3 and v.dim() == 3, lambda: "q, k, v must be [T, heads, d]")
     return torch.empty_like(q), q.new_empty((q.shape[0], q.shape[1]), dtype=torch.float32)
 
@@ -43,29 +44,31 @@ def _fwd_fake(q, k, v, q_ranges, k_ranges, attn_type_map, scale, softcap):
 @torch.library.custom_op(f"{NAMESPACE}::bwd", mutates_args=(), device_types="cuda")
 def bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
         lse: torch.Tensor, q_ranges: torch.Tensor, k_ranges: torch.Tensor,
-        attn_type_map: torch.Tensor, scale: float,
-        softcap: float) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+        attn_type_map: torch.Tensor, scale: float, softcap: float,
+        alibi_slopes: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     return _ffa_bwd(q, k, v, out, lse, dout.contiguous(), q_ranges, k_ranges, attn_type_map,
-                    scale, softcap)
+                    scale, softcap, alibi_slopes=alibi_slopes)
 
 
 @bwd.register_fake
-def _bwd_fake(dout, q, k, v, out, lse, q_ranges, k_ranges, attn_type_map, scale, softcap):
+def _bwd_fake(dout, q, k, v, out, lse, q_ranges, k_ranges, attn_type_map, scale, softcap,
+              alibi_slopes=None):
     return torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
 
 
 def _setup_context(ctx, inputs, output):
-    q, k, v, q_ranges, k_ranges, attn_type_map, scale, softcap = inputs
+    q, k, v, q_ranges, k_ranges, attn_type_map, scale, softcap, alibi_slopes = inputs
     out, lse = output
-    ctx.save_for_backward(q, k, v, out, lse, q_ranges, k_ranges, attn_type_map)
+    ctx.save_for_backward(q, k, v, out, lse, q_ranges, k_ranges, attn_type_map, alibi_slopes)
     ctx.scale, ctx.softcap = scale, softcap
     ctx.mark_non_differentiable(lse)
 
 
 def _backward(ctx, dout, dlse):
-    q, k, v, out, lse, q_ranges, k_ranges, attn_type_map = ctx.saved_tensors
-    dq, dk, dv = bwd(dout, q, k, v, out, lse, q_ranges, k_ranges, attn_type_map, ctx.scale, ctx.softcap)
-    return dq, dk, dv, None, None, None, None, None
+    q, k, v, out, lse, q_ranges, k_ranges, attn_type_map, alibi_slopes = ctx.saved_tensors
+    dq, dk, dv = bwd(dout, q, k, v, out, lse, q_ranges, k_ranges, attn_type_map, ctx.scale, ctx.softcap,
+                     alibi_slopes)
+    return dq, dk, dv, None, None, None, None, None, None
 
 
 fwd.register_autograd(_backward, setup_context=_setup_context)

@@ -125,3 +125,14 @@ def test_plan_api_validation(lib):
 def test_misaligned_pointer_rejected(lib):
     assert _fwd(lib, ptr=72) == -1
     assert "aligned" in ffa.ffa_last_error()
+
+
+def test_alibi_slopes_validation(lib):
+    """A misaligned slope pointer is rejected before any GPU work."""
+    ip = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    qr = np.array([[0, 4]], np.int32); kr = np.array([[0, 4]], np.int32); ty = np.array([1], np.int32)
+    rc = lib.ffa_fwd_ex(64, 64, 64, 4, 4, 2, 2, 64, ip(qr), ip(kr), ip(ty), 1, 0.1, 0.0, 66, 64, 64, None)
+    assert rc == -1 and "alibi_slopes" in ffa.ffa_last_error()
+    rc = lib.ffa_bwd_ex(64, 64, 64, 64, 64, 64, 4, 4, 2, 2, 64, ip(qr), ip(kr), ip(ty), 1,
+                        0.1, 0.0, 66, 64, 64, 64, None, 0, None)
+    assert rc == -1 and "alibi_slopes" in ffa.ffa_last_error()

@@ -54,3 +54,21 @@ def test_traces_as_one_opaque_op():
     gm = make_fx(f, tracing_mode="fake")(*args)
     targets = [str(n.target) for n in gm.graph.nodes if n.op == "call_function"]
     assert any("ffa_amd.fwd" in t for t in targets), targets
+
+
+def test_alibi_slopes_argument_is_optional_tensor():
+    schema = str(torch.ops.ffa_amd.fwd.default._schema)
+    assert "Tensor? alibi_slopes=None" in schema, schema
+    assert "Tensor? alibi_slopes=None" in str(torch.ops.ffa_amd.bwd.default._schema)
+    with FakeTensorMode():
+        q, k, v, qr, kr, ty = _fake_inputs()
+        slopes = torch.empty(8, dtype=torch.float32, device="cuda")
+        out, lse = torch.ops.ffa_amd.fwd(q, k, v, qr, kr, ty, 0.1, 0.0, slopes)
+        assert out.shape == q.shape and lse.shape == (100, 8)
+
+
+def test_alibi_geometric_slopes():
+    # ALiBi's slopes for 8 heads: 1/2, 1/4, ..., 1/256
+    assert ffa.alibi_geometric_slopes(8) == [2.0 ** -(h + 1) for h in range(8)]
+    s = ffa.alibi_geometric_slopes(32)
+    assert len(s) == 32 and all(a > b > 0 for a, b in zip(s, s[1:])) and s[-1] == 2.0 ** -8
