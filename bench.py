@@ -111,6 +111,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=4, help="workload number (1-5); 4 is the 64K-token batch")
     ap.add_argument("--no-bwd", action="store_true", help="time the forward only")
+    ap.add_argument("--alibi", action="store_true",
+                    help="add the distance bias with ALiBi's geometric slopes (a variant, not the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the oracle sample")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
@@ -142,6 +144,8 @@ def main():
     dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
     ws = torch.empty(max(ffa.ffa_bwd_workspace_size(w.Tq, w.Tk, w.hq, w.hkv, w.d), 16), dtype=torch.uint8, device=dev)
     qr, kr, ty = w.slices()
+    slopes = (torch.tensor(ffa.alibi_geometric_slopes(w.hq), dtype=torch.float32, device=dev)
+              if args.alibi else None)
     pairs = visible_pairs(w)
     fwd_flop = 4.0 * w.d * w.hq * pairs
     bwd_flop = 10.0 * w.d * w.hq * pairs
@@ -162,12 +166,12 @@ def main():
         t_plan = time.perf_counter() - t_plan
         if events:
             events[0].record(stream)
-        ffa.ffa_fwd_planned(plan, qd, kd, vd, w.scale, w.softcap, out=out, lse=lse)
+        ffa.ffa_fwd_planned(plan, qd, kd, vd, w.scale, w.softcap, out=out, lse=lse, alibi_slopes=slopes)
         if events:
             events[1].record(stream)
         if do_bwd:
             ffa.ffa_bwd_planned(plan, qd, kd, vd, out, lse, od, w.scale, w.softcap,
-                                dq=dq, dk=dk, dv=dv, workspace=ws)
+                                dq=dq, dk=dk, dv=dv, workspace=ws, alibi_slopes=slopes)
             if events:
                 events[2].record(stream)
         ffa.ffa_plan_destroy(plan)
@@ -225,7 +229,8 @@ def main():
         "data": "synthetic (seeded N(0,1) bf16 q/k/v/dO drawn on the CPU)",
         "config": {
             "workload": f"{w.name}: {w.Tq} tokens, {len(w.slices(padded=False)[0])} slices, "
-                        f"hq={w.hq} hkv={w.hkv} d={w.d} softcap={w.softcap}",
+                        f"hq={w.hq} hkv={w.hkv} d={w.d} softcap={w.softcap}"
+                        + (", ALiBi slopes" if args.alibi else ""),
             "tokens": w.Tq, "hq": w.hq, "hkv": w.hkv, "head_dim": w.d,
             "visible_pairs": pairs, "step": "plan + fwd" + (" + bwd" if do_bwd else ""),
         },
@@ -242,7 +247,7 @@ def main():
         "bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
         "traffic": measured_traffic(algo_bytes),
-        "kernel": "fwd_kernel<128,false>" if w.d == 128 and w.softcap == 0 else "fwd_kernel",
+        "kernel": f"fwd_kernel<{w.d},{str(w.softcap > 0).lower()},{str(args.alibi).lower()}>",
         "flop_per_launch": fwd_flop, "min_hbm_bytes_per_launch": algo_bytes,
     }
     if not args.no_cpu_baseline:

@@ -282,6 +282,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   // this lane's first cell minus the tile's first key
   const float sigma = BIAS ? const_load<float>(a.slopes, head) * a.bias_mult : 0.f;
   const int d0 = 4 * hh - row;
+  // tile j of the walk.  With a positive slope the bias grows with the key,
+  // so the list is walked from its last key tile down: the first tiles then
+  // set the running max and later ones rarely move it (walked upwards, every
+  // tile would raise the max by slope * 64 and force a rescale of O)
+  const bool down = BIAS && sigma > 0.f;
+  auto entry = [&](int j) { return plan_entry(a.entries, down ? e_end - 1 - j : e_begin + j); };
   // S^T of a tile: accumulators start from the bias (no softcap), or the
   // bias joins the softcap
   auto scores = [&](const __bf16* kl, int ktile, f32x16* s) {
@@ -311,12 +317,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
     TileDma<D> dma;
     dma.init(a, g, lane);
     // ---- prologue: K0, V0 and K1 in LDS; S0 and its row max
-    dma.load_k(plan_entry(a.entries, e_begin).tile, kb0, w);
-    dma.load_v(plan_entry(a.entries, e_begin).tile, vb0, w);
-    if (n_tiles > 1) dma.load_k(plan_entry(a.entries, e_begin + 1).tile, kb1, w);
+    dma.load_k(entry(0).tile, kb0, w);
+    dma.load_v(entry(0).tile, vb0, w);
+    if (n_tiles > 1) dma.load_k(entry(1).tile, kb1, w);
     dma_barrier();
     f32x16 sa[2], sb[2];
-    scores(kb0, plan_entry(a.entries, e_begin).tile, sa);
+    scores(kb0, entry(0).tile, sa);
     float mx_cur = tile_max(sa);
     __syncthreads();  // K0's buffer is refilled in the first step
 
@@ -326,9 +332,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
     auto step = [&](int j, f32x16* s_cur, f32x16* s_next, __bf16* kcur, const __bf16* knext,
                     const __bf16* vcur, __bf16* vnext, auto more_tag) {
       constexpr bool MORE = decltype(more_tag)::value;
-      const int e = e_begin + j;
       // ---- tile j: mask (PARTIAL only) and the running max
-      const DevEntry ent = plan_entry(a.entries, e);
+      const DevEntry ent = entry(j);
       if (ent.meta & 1) {
         mask_tile(plan_slice(a.slices, ent.meta >> 1), ent.tile, row, hh, s_cur);
         mx_cur = tile_max(s_cur);
@@ -356,8 +361,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
         // among the QK products (the schedule below spreads them); past the
         // last tile the K fetch reloads the last tile into a buffer nobody
         // reads again, so every step issues the same loads
-        dma.load_k(plan_entry(a.entries, e_begin + min(j + 2, n_tiles - 1)).tile, kcur, w);
-        const int next_tile = plan_entry(a.entries, e + 1).tile;
+        dma.load_k(entry(min(j + 2, n_tiles - 1)).tile, kcur, w);
+        const int next_tile = entry(j + 1).tile;
         dma.load_v(next_tile, vnext, w);
         if constexpr (BIAS && !SOFTCAP) {
           bias_tile(sigma, next_tile, d0, s_next);
@@ -401,7 +406,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
           o[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, pw[t]), o[db]);
         }
       if constexpr (MORE) {
-        if constexpr (SOFTCAP) softcap_tile<BIAS>(a, s_next, sigma, plan_entry(a.entries, e + 1).tile, d0);
+        if constexpr (SOFTCAP) softcap_tile<BIAS>(a, s_next, sigma, entry(j + 1).tile, d0);
         mx_cur = tile_max(s_next);
         // Instruction order for the block above: the K reads run 4 ahead of
         // the QK products, and the softmax VALU fills the shadow of each
