@@ -288,6 +288,62 @@ def attention_bwd(q, k, v, dout, q_ranges, k_ranges, types, scale, softcap=0.0,
 
 
 # --------------------------------------------------------------------------
+# block lists (BlockMask-style masks)
+# --------------------------------------------------------------------------
+def block_visibility(kv_num_blocks, kv_indices, block_q: int, block_k: int, Tq: int, Tk: int):
+    """Boolean [Tq, Tk]: cell (i, j) is visible iff k block j // block_k is
+    among the first kv_num_blocks[b] entries of kv_indices[b], b = i // block_q.
+
+    FlexAttention paper summary, section 4 (block sparsity): the BlockMask
+    keeps, per query block, the number of non-masked key blocks and their
+    indices, which need not be contiguous.  Here every listed block is fully
+    visible (no per-cell mask function runs inside a block).
+    """
+    num = np.asarray(kv_num_blocks, dtype=np.int64).reshape(-1)
+    idx = np.asarray(kv_indices, dtype=np.int64).reshape(num.size, -1)
+    n_qb = -(-Tq // block_q)
+    n_kb = -(-Tk // block_k)
+    if num.size != n_qb:
+        raise ValueError("kv_num_blocks needs one count per query block")
+    vis = np.zeros((Tq, Tk), dtype=bool)
+    for b in range(n_qb):
+        if not 0 <= num[b] <= idx.shape[1]:
+            raise ValueError(f"query block {b}: count out of range")
+        listed = idx[b, :num[b]]
+        if np.any(listed < 0) or np.any(listed >= n_kb):
+            raise ValueError(f"query block {b}: key block index out of range")
+        if np.unique(listed).size != listed.size:
+            raise ValueError(f"query block {b}: key block listed twice")
+        for kb in listed:
+            vis[b * block_q:(b + 1) * block_q, kb * block_k:(kb + 1) * block_k] = True
+    return vis
+
+
+def attention_fwd_masked(q, k, v, vis, scale, softcap=0.0):
+    """Forward pass under an explicit boolean mask ``vis`` [Tq, Tk]: the same
+    scores, softcap and softmax as ``attention_fwd``, every row at once."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    Tq, hq, d = q.shape
+    grp = hq // k.shape[1]
+    out = np.zeros((Tq, hq, d))
+    lse = np.full((Tq, hq), -np.inf)
+    has = vis.any(axis=1)
+    for h in range(hq):
+        g = h // grp
+        u = scale * (q[:, h, :] @ k[:, g, :].T)
+        s = softcap * np.tanh(u / softcap) if softcap > 0 else u
+        s = np.where(vis, s, -np.inf)
+        m = np.where(has, s.max(axis=1), 0.0)
+        p = np.exp(s - m[:, None])
+        l = p.sum(axis=1)
+        out[:, h, :] = np.where(has[:, None], (p @ v[:, g, :]) / np.where(has, l, 1.0)[:, None], 0.0)
+        lse[:, h] = np.where(has, m + np.log(np.where(has, l, 1.0)), -np.inf)
+    return out, lse
+
+
+# --------------------------------------------------------------------------
 # tile lists
 # --------------------------------------------------------------------------
 def tile_set(q_ranges, k_ranges, types, Tq: int, Tk: int, BM: int, BN: int):

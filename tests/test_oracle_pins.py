@@ -516,3 +516,66 @@ def test_alibi_backward_matches_autograd(cap):
     np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-10, atol=1e-11)
     o_ref, _ = O.attention_fwd(q, k, v, qr, kr, ty, 0.5, softcap=cap, alibi_slopes=slopes)
     np.testing.assert_allclose(o_ref, out.detach().numpy(), rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------- block lists
+def test_block_visibility_brute_force():
+    rng = np.random.default_rng(50)
+    for trial in range(20):
+        Tq, Tk = int(rng.integers(1, 40)), int(rng.integers(1, 40))
+        bq, bk = int(rng.integers(1, 9)), int(rng.integers(1, 9))
+        nqb, nkb = -(-Tq // bq), -(-Tk // bk)
+        width = int(rng.integers(1, nkb + 1))
+        num = rng.integers(0, width + 1, nqb)
+        idx = np.full((nqb, width), -7)
+        for b in range(nqb):
+            idx[b, :num[b]] = rng.permutation(nkb)[:num[b]]
+        vis = O.block_visibility(num, idx, bq, bk, Tq, Tk)
+        for i in range(Tq):
+            for j in range(Tk):
+                listed = [int(x) for x in idx[i // bq, :num[i // bq]]]
+                assert vis[i, j] == ((j // bk) in listed), (trial, i, j)
+
+
+def test_block_visibility_rejects_bad_lists():
+    with pytest.raises(ValueError):
+        O.block_visibility([1, 1], [[0], [0]], 4, 4, 12, 8)      # three q blocks, two counts
+    with pytest.raises(ValueError):
+        O.block_visibility([2], [[0, 0]], 4, 4, 4, 8)            # listed twice
+    with pytest.raises(ValueError):
+        O.block_visibility([1], [[2]], 4, 4, 4, 8)               # index past the last k block
+
+
+@pytest.mark.parametrize("cap", [0.0, 2.5])
+def test_masked_attention_matches_sdpa_bool_mask(cap):
+    """Explicit-mask forward against torch SDPA with a boolean mask (rows that
+    see nothing excluded: SDPA gives NaN there, the oracle 0 and -inf)."""
+    rng = np.random.default_rng(51)
+    Tq, Tk, hq, hkv, d = 33, 45, 4, 2, 8
+    vis = rng.random((Tq, Tk)) < 0.3
+    vis[5] = False
+    q, k, v = _rand((Tq, hq, d), rng), _rand((Tk, hkv, d), rng), _rand((Tk, hkv, d), rng)
+    out, lse = O.attention_fwd_masked(q, k, v, vis, 0.4, softcap=cap)
+    assert np.all(out[5] == 0.0) and np.all(np.isneginf(lse[5]))
+    kr, vr = np.repeat(k, hq // hkv, axis=1), np.repeat(v, hq // hkv, axis=1)
+    live = vis.any(axis=1)
+    if cap == 0:
+        ref = _sdpa(q, kr, vr, 0.4, mask=torch.from_numpy(vis))
+        np.testing.assert_allclose(out[live], ref[live], rtol=1e-10, atol=1e-12)
+    u = 0.4 * np.einsum("ihc,jhc->hij", q, kr)
+    s = cap * np.tanh(u / cap) if cap else u
+    s = np.where(vis[None], s, -np.inf)
+    np.testing.assert_allclose(lse[live], logsumexp(s, axis=-1).T[live], rtol=1e-12, atol=1e-12)
+
+
+def test_masked_attention_agrees_with_slices():
+    """The slice forward and the explicit-mask forward on the slices' mask."""
+    rng = np.random.default_rng(52)
+    T, d = 70, 8
+    qr, kr, ty = W.random_slices(rng, T, T, max_slices=5)
+    q, k, v = _rand((T, 2, d), rng), _rand((T, 1, d), rng), _rand((T, 1, d), rng)
+    vis = O.visibility(O.normalise_slices(qr, kr, ty, T, T), np.arange(T), np.arange(T)) > 0
+    a = O.attention_fwd(q, k, v, qr, kr, ty, 0.3, softcap=1.5)
+    b = O.attention_fwd_masked(q, k, v, vis, 0.3, softcap=1.5)
+    np.testing.assert_allclose(a[0], b[0], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(a[1], b[1], rtol=1e-12, atol=1e-13)
