@@ -177,6 +177,34 @@ int64_t ffa_plan_host(int64_t Tq, int64_t Tk,
                       int32_t* order);
 
 /*
+ * ffa_block_slices -- slices for a BlockMask-style block list (host only).
+ *
+ * The FlexAttention paper summary (section 4, block sparsity) describes the
+ * BlockMask: per query block, the number of key blocks that are not masked
+ * and their indices, which need not be contiguous.  Here query block b
+ * (rows [b*block_q, (b+1)*block_q), clipped to Tq) sees every cell of the
+ * key blocks kv_indices[b*max_blocks .. b*max_blocks + kv_num_blocks[b])
+ * (keys [kb*block_k, (kb+1)*block_k), clipped to Tk); listed blocks are fully
+ * visible.  The result is a list of disjoint FULL slices covering exactly
+ * those cells, for ffa_fwd / ffa_bwd / ffa_plan_create: adjacent key blocks
+ * merge into one key range and a key range repeated over consecutive query
+ * blocks into one slice.  Slices are sorted by (q start, k start).
+ *
+ * kv_num_blocks  [ceil(Tq / block_q)] int32, each in [0, max_blocks]
+ * kv_indices     [ceil(Tq / block_q)][max_blocks] int32; the first
+ *                kv_num_blocks[b] of row b are distinct key block indices in
+ *                [0, ceil(Tk / block_k)), any order; the rest is ignored
+ * q_ranges, k_ranges [cap][2], attn_type_map [cap] int32 outputs (any may
+ *                be NULL); the first min(R, cap) slices are written
+ * Returns R >= 0, the number of slices (call with cap = 0 to size the
+ * outputs), or FFA_ERR_INVALID_ARG for a bad count, index or repeat.
+ */
+int64_t ffa_block_slices(int64_t Tq, int64_t Tk, int block_q, int block_k,
+                         const int32_t* kv_num_blocks, const int32_t* kv_indices,
+                         int max_blocks, int32_t* q_ranges, int32_t* k_ranges,
+                         int32_t* attn_type_map, int64_t cap);
+
+/*
  * Plans that outlive one call.  A plan depends only on Tq, Tk and the slice
  * list (not on heads, head size, scale or data), so callers whose layers
  * share one mask plan once and launch many times.

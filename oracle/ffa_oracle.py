@@ -319,6 +319,21 @@ def block_visibility(kv_num_blocks, kv_indices, block_q: int, block_k: int, Tq: 
     return vis
 
 
+def block_slices_plain(kv_num_blocks, kv_indices, block_q: int, block_k: int, Tq: int, Tk: int):
+    """The same block list as one FULL slice per listed block (no merging):
+    (q_ranges, k_ranges, types) for the slice-based functions above."""
+    num = np.asarray(kv_num_blocks, dtype=np.int64).reshape(-1)
+    idx = np.asarray(kv_indices, dtype=np.int64).reshape(num.size, -1)
+    qr, kr = [], []
+    for b in range(num.size):
+        for kb in idx[b, :num[b]]:
+            qr.append((b * block_q, min(Tq, (b + 1) * block_q)))
+            kr.append((int(kb) * block_k, min(Tk, (int(kb) + 1) * block_k)))
+    n = len(qr)
+    return (np.array(qr, dtype=np.int64).reshape(n, 2), np.array(kr, dtype=np.int64).reshape(n, 2),
+            np.zeros(n, dtype=np.int64))
+
+
 def attention_fwd_masked(q, k, v, vis, scale, softcap=0.0):
     """Forward pass under an explicit boolean mask ``vis`` [Tq, Tk]: the same
     scores, softcap and softmax as ``attention_fwd``, every row at once."""

@@ -28,7 +28,7 @@ __all__ = [
     "ffa_plan_create", "ffa_fwd_planned", "ffa_bwd_planned", "ffa_plan_destroy",
     "ffa_plan_device_workspace_size", "ffa_plan_create_device", "ffa_plan_refresh", "ffa_plan_status",
     "ffa_plan_export", "FFA_PLAN_BAD_SLICE", "FFA_PLAN_CAPACITY", "flex_flash_attn_func",
-    "alibi_geometric_slopes", "ffa_fwd_ex", "ffa_bwd_ex", "ffa_fwd_planned_ex", "ffa_bwd_planned_ex",
+    "alibi_geometric_slopes", "ffa_block_slices", "ffa_fwd_ex", "ffa_bwd_ex", "ffa_fwd_planned_ex", "ffa_bwd_planned_ex",
 ]
 
 FULL = 0
@@ -80,6 +80,8 @@ def load_library():
     lib.ffa_plan_host.argtypes = [i64, i64, ip32, ip32, ip32, i32, i32, i32, i32,
                                   ctypes.POINTER(ctypes.c_int64), ip32, i64, ip32]
     lib.ffa_plan_host.restype = ctypes.c_int64
+    lib.ffa_block_slices.argtypes = [i64, i64, i32, i32, ip32, ip32, i32, ip32, ip32, ip32, i64]
+    lib.ffa_block_slices.restype = ctypes.c_int64
     lib.ffa_plan_create.argtypes = [i64, i64, ip32, ip32, ip32, i32, vp, ctypes.POINTER(vp)]
     lib.ffa_plan_create.restype = ctypes.c_int
     lib.ffa_fwd_planned.argtypes = [vp, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp, vp]
@@ -280,6 +282,38 @@ def ffa_plan_host(Tq: int, Tk: int, q_ranges, k_ranges, attn_type_map, bm: int, 
     if n2 != n:
         raise FfaError(int(n2), ffa_last_error())
     return row_ptr, entries[:n], order[:n_tiles]
+
+
+def ffa_block_slices(kv_num_blocks, kv_indices, Tq: int, Tk: int, block_q: int = 128,
+                     block_k: int = 128):
+    """C ABI ``ffa_block_slices``: FULL slices covering a BlockMask-style block list.
+
+    ``kv_num_blocks`` [n_qblocks] and ``kv_indices`` [n_qblocks, max_blocks]
+    (host arrays or tensors, int32-convertible): query block b sees the key
+    blocks ``kv_indices[b, :kv_num_blocks[b]]``.  Returns (q_ranges [R, 2],
+    k_ranges [R, 2], attn_type_map [R]) as int32 NumPy arrays.
+    """
+    lib = load_library()
+
+    def host(x):
+        if hasattr(x, "detach"):
+            x = x.detach().cpu().numpy()
+        return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+    num = host(kv_num_blocks).reshape(-1)
+    idx = host(kv_indices)
+    idx = idx.reshape(num.shape[0], -1) if idx.size else np.zeros((num.shape[0], 0), np.int32)
+    width = idx.shape[1]
+    args = (Tq, Tk, block_q, block_k, _iptr(num), _iptr(idx), width)
+    n = lib.ffa_block_slices(*args, None, None, None, 0)
+    if n < 0:
+        raise FfaError(int(n), ffa_last_error())
+    qr = np.zeros((n, 2), np.int32)
+    kr = np.zeros((n, 2), np.int32)
+    ty = np.zeros(n, np.int32)
+    n2 = lib.ffa_block_slices(*args, _iptr(qr), _iptr(kr), _iptr(ty), n)
+    if n2 != n:
+        raise FfaError(int(n2), ffa_last_error())
+    return qr, kr, ty
 
 
 def ffa_plan_create(Tq: int, Tk: int, q_ranges, k_ranges, attn_type_map, device=None) -> int:

@@ -442,6 +442,28 @@ int64_t ffa_plan_host(int64_t Tq, int64_t Tk, const int32_t* q_ranges, const int
   return n;
 }
 
+int64_t ffa_block_slices(int64_t Tq, int64_t Tk, int block_q, int block_k, const int32_t* kv_num_blocks,
+                         const int32_t* kv_indices, int max_blocks, int32_t* q_ranges, int32_t* k_ranges,
+                         int32_t* attn_type_map, int64_t cap) {
+  g_err.clear();
+  std::string m = check_sizes(Tq, Tk);
+  if (!m.empty()) return fail(FFA_ERR_INVALID_ARG, m);
+  std::vector<ffa::RangePair> sl;
+  try {
+    m = ffa::block_slices(Tq, Tk, block_q, block_k, kv_num_blocks, kv_indices, max_blocks, &sl);
+  } catch (const std::bad_alloc&) {
+    return fail(FFA_ERR_NOMEM, "out of host memory while converting blocks");
+  }
+  if (!m.empty()) return fail(FFA_ERR_INVALID_ARG, m);
+  const int64_t n = static_cast<int64_t>(sl.size());
+  for (int64_t i = 0; i < std::min(n, cap); ++i) {
+    if (q_ranges) { q_ranges[2 * i] = sl[i].qs; q_ranges[2 * i + 1] = sl[i].qe; }
+    if (k_ranges) { k_ranges[2 * i] = sl[i].ks; k_ranges[2 * i + 1] = sl[i].ke; }
+    if (attn_type_map) attn_type_map[i] = FFA_FULL;
+  }
+  return n;
+}
+
 int ffa_plan_create(int64_t Tq, int64_t Tk, const int32_t* q_ranges, const int32_t* k_ranges,
                     const int32_t* attn_type_map, int R, void* stream, ffa_plan_t* plan) {
   g_err.clear();

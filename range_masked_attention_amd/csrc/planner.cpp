@@ -151,4 +151,54 @@ void build_plan(const std::vector<Slice>& slices, int64_t Tq, int64_t Tk, int bm
   });
 }
 
+std::string block_slices(int64_t Tq, int64_t Tk, int block_q, int block_k, const int32_t* num,
+                         const int32_t* idx, int width, std::vector<RangePair>* out) {
+  out->clear();
+  if (Tq < 0 || Tk < 0) return "Tq and Tk must be >= 0";
+  if (block_q <= 0 || block_k <= 0) return "block sizes must be positive";
+  if (width < 0) return "max_blocks must be >= 0";
+  const int64_t n_qb = (Tq + block_q - 1) / block_q, n_kb = (Tk + block_k - 1) / block_k;
+  if (n_qb > 0 && (!num || (width > 0 && !idx))) return "block arrays must not be NULL";
+  // key ranges open from an earlier query block: (ks, ke) -> first row
+  std::map<std::pair<int64_t, int64_t>, int64_t> open;
+  auto emit = [&](int64_t qs, int64_t qe, int64_t ks, int64_t ke) {
+    out->push_back(RangePair{static_cast<int32_t>(qs), static_cast<int32_t>(qe), static_cast<int32_t>(ks),
+                             static_cast<int32_t>(ke)});
+  };
+  std::vector<int64_t> kb;
+  for (int64_t b = 0; b < n_qb; ++b) {
+    const int64_t n = num[b];
+    if (n < 0 || n > width)
+      return "query block " + std::to_string(b) + ": count " + std::to_string(n) + " is not in [0, " +
+             std::to_string(width) + "]";
+    kb.assign(idx + b * width, idx + b * width + n);
+    std::sort(kb.begin(), kb.end());
+    for (size_t i = 0; i < kb.size(); ++i) {
+      if (kb[i] < 0 || kb[i] >= n_kb)
+        return "query block " + std::to_string(b) + ": key block " + std::to_string(kb[i]) +
+               " is not in [0, " + std::to_string(n_kb) + ")";
+      if (i > 0 && kb[i] == kb[i - 1])
+        return "query block " + std::to_string(b) + ": key block " + std::to_string(kb[i]) + " listed twice";
+    }
+    // this block's key ranges: runs of adjacent key blocks
+    std::map<std::pair<int64_t, int64_t>, int64_t> now;
+    for (size_t i = 0; i < kb.size();) {
+      size_t j = i + 1;
+      while (j < kb.size() && kb[j] == kb[j - 1] + 1) ++j;
+      const int64_t ks = kb[i] * block_k, ke = std::min<int64_t>(Tk, (kb[j - 1] + 1) * block_k);
+      auto it = open.find({ks, ke});
+      now[{ks, ke}] = it != open.end() ? it->second : b * block_q;
+      i = j;
+    }
+    for (const auto& o : open)
+      if (!now.count(o.first)) emit(o.second, b * block_q, o.first.first, o.first.second);
+    open.swap(now);
+  }
+  for (const auto& o : open) emit(o.second, Tq, o.first.first, o.first.second);
+  std::sort(out->begin(), out->end(), [](const RangePair& x, const RangePair& y) {
+    return std::tie(x.qs, x.ks) < std::tie(y.qs, y.ks);
+  });
+  return "";
+}
+
 }  // namespace ffa

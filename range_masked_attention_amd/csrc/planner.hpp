@@ -55,4 +55,18 @@ std::string check_disjoint(const std::vector<Slice>& s);
 void build_plan(const std::vector<Slice>& slices, int64_t Tq, int64_t Tk, int bm, int bn,
                 bool transpose, Plan* plan);
 
+// Slices that cover exactly the blocks of a BlockMask-style list: query
+// block b (rows [b*block_q, (b+1)*block_q) clipped to Tq) sees the key
+// blocks idx[b*width .. b*width + num[b]) (any order, no repeats).  Runs of
+// adjacent key blocks become one key range, and a key range that continues
+// over consecutive query blocks becomes one slice, so sliding-window and
+// local-global lists give a few slices per block row, not one per block.
+// All slices are FULL, sorted by (qs, ks) and disjoint.  Returns "" on
+// success, else a message.
+struct RangePair {
+  int32_t qs, qe, ks, ke;
+};
+std::string block_slices(int64_t Tq, int64_t Tk, int block_q, int block_k, const int32_t* num,
+                         const int32_t* idx, int width, std::vector<RangePair>* out);
+
 }  // namespace ffa

@@ -579,3 +579,15 @@ def test_masked_attention_agrees_with_slices():
     b = O.attention_fwd_masked(q, k, v, vis, 0.3, softcap=1.5)
     np.testing.assert_allclose(a[0], b[0], rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(a[1], b[1], rtol=1e-12, atol=1e-13)
+
+
+def test_block_slices_plain_cover_the_blocks():
+    rng = np.random.default_rng(53)
+    Tq, Tk, bq, bk = 37, 29, 8, 6
+    nqb, nkb = -(-Tq // bq), -(-Tk // bk)
+    num = rng.integers(0, nkb + 1, nqb)
+    idx = np.stack([rng.permutation(nkb) for _ in range(nqb)])
+    qr, kr, ty = O.block_slices_plain(num, idx, bq, bk, Tq, Tk)
+    M = O.visibility(O.normalise_slices(qr, kr, ty, Tq, Tk), np.arange(Tq), np.arange(Tk))
+    assert M.max() <= 1
+    assert np.array_equal(M > 0, O.block_visibility(num, idx, bq, bk, Tq, Tk))
