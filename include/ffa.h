@@ -216,6 +216,13 @@ typedef struct ffa_plan_s* ffa_plan_t;
  * backward (per key tile) block lists on the host and copy them to device
  * memory on `stream`.  *plan receives the handle.  Use the plan on `stream`
  * (or after synchronising with it).  Errors as for ffa_fwd.
+ *
+ * The plan also holds the forward's scratch (about 32 MiB): a q tile whose
+ * list is longer than one workgroup slot's share of the work (a short query
+ * block against a long context) is walked by several workgroups whose
+ * partial outputs are merged by their lse, in a fixed order.  Forward calls
+ * on one plan therefore must not run concurrently on different streams;
+ * backward calls keep their own workspace.
  */
 int ffa_plan_create(int64_t Tq, int64_t Tk,
                     const int32_t* q_ranges, const int32_t* k_ranges,

@@ -189,6 +189,7 @@ struct BwdArgs {
   const float* slopes;      // [hq] distance-bias slopes (biased kernels only)
   int32_t Tq, Tk, hq, hkv, grp;
   int32_t n_units;
+  int32_t direct;           // dK/dV: 1 = one item per key tile, from the plan itself
   float scale;
   float score_mult;  // scale*log2(e), or 1 with softcap
   float cap_in;      // softcap: 2*scale*log2(e)/softcap
@@ -258,12 +259,25 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     else return o_s1;
   };
 
-  // work item: a run of one key tile's entries, for kv head g
+  // work item: a run of one key tile's entries (or, with a.direct, the
+  // whole list of the key tile at that place in the plan order), kv head g
   const int u = blockIdx.x;
   const int item = u / a.hkv, g = u % a.hkv;
-  if (item >= plan_i32(a.counts, 0)) return;
-  const i32x4 it = const_load<i32x4>(a.items, item);
-  const int kt = it[0], e_begin = it[1], e_end = it[2], slot = it[3];
+  int kt, e_begin, e_end, slot;
+  if (a.direct) {
+    if (item >= a.n_units) return;
+    kt = plan_i32(a.order, item);
+    e_begin = plan_i32(a.row_ptr, kt);
+    e_end = plan_i32(a.row_ptr, kt + 1);
+    slot = -1;
+  } else {
+    if (item >= plan_i32(a.counts, 0)) return;
+    const i32x4 it = const_load<i32x4>(a.items, item);
+    kt = it[0];
+    e_begin = it[1];
+    e_end = it[2];
+    slot = it[3];
+  }
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, hh = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int pair = w & 3;
@@ -522,110 +536,13 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 // A key tile's list is one serial chain in the dK/dV kernel, so a tile that
 // many q tiles see (a global "sink" that every block attends, a long causal
 // sequence shared by few heads) would set the kernel's duration by itself.
-// bwd_split cuts every list longer than `ec` entries into runs of at most
-// ec entries, with ec chosen so that all runs over all kv heads number about
-// kBalanceItems (twice the 256 CUs): no run is then longer than half of one
-// CU's share of the work.  Runs of a split tile write fp32 partial sums and
-// bwd_dkdv_reduce adds them in run order, so the result does not depend on
-// timing.  Item and split counts are bounded on the host side:
-//   items  <= n_kt + E / ec <= n_kt + kBalanceItems / hkv
-//   splits <  E / ec        <= kBalanceItems / hkv
-// (E = entries of all key tiles); partial buffers are capped at
-// kMaxSlotHeads (runs of split tiles times kv heads) by doubling ec.
-constexpr int kSplitThreads = 1024;
-constexpr int kBalanceItems = 512;
-constexpr int kMinItemSteps = 32;   // (entry, q head) steps: never split below this
-constexpr int kMaxSlotHeads = 512;
-
-// Inclusive prefix sums of three values over the 1024 threads.
-__device__ __forceinline__ void block_scan3(int v[3], int (*s_wave)[16]) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1)
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const int y = __shfl_up(v[j], d, 64);
-      if (lane >= d) v[j] += y;
-    }
-  if (lane == 63)
-    for (int j = 0; j < 3; ++j) s_wave[j][w] = v[j];
-  __syncthreads();
-  for (int j = 0; j < 3; ++j) {
-    int off = 0;
-    for (int i = 0; i < w; ++i) off += s_wave[j][i];
-    v[j] += off;
-  }
-  __syncthreads();
-}
-
-__global__ __launch_bounds__(kSplitThreads) void bwd_split_kernel(const int32_t* __restrict__ row_ptr,
-                                                                  const int32_t* __restrict__ order,
-                                                                  int n_kt, int grp, int hkv, i32x4* items,
-                                                                  int items_cap, i32x4* splits, int splits_cap,
-                                                                  int32_t* counts) {
-  __shared__ int s_wave[3][16];
-  __shared__ int s_tot[3];
-  __shared__ long long s_slots;
-  const int tid = threadIdx.x;
-  const long long E = (long long)row_ptr[n_kt] - row_ptr[0];
-  long long ec = max((long long)((kMinItemSteps + grp - 1) / grp),
-                     (E * hkv + kBalanceItems - 1) / kBalanceItems);
-  if (ec < 1) ec = 1;
-  // runs of split tiles (one partial buffer each per kv head) for this ec
-  for (;;) {
-    if (tid == 0) s_slots = 0;
-    __syncthreads();
-    long long part = 0;
-    for (int u = tid; u < n_kt; u += kSplitThreads) {
-      const int kt = order[u];
-      const long long len = (long long)row_ptr[kt + 1] - row_ptr[kt];
-      if (len > ec) part += (len + ec - 1) / ec;
-    }
-    if (part) atomicAdd(reinterpret_cast<unsigned long long*>(&s_slots), (unsigned long long)part);
-    __syncthreads();
-    const long long slots = s_slots;
-    __syncthreads();
-    if (slots * hkv <= kMaxSlotHeads) break;
-    ec *= 2;
-  }
-
-  int base_item = 0, base_slot = 0, base_split = 0;
-  for (int u0 = 0; u0 < n_kt; u0 += kSplitThreads) {
-    const int u = u0 + tid;
-    int kt = 0, lo = 0, len = 0, ns = 0;
-    if (u < n_kt) {
-      kt = order[u];
-      lo = row_ptr[kt];
-      len = row_ptr[kt + 1] - lo;
-      ns = len > ec ? (int)((len + ec - 1) / ec) : 1;
-    }
-    const bool sp = ns > 1;
-    int v[3] = {ns, sp ? ns : 0, sp ? 1 : 0};
-    block_scan3(v, s_wave);
-    if (u < n_kt) {
-      const int item0 = base_item + v[0] - ns;
-      const int slot0 = base_slot + v[1] - (sp ? ns : 0);
-      const int ce = (len + ns - 1) / ns;
-      for (int c = 0; c < ns; ++c) {
-        const int e_lo = lo + min(len, c * ce), e_hi = lo + min(len, (c + 1) * ce);
-        if (item0 + c < items_cap) items[item0 + c] = i32x4{kt, e_lo, e_hi, sp ? slot0 + c : -1};
-      }
-      const int si = base_split + v[2] - 1;
-      if (sp && si < splits_cap) splits[si] = i32x4{kt, slot0, ns, 0};
-    }
-    if (tid == kSplitThreads - 1)
-      for (int j = 0; j < 3; ++j) s_tot[j] = v[j];
-    __syncthreads();
-    base_item += s_tot[0];
-    base_slot += s_tot[1];
-    base_split += s_tot[2];
-    __syncthreads();
-  }
-  if (tid == 0) {
-    counts[0] = min(base_item, items_cap);
-    counts[1] = min(base_split, splits_cap);
-  }
-}
+// The split pass (split.hip) cuts long lists into runs so that the runs of
+// all tiles over all kv heads number about kDkvBalance (twice the 256 CUs);
+// runs of a split tile write fp32 partial sums and bwd_dkdv_reduce adds them
+// in run order, so the result does not depend on timing.
+constexpr int kDkvBalance = 512;
+constexpr int kDkvMinSteps = 32;   // (entry, q head) steps: never split below this
+constexpr int kDkvMaxSlots = 512;  // partial buffers: runs of split tiles x kv heads
 
 // Sum of the partial dK^T / dV^T of a split tile's runs, in run order, to
 // bf16 dK (times the softmax scale) and dV.
@@ -855,17 +772,36 @@ hipError_t launch_bwd_t(const BwdLaunch& p, hipStream_t stream) {
   a.entries = reinterpret_cast<const DevEntry*>(p.kv_entries);
   a.order = p.kv_order;
   const int64_t n_kt = (p.Tk + kDkvKeys - 1) / kDkvKeys;
-  if (n_kt > 0) {
-    hipLaunchKernelGGL(bwd_split_kernel, dim3(1), dim3(kSplitThreads), 0, stream, p.kv_row_ptr, p.kv_order,
-                       (int)n_kt, a.grp, a.hkv, reinterpret_cast<i32x4*>(ws + L.items), (int)L.items_cap,
-                       reinterpret_cast<i32x4*>(ws + L.splits), (int)L.splits_cap,
-                       reinterpret_cast<int32_t*>(ws + L.counts));
+  a.direct = 0;
+  if (n_kt > 0 && !split_possible(p.kv_n_entries, p.kv_max_len, a.grp, a.hkv, kDkvMinSteps, kDkvBalance)) {
+    // no list can be cut: one workgroup per (key tile, kv head), no reduce
+    a.direct = 1;
+    a.n_units = (int32_t)n_kt;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, SC, BIAS>), dim3((unsigned)(n_kt * p.hkv)), dim3(kDkvThreads), 0,
+                       stream, a);
+  } else if (n_kt > 0) {
+    SplitLaunch sp;
+    sp.row_ptr = p.kv_row_ptr;
+    sp.order = p.kv_order;
+    sp.n_tiles = n_kt;
+    sp.steps_per_entry = a.grp;
+    sp.units = a.hkv;
+    sp.min_steps = kDkvMinSteps;
+    sp.balance = kDkvBalance;
+    sp.max_slot_units = kDkvMaxSlots;
+    sp.items = ws + L.items;
+    sp.items_cap = L.items_cap;
+    sp.splits = ws + L.splits;
+    sp.splits_cap = L.splits_cap;
+    sp.counts = reinterpret_cast<int32_t*>(ws + L.counts);
+    launch_split(sp, stream);
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, SC, BIAS>), dim3((unsigned)(L.items_cap * p.hkv)), dim3(kDkvThreads), 0,
                        stream, a);
     hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<D>), dim3((unsigned)(L.splits_cap * p.hkv)), dim3(kThreads), 0,
                        stream, a);
   }
   // dQ: one workgroup per (q tile, head)
+  a.direct = 0;
   a.row_ptr = p.q_row_ptr;
   a.entries = reinterpret_cast<const DevEntry*>(p.q_entries);
   a.order = p.q_order;
@@ -889,10 +825,10 @@ static size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 BwdWorkspaceLayout bwd_workspace_layout(int64_t Tq, int64_t Tk, int hq, int hkv, int d) {
   BwdWorkspaceLayout L{};
   const int64_t n_kt = Tk > 0 ? (Tk + kDkvKeys - 1) / kDkvKeys : 0;
-  const int64_t per_head = hkv > 0 ? kBalanceItems / hkv : 0;
-  L.items_cap = n_kt + per_head;
-  L.splits_cap = per_head > 0 ? per_head : 1;
-  const int64_t slot_heads = kMaxSlotHeads;
+  const SplitCaps caps = split_caps(n_kt, hkv > 0 ? hkv : 1, kDkvBalance);
+  L.items_cap = caps.items;
+  L.splits_cap = caps.splits;
+  const int64_t slot_heads = kDkvMaxSlots;
   size_t off = 0;
   L.dvec = off;
   off += round256((size_t)(Tq > 0 ? Tq : 0) * (size_t)(hq > 0 ? hq : 0) * sizeof(float));

@@ -82,13 +82,21 @@ int check_slices(int64_t Tq, int64_t Tk, const int32_t* qr, const int32_t* kr, c
 struct PlanPart {
   size_t off_row_ptr = 0, off_entries = 0, off_order = 0;
   int64_t n_tiles = 0;
+  // host-built lists: entry count and longest list, which let the launch
+  // skip the run split when no list can be cut (-1: built on the device)
+  int64_t n_entries = -1, max_len = -1;
 };
 
 size_t align16(size_t x) { return (x + 15) & ~size_t(15); }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 void append_part(const ffa::Plan& plan, std::vector<unsigned char>* img, PlanPart* part) {
   const size_t n_rp = plan.row_ptr.size(), n_e = plan.entries.size(), n_o = plan.order.size();
   part->n_tiles = plan.n_tiles;
+  part->n_entries = static_cast<int64_t>(plan.entries.size());
+  part->max_len = 0;
+  for (size_t i = 0; i + 1 < plan.row_ptr.size(); ++i)
+    part->max_len = std::max<int64_t>(part->max_len, plan.row_ptr[i + 1] - plan.row_ptr[i]);
   part->off_row_ptr = img->size();
   part->off_entries = part->off_row_ptr + align16(n_rp * 4);
   part->off_order = part->off_entries + align16(n_e * sizeof(ffa::HostDevEntry));
@@ -172,6 +180,7 @@ struct ffa_plan_s {
   PlanPart fwd, kv, dq;  // forward q tiles; per key tile (dK/dV); dQ q tiles
   unsigned char* dev = nullptr;
   size_t bytes = 0;
+  size_t off_fwd_scratch = 0;  // the forward's scratch (fwd_scratch_layout), after the lists
   // host-built plans: the caller's index of each slice in the device table
   std::vector<int32_t> slice_index;
   // plans built on the device: the planner's arguments (re-run by
@@ -243,6 +252,10 @@ int plan_create(int64_t Tq, int64_t Tk, const int32_t* qr, const int32_t* kr, co
     return fail(FFA_ERR_NOMEM, "out of host memory while planning");
   }
   p->bytes = img.size();
+  if (want & kWantFwd) {
+    p->off_fwd_scratch = align256(img.size());
+    p->bytes = p->off_fwd_scratch + ffa::fwd_scratch_layout(Tq).total;
+  }
   hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&p->dev), p->bytes, stream);
   if (e != hipSuccess) {
     delete p;
@@ -294,6 +307,9 @@ int fwd_planned(const ffa_plan_s* p, const void* q, const void* k, const void* v
   L.order = reinterpret_cast<const int32_t*>(p->dev + p->fwd.off_order);
   L.slices = p->dev + p->off_slices;
   L.alibi_slopes = slopes;
+  L.scratch = p->dev + p->off_fwd_scratch;
+  L.n_entries = p->fwd.n_entries;
+  L.max_len = p->fwd.max_len;
   hipError_t e = ffa::launch_fwd(L, stream);
   if (e != hipSuccess) return hip_fail(e, "forward kernel launch");
   return FFA_OK;
@@ -337,6 +353,8 @@ int bwd_planned(const ffa_plan_s* p, const void* q, const void* k, const void* v
   L.q_order = reinterpret_cast<const int32_t*>(p->dev + p->dq.off_order);
   L.slices = p->dev + p->off_slices;
   L.alibi_slopes = slopes;
+  L.kv_n_entries = p->kv.n_entries;
+  L.kv_max_len = p->kv.max_len;
   hipError_t e = ffa::launch_bwd(L, stream);
   if (ws != workspace) (void)hipFreeAsync(ws, stream);
   if (e != hipSuccess) return hip_fail(e, "backward kernel launch");
@@ -346,10 +364,9 @@ int bwd_planned(const ffa_plan_s* p, const void* q, const void* k, const void* v
 // Layout of a device-built plan inside the caller's workspace (256-byte
 // aligned pieces): slice table, slice ranks, status word, then per list
 // row_ptr, entries, order and three scratch arrays.
-size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct DeviceLayout {
-  size_t slices, rank, status, total;
+  size_t slices, rank, status, fwd_scratch, total;
   struct Part {
     int64_t n_tiles;
     size_t row_ptr, entries, order, count, key, glen;
@@ -378,6 +395,8 @@ DeviceLayout device_layout(int64_t Tq, int64_t Tk, int R, int64_t cap) {
     P.key = off;     off += align256(std::max<size_t>(n, 1) * 4);
     P.glen = off;    off += align256(std::max<size_t>(n, 1) * 4);
   }
+  L.fwd_scratch = off;
+  off += align256(ffa::fwd_scratch_layout(Tq).total);
   L.total = off;
   return L;
 }
@@ -629,6 +648,7 @@ int ffa_plan_create_device(int64_t Tq, int64_t Tk, const int32_t* q_ranges, cons
   p->off_slices = L.slices;
   p->dev = base;
   p->bytes = L.total;
+  p->off_fwd_scratch = L.fwd_scratch;
   p->on_device = true;
   PlanPart* parts[2] = {&p->fwd, &p->kv};
   ffa::PlanDeviceLaunch& D = p->dl;

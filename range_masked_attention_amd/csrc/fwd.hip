@@ -46,18 +46,38 @@ constexpr int kBM = 128;  // q rows per work item
 constexpr int kBN = 64;   // keys per k tile
 constexpr int kThreads = 256;
 
+// Long q-tile lists (a short query block against a long context, global
+// query rows) are cut into runs by the split pass (split.hip): lists longer
+// than one resident workgroup slot's share of the work (kFwdBalance = the
+// 512 slots of two workgroups per CU) are cut into runs of at most that
+// share, each of at least kFwdMinSteps key tiles; balanced lists (the
+// longest-first order already spreads them) stay whole.  Runs of a split tile write their own
+// normalised output and lse in fp32, and fwd_combine merges them by their
+// lse in run order.  The plan holds the scratch (fwd_scratch_layout), sized
+// for kFwdMaxSlots (run, q head) pairs.
+constexpr int kFwdBalance = 512;
+constexpr int kFwdMinSteps = 64;
+constexpr int kFwdMaxSlots = 512;
+constexpr int kFwdMaxD = 128;
+
 struct FwdArgs {
   const __bf16* q;
   const __bf16* k;
   const __bf16* v;
   __bf16* out;
   float* lse;
-  const int32_t* row_ptr;   // [n_qtiles + 1]
   const DevEntry* entries;  // grouped by q tile
-  const int32_t* order;     // q tiles, longest list first
   const DevSlice* slices;
+  const int32_t* row_ptr;   // [n_qtiles + 1]
+  const int32_t* order;     // q tiles, longest list first
+  int32_t direct;           // 1: one item per q tile, taken from the plan itself
+  int32_t n_units;          // direct: n_qtiles * hkv
+  const i32x4* items;       // runs of q-tile lists, in plan order (split.hip)
+  const i32x4* splits;      // q tiles cut into several runs
+  const int32_t* counts;    // [0] items, [1] split tiles
+  float* partial_o;         // [slot][hq][kBM][D] normalised output of one run
+  float* partial_lse;       // [slot][hq][kBM] its lse (natural log)
   int32_t Tq, Tk, hq, hkv, grp;
-  int32_t n_units;          // n_qtiles * hkv
   float score_mult;         // exponent multiplier: scale*log2(e), or 1 with softcap
   float cap_in;             // softcap: 2*scale*log2(e)/softcap (tanh argument, see tanh_from_2xlog2e)
   float cap_out;            // softcap: softcap*log2(e)
@@ -83,19 +103,35 @@ struct FwdSmem {
 };
 
 // Work-item decode.  Workgroups are handed to the 8 XCDs round-robin
-// (wg % 8); all q heads that share a kv head for one q tile go to the same
-// XCD on consecutive slots, so the K/V tiles they read are shared in that
-// XCD's L2.  Units (q tile, kv head) are spread over XCDs in plan order,
-// longest list first.
-__device__ __forceinline__ bool decode_item(const FwdArgs& a, int* qt, int* head, int* g) {
+// (wg % 8); all q heads that share a kv head for one run go to the same XCD
+// on consecutive slots, so the K/V tiles they read are shared in that XCD's
+// L2.  Units (run, kv head) are spread over XCDs in plan order, longest list
+// first.
+struct FwdItem {
+  int qt, head, g, e_begin, e_end, slot;
+};
+__device__ __forceinline__ bool decode_item(const FwdArgs& a, FwdItem* it) {
   const int wg = blockIdx.x;
   const int xcd = wg & 7, slot = wg >> 3;
   const int r = slot % a.grp;
   const int u = (slot / a.grp) * 8 + xcd;
-  if (u >= a.n_units) return false;
-  *qt = plan_i32(a.order, u / a.hkv);
-  *g = u % a.hkv;
-  *head = *g * a.grp + r;
+  const int item = u / a.hkv;
+  if (a.direct) {
+    if (u >= a.n_units) return false;
+    it->qt = plan_i32(a.order, item);
+    it->e_begin = plan_i32(a.row_ptr, it->qt);
+    it->e_end = plan_i32(a.row_ptr, it->qt + 1);
+    it->slot = -1;
+  } else {
+    if (item >= plan_i32(a.counts, 0)) return false;
+    const i32x4 run = const_load<i32x4>(a.items, item);
+    it->qt = run[0];
+    it->e_begin = run[1];
+    it->e_end = run[2];
+    it->slot = run[3];
+  }
+  it->g = u % a.hkv;
+  it->head = it->g * a.grp + r;
   return true;
 }
 
@@ -255,8 +291,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) __bf16 vb0[kTileElems];
   __shared__ __attribute__((aligned(1024))) __bf16 vb1[kTileElems];
 
-  int qt, head, g;
-  if (!decode_item(a, &qt, &head, &g)) return;
+  FwdItem item;
+  if (!decode_item(a, &item)) return;
+  const int qt = item.qt, head = item.head, g = item.g;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, n = lane & 31, hh = lane >> 5;
@@ -276,7 +313,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
       qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(n * q_row_bytes + (16 * ks + 8 * hh) * 2)));
   }
 
-  const int e_begin = plan_i32(a.row_ptr, qt), e_end = plan_i32(a.row_ptr, qt + 1);
+  const int e_begin = item.e_begin, e_end = item.e_end;
   const int n_tiles = e_end - e_begin;
   // distance bias: slope of this head in running-max units, and j - i of
   // this lane's first cell minus the tile's first key
@@ -454,7 +491,24 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   // ---- epilogue: normalise once in fp32, round to bf16 once
   const float l = l_part + __shfl_xor(l_part, 32);
   const float inv = l > 0.f ? 1.0f / l : 0.f;
-  if (row < a.Tq) {
+  if (item.slot >= 0) {
+    // one run of a split q tile: fp32 output and lse for fwd_combine
+    const int64_t pr = ((int64_t)item.slot * a.hq + head) * kBM + (row - q0);
+    float* po = a.partial_o + pr * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 x;
+        x[0] = o[db][4 * j + 0] * inv;
+        x[1] = o[db][4 * j + 1] * inv;
+        x[2] = o[db][4 * j + 2] * inv;
+        x[3] = o[db][4 * j + 3] * inv;
+        *reinterpret_cast<f32x4*>(po + 32 * db + 8 * j + 4 * hh) = x;
+      }
+    if (hh == 0)
+      a.partial_lse[pr] = l > 0.f ? (m_run * a.score_mult + fast_log2(l)) * 0.69314718055994531f : -INFINITY;
+  } else if (row < a.Tq) {
     __bf16* orow = a.out + ((int64_t)row * a.hq + head) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -472,6 +526,44 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   }
 }
 
+// Merge of the runs of a split q tile, per (row, head): lse = log sum_r
+// exp(lse_r), out = sum_r exp(lse_r - lse) out_r, runs taken in order.
+template <int D>
+__global__ __launch_bounds__(kThreads) void fwd_combine_kernel(FwdArgs a) {
+  const int u = blockIdx.x;
+  const int s = u / a.hq, head = u % a.hq;
+  if (s >= plan_i32(a.counts, 1)) return;
+  const i32x4 sp = const_load<i32x4>(a.splits, s);
+  const int qt = sp[0], slot0 = sp[1], ns = sp[2];
+  constexpr int kChunks = D / 4;
+  const float log2e = 1.4426950408889634f;
+  for (int i = threadIdx.x; i < kBM * kChunks; i += kThreads) {
+    const int rl = i / kChunks, c = i % kChunks;
+    const int64_t row = (int64_t)qt * kBM + rl;
+    if (row >= a.Tq) continue;
+    auto at = [&](int r) { return ((int64_t)(slot0 + r) * a.hq + head) * kBM + rl; };
+    float m = -INFINITY;
+    for (int r = 0; r < ns; ++r) m = fmaxf(m, a.partial_lse[at(r)]);
+    f32x4 acc = f32x4{};
+    float sum = 0.f;
+    if (m != -INFINITY) {
+      for (int r = 0; r < ns; ++r) {
+        const float lr = a.partial_lse[at(r)];
+        if (lr == -INFINITY) continue;
+        const float wr = fast_exp2((lr - m) * log2e);
+        sum += wr;
+        acc += wr * *reinterpret_cast<const f32x4*>(a.partial_o + at(r) * D + 4 * c);
+      }
+    }
+    const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+    u32x2 w2;
+    w2[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    w2[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    *reinterpret_cast<u32x2*>(a.out + (row * a.hq + head) * D + 4 * c) = w2;
+    if (c == 0) a.lse[row * a.hq + head] = sum > 0.f ? m + fast_log2(sum) * 0.69314718055994531f : -INFINITY;
+  }
+}
+
 template <int D, bool SC, bool BIAS>
 hipError_t launch_fwd_t(const FwdLaunch& p, hipStream_t stream) {
   FwdArgs a;
@@ -480,17 +572,26 @@ hipError_t launch_fwd_t(const FwdLaunch& p, hipStream_t stream) {
   a.v = static_cast<const __bf16*>(p.v);
   a.out = static_cast<__bf16*>(p.out);
   a.lse = p.lse;
-  a.row_ptr = p.row_ptr;
   a.entries = reinterpret_cast<const DevEntry*>(p.entries);
-  a.order = p.order;
   a.slices = reinterpret_cast<const DevSlice*>(p.slices);
+  a.row_ptr = p.row_ptr;
+  a.order = p.order;
   a.Tq = (int32_t)p.Tq;
   a.Tk = (int32_t)p.Tk;
   a.hq = p.hq;
   a.hkv = p.hkv;
   a.grp = p.hq / p.hkv;
   const int64_t n_qt = (p.Tq + kBM - 1) / kBM;
-  a.n_units = (int32_t)(n_qt * p.hkv);
+  const FwdScratchLayout S = fwd_scratch_layout(p.Tq);
+  unsigned char* ws = static_cast<unsigned char*>(p.scratch);
+  a.items = reinterpret_cast<const i32x4*>(ws + S.items);
+  a.splits = reinterpret_cast<const i32x4*>(ws + S.splits);
+  a.counts = reinterpret_cast<const int32_t*>(ws + S.counts);
+  a.partial_o = reinterpret_cast<float*>(ws + S.partial_o);
+  a.partial_lse = reinterpret_cast<float*>(ws + S.partial_lse);
+  // runs for this head count: the caps below are within the scratch's, which
+  // hold for a single head
+  const SplitCaps caps = split_caps(n_qt, p.hq, kFwdBalance);
   const float log2e = 1.4426950408889634f;
   if (SC) {
     a.score_mult = 1.0f;
@@ -503,13 +604,63 @@ hipError_t launch_fwd_t(const FwdLaunch& p, hipStream_t stream) {
   a.rescale_thr = 8.0f / a.score_mult;
   a.slopes = p.alibi_slopes;
   a.bias_mult = SC ? log2e : 1.0f / p.scale;
-  const int64_t n_wg = ((a.n_units + 7) / 8) * 8 * (int64_t)a.grp;
-  if (n_wg == 0) return hipSuccess;
+  if (n_qt == 0) return hipSuccess;
+  if (!split_possible(p.n_entries, p.max_len, 1, p.hq, kFwdMinSteps, kFwdBalance)) {
+    // no list can be cut: one work item per q tile, straight from the plan
+    a.direct = 1;
+    a.n_units = (int32_t)(n_qt * p.hkv);
+    const int64_t n_wg = ((a.n_units + 7) / 8) * 8 * (int64_t)a.grp;
+    hipLaunchKernelGGL((fwd_kernel<D, SC, BIAS>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+  }
+  a.direct = 0;
+  a.n_units = 0;
+  SplitLaunch sp;
+  sp.row_ptr = p.row_ptr;
+  sp.order = p.order;
+  sp.n_tiles = n_qt;
+  sp.steps_per_entry = 1;
+  sp.units = p.hq;
+  sp.min_steps = kFwdMinSteps;
+  sp.balance = kFwdBalance;
+  sp.max_slot_units = kFwdMaxSlots;
+  sp.items = ws + S.items;
+  sp.items_cap = caps.items;
+  sp.splits = ws + S.splits;
+  sp.splits_cap = caps.splits;
+  sp.counts = reinterpret_cast<int32_t*>(ws + S.counts);
+  launch_split(sp, stream);
+  const int64_t n_units = caps.items * p.hkv;
+  const int64_t n_wg = ((n_units + 7) / 8) * 8 * (int64_t)a.grp;
   hipLaunchKernelGGL((fwd_kernel<D, SC, BIAS>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((fwd_combine_kernel<D>), dim3((unsigned)(caps.splits * p.hq)), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
+
+static size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+FwdScratchLayout fwd_scratch_layout(int64_t Tq) {
+  FwdScratchLayout L{};
+  const int64_t n_qt = Tq > 0 ? (Tq + kBM - 1) / kBM : 0;
+  const SplitCaps caps = split_caps(n_qt, 1, kFwdBalance);  // one head: the largest caps
+  L.items_cap = caps.items;
+  L.splits_cap = caps.splits;
+  size_t off = 0;
+  L.counts = off;
+  off += 256;
+  L.items = off;
+  off += round256((size_t)L.items_cap * 16);
+  L.splits = off;
+  off += round256((size_t)L.splits_cap * 16);
+  L.partial_lse = off;
+  off += round256((size_t)kFwdMaxSlots * kBM * sizeof(float));
+  L.partial_o = off;
+  off += (size_t)kFwdMaxSlots * kBM * kFwdMaxD * sizeof(float);
+  L.total = off;
+  return L;
+}
 
 int fwd_tile_rows() { return kBM; }
 int fwd_tile_cols() { return kBN; }

@@ -29,7 +29,21 @@ struct FwdLaunch {
   const int32_t* order;    // device: [n_qtiles]
   const void* slices;      // device: HostDevSlice[]
   const float* alibi_slopes = nullptr;  // device: [hq], or null for no distance bias
+  void* scratch = nullptr;  // device: fwd_scratch_layout(Tq).total bytes (held by the plan)
+  // entries and longest list of the q-tile lists when the host knows them
+  // (host-built plans), else -1: with them the launch skips the run split
+  // when no list can be cut
+  int64_t n_entries = -1, max_len = -1;
 };
+
+// The forward's scratch (held by the plan): work items and the partial
+// results of q tiles cut into several runs.  Independent of the head count
+// and head size (sized for the largest).
+struct FwdScratchLayout {
+  size_t counts, items, splits, partial_lse, partial_o, total;
+  int64_t items_cap, splits_cap;
+};
+FwdScratchLayout fwd_scratch_layout(int64_t Tq);
 
 struct BwdLaunch {
   const void* q;
@@ -55,6 +69,7 @@ struct BwdLaunch {
   const int32_t* q_order;
   const void* slices;
   const float* alibi_slopes = nullptr;  // device: [hq], or null for no distance bias
+  int64_t kv_n_entries = -1, kv_max_len = -1;  // key-side lists, as in FwdLaunch
 };
 
 int fwd_tile_rows();
@@ -98,6 +113,29 @@ int bwd_kv_tile_cols();  // keys per dK/dV workgroup
 int bwd_q_tile_rows();   // q rows per dQ workgroup
 int bwd_q_tile_cols();   // keys per dQ step
 hipError_t launch_bwd(const BwdLaunch& p, hipStream_t stream);
+
+// Run split of plan lists (split.hip): the work items of the kernels that
+// walk one tile's list per workgroup.  See split.hip for the rule.
+struct SplitLaunch {
+  const int32_t* row_ptr;  // device: [n_tiles + 1]
+  const int32_t* order;    // device: [n_tiles]
+  int64_t n_tiles;
+  int steps_per_entry, units, min_steps, balance, max_slot_units;
+  void* items;             // device: int32x4 [items_cap]
+  int64_t items_cap;
+  void* splits;            // device: int32x4 [splits_cap]
+  int64_t splits_cap;
+  int32_t* counts;         // device: [2]
+};
+struct SplitCaps {
+  int64_t items, splits;
+};
+SplitCaps split_caps(int64_t n_tiles, int units, int balance);
+// false when lists of n_entries entries in all, none longer than max_len,
+// certainly stay whole under the split rule (n_entries < 0: unknown).
+bool split_possible(int64_t n_entries, int64_t max_len, int steps_per_entry, int units, int min_steps,
+                    int balance);
+void launch_split(const SplitLaunch& s, hipStream_t stream);
 
 // Byte offsets of the backward workspace pieces (each 256-byte aligned):
 // the row term D [Tq][hq] fp32, two counters, the dK/dV work items and the

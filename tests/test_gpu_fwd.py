@@ -187,3 +187,38 @@ def test_invalid_tensor_arguments_raise():
         ffa.ffa_fwd(q.transpose(0, 1), q, q, [[0, 16]], [[0, 16]], [0], 0.1)
     with pytest.raises(ffa.FfaError, match="q range"):
         ffa.ffa_fwd(q, q, q, [[0, 17]], [[0, 16]], [0], 0.1)
+
+
+# Long q-tile lists cut into runs (of at least 64 key tiles) whose outputs
+# are merged by their lse: a short query block against a long context (each
+# q tile's list is 512 key tiles: 8 runs per tile), and a causal slice whose
+# rows see a long prefix (141 key tiles: 3 runs), with softcap and the
+# distance bias (runs walked downwards).
+SPLIT_CASES = [
+    ("context", 256, 32768, 4, 1, 128, 0.0, False),
+    ("prefix", 300, 9000, 2, 2, 64, 20.0, True),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_split_q_tiles_full_compare(case):
+    name, Tq, Tk, hq, hkv, d, cap, bias = case
+    say(f"fwd split q tiles {case}")
+    if name == "context":
+        qr, kr, ty = [[0, Tq], [7, 7]], [[0, Tk], [0, 0]], [0, 0]
+    else:
+        qr, kr, ty = [[0, Tq]], [[0, Tk]], [1]
+    q, k, v, _ = W.make_tensors(Tq, Tk, hq, hkv, d, seed=21, with_dout=False)
+    scale = d ** -0.5
+    dv_ = dev()
+    slopes = np.array(ffa.alibi_geometric_slopes(hq)) if bias else None
+    st = torch.tensor(slopes, dtype=torch.float32, device=dv_) if bias else None
+    qd, kd, vd = q.to(dv_), k.to(dv_), v.to(dv_)
+    out, lse = ffa.ffa_fwd(qd, kd, vd, qr, kr, ty, scale, cap, alibi_slopes=st)
+    out2, lse2 = ffa.ffa_fwd(qd, kd, vd, qr, kr, ty, scale, cap, alibi_slopes=st)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    sl32 = st.double().cpu().numpy() if bias else None
+    ref_out, ref_lse = O.attention_fwd(to64(q), to64(k), to64(v), qr, kr, ty, scale, cap, alibi_slopes=sl32)
+    e_out, e_lse = compare_out_lse(out.cpu(), lse.cpu(), ref_out, ref_lse, name)
+    say(f"  out max-abs {e_out:.3e}  lse max-abs {e_lse:.3e}")
