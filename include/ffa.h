@@ -85,11 +85,14 @@ int ffa_fwd(const void* q, const void* k, const void* v,
 /*
  * ffa_bwd_workspace_size -- bytes of device workspace ffa_bwd and
  * ffa_bwd_planned need for these sizes (0 for invalid sizes or Tq == Tk == 0):
- * the fp32 row term D = rowsum(dO * out) [Tq][hq], the dK/dV work list, and
- * fp32 partial sums for key tiles whose list is cut into several runs (at
- * most 512 runs x kv heads of 128 keys x d x 2: 64 MiB at d = 128, 32 MiB at
- * d = 64, present whenever Tk > 0).  The contents need no initialisation and
- * are scratch after the call.
+ * the fp32 row term D = rowsum(dO * out) [Tq][hq], the work lists of the
+ * dK/dV and dQ passes, and fp32 partial sums for tiles whose list is cut
+ * into several runs (a list much longer than the average, e.g. a key block
+ * every query sees or a short query block against a long context): at most
+ * 512 runs x kv heads of 128 keys x d x 2 (present when Tk > 0) plus 512
+ * runs x q heads of 128 rows x d (present when Tq > 0), 96 MiB in all at
+ * d = 128.  The contents need no initialisation and are scratch after the
+ * call.
  */
 size_t ffa_bwd_workspace_size(int64_t Tq, int64_t Tk, int hq, int hkv, int d);
 

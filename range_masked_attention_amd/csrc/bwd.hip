@@ -185,7 +185,7 @@ struct BwdArgs {
   const i32x4* items;       // dK/dV work items (key tile, entries, slot)
   const i32x4* splits;      // key tiles split over several items
   const int32_t* counts;    // [0] items, [1] split tiles
-  float* partial;           // fp32 dK^T / dV^T of the items of split tiles
+  float* partial;           // fp32 dK^T / dV^T of the items of split tiles (dQ: fp32 dQ)
   const float* slopes;      // [hq] distance-bias slopes (biased kernels only)
   int32_t Tq, Tk, hq, hkv, grp;
   int32_t n_units;
@@ -576,6 +576,13 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_reduce_kernel(BwdArgs a) {
 // each access names its buffer at compile time (see the dK/dV kernel).
 constexpr int kDqRows = 128;  // q rows per workgroup (32 per wave)
 constexpr int kDqKeys = 64;   // keys per k tile
+// Long q-tile lists are cut into runs as in the forward (split.hip): lists
+// longer than one workgroup slot's share (512 slots: two per CU) become runs
+// of at least kDqMinSteps key tiles, whose fp32 dQ bwd_dq_reduce adds in run
+// order.
+constexpr int kDqBalance = 512;
+constexpr int kDqMinSteps = 64;
+constexpr int kDqMaxSlots = 512;  // partial buffers: runs of split tiles x q heads
 
 template <int D, bool SOFTCAP, bool BIAS>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
@@ -586,13 +593,29 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char v_s0[T::kBytes];
   __shared__ __attribute__((aligned(1024))) char v_s1[T::kBytes];
 
-  // work item: (q tile, head), q heads of one kv head on one XCD
+  // work item: (run of a q tile's list, head), q heads of one kv head on
+  // one XCD; with a.direct the whole list of the q tile at that place in the
+  // plan order
   const int wg = blockIdx.x;
-  const int xcd = wg & 7, slot = wg >> 3;
-  const int r = slot % a.grp;
-  const int u = (slot / a.grp) * 8 + xcd;
-  if (u >= a.n_units) return;
-  const int qt = plan_i32(a.order, u / a.hkv), g = u % a.hkv, head = g * a.grp + r;
+  const int xcd = wg & 7, wslot = wg >> 3;
+  const int r = wslot % a.grp;
+  const int u = (wslot / a.grp) * 8 + xcd;
+  const int item = u / a.hkv, g = u % a.hkv, head = g * a.grp + r;
+  int qt, e_begin, e_end, pslot;
+  if (a.direct) {
+    if (u >= a.n_units) return;
+    qt = plan_i32(a.order, item);
+    e_begin = plan_i32(a.row_ptr, qt);
+    e_end = plan_i32(a.row_ptr, qt + 1);
+    pslot = -1;
+  } else {
+    if (item >= plan_i32(a.counts, 0)) return;
+    const i32x4 it = const_load<i32x4>(a.items, item);
+    qt = it[0];
+    e_begin = it[1];
+    e_end = it[2];
+    pslot = it[3];
+  }
 
   const int tid = threadIdx.x, lane = tid & 63, n = lane & 31, hh = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -629,7 +652,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
 
-  const int e_begin = plan_i32(a.row_ptr, qt), e_end = plan_i32(a.row_ptr, qt + 1);
   const int tro = tr_lane_offset<D>(lane);
   const int lrow = T::off(n, hh);
   auto issue = [&](int e, char* kd, char* vd) {
@@ -707,7 +729,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     }
   }
 
-  if (row < a.Tq) {
+  if (pslot >= 0) {
+    // one run of a split q tile: fp32 dQ for bwd_dq_reduce
+    float* prow = a.partial + (((int64_t)pslot * a.hq + head) * kDqRows + (row - q0)) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 x;
+        x[0] = a.scale * acc[db][4 * j + 0];
+        x[1] = a.scale * acc[db][4 * j + 1];
+        x[2] = a.scale * acc[db][4 * j + 2];
+        x[3] = a.scale * acc[db][4 * j + 3];
+        *reinterpret_cast<f32x4*>(prow + 32 * db + 8 * j + 4 * hh) = x;
+      }
+  } else if (row < a.Tq) {
     __bf16* drow = a.dq + ((int64_t)row * a.hq + head) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -718,6 +754,27 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
         w2[1] = pack_bf16x2(a.scale * acc[db][4 * j + 2], a.scale * acc[db][4 * j + 3]);
         *reinterpret_cast<u32x2*>(drow + 32 * db + 8 * j + 4 * hh) = w2;
       }
+  }
+}
+
+// Sum of the fp32 dQ of a split q tile's runs, in run order, to bf16 dQ.
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_dq_reduce_kernel(BwdArgs a) {
+  const int u = blockIdx.x;
+  const int s = u / a.hq, head = u % a.hq;
+  if (s >= plan_i32(a.counts, 1)) return;
+  const i32x4 sp = const_load<i32x4>(a.splits, s);
+  const int qt = sp[0], slot0 = sp[1], ns = sp[2];
+  for (int i = 4 * threadIdx.x; i < kDqRows * D; i += 4 * kThreads) {
+    const int64_t row = (int64_t)qt * kDqRows + i / D;
+    if (row >= a.Tq) continue;
+    f32x4 sum = f32x4{};
+    for (int c = 0; c < ns; ++c)
+      sum += *reinterpret_cast<const f32x4*>(a.partial + ((int64_t)(slot0 + c) * a.hq + head) * kDqRows * D + i);
+    u32x2 w;
+    w[0] = pack_bf16x2(sum[0], sum[1]);
+    w[1] = pack_bf16x2(sum[2], sum[3]);
+    *reinterpret_cast<u32x2*>(a.dq + (row * a.hq + head) * D + i % D) = w;
   }
 }
 
@@ -800,16 +857,45 @@ hipError_t launch_bwd_t(const BwdLaunch& p, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<D>), dim3((unsigned)(L.splits_cap * p.hkv)), dim3(kThreads), 0,
                        stream, a);
   }
-  // dQ: one workgroup per (q tile, head)
-  a.direct = 0;
+  // dQ: one workgroup per (q tile or run of its list, q head), then the
+  // sums over the runs of split q tiles
   a.row_ptr = p.q_row_ptr;
   a.entries = reinterpret_cast<const DevEntry*>(p.q_entries);
   a.order = p.q_order;
+  a.counts = reinterpret_cast<const int32_t*>(ws + L.dq_counts);
+  a.items = reinterpret_cast<const i32x4*>(ws + L.dq_items);
+  a.splits = reinterpret_cast<const i32x4*>(ws + L.dq_splits);
+  a.partial = reinterpret_cast<float*>(ws + L.dq_partial);
   const int64_t n_qt = (p.Tq + kDqRows - 1) / kDqRows;
-  a.n_units = (int32_t)(n_qt * p.hkv);
-  const int64_t n_wg = ((a.n_units + 7) / 8) * 8 * (int64_t)a.grp;
-  if (n_wg > 0)
+  if (n_qt > 0 && !split_possible(p.q_n_entries, p.q_max_len, 1, p.hq, kDqMinSteps, kDqBalance)) {
+    a.direct = 1;
+    a.n_units = (int32_t)(n_qt * p.hkv);
+    const int64_t n_wg = ((a.n_units + 7) / 8) * 8 * (int64_t)a.grp;
     hipLaunchKernelGGL((bwd_dq_kernel<D, SC, BIAS>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream, a);
+  } else if (n_qt > 0) {
+    a.direct = 0;
+    const SplitCaps caps = split_caps(n_qt, p.hq, kDqBalance);
+    SplitLaunch sp;
+    sp.row_ptr = p.q_row_ptr;
+    sp.order = p.q_order;
+    sp.n_tiles = n_qt;
+    sp.steps_per_entry = 1;
+    sp.units = p.hq;
+    sp.min_steps = kDqMinSteps;
+    sp.balance = kDqBalance;
+    sp.max_slot_units = kDqMaxSlots;
+    sp.items = ws + L.dq_items;
+    sp.items_cap = caps.items;
+    sp.splits = ws + L.dq_splits;
+    sp.splits_cap = caps.splits;
+    sp.counts = reinterpret_cast<int32_t*>(ws + L.dq_counts);
+    launch_split(sp, stream);
+    const int64_t n_units = caps.items * p.hkv;
+    const int64_t n_wg = ((n_units + 7) / 8) * 8 * (int64_t)a.grp;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, SC, BIAS>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((bwd_dq_reduce_kernel<D>), dim3((unsigned)(caps.splits * p.hq)), dim3(kThreads), 0,
+                       stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -840,6 +926,19 @@ BwdWorkspaceLayout bwd_workspace_layout(int64_t Tq, int64_t Tk, int hq, int hkv,
   off += round256((size_t)L.splits_cap * 16);
   L.partial = off;
   if (n_kt > 0) off += (size_t)slot_heads * 2 * kDkvKeys * (size_t)d * sizeof(float);
+  // dQ runs: counters, items and split records for the largest caps (one
+  // head), fp32 partial dQ for kDqMaxSlots (run, q head) pairs
+  const int64_t n_qt = Tq > 0 ? (Tq + kDqRows - 1) / kDqRows : 0;
+  const SplitCaps qc = split_caps(n_qt, 1, kDqBalance);
+  off = round256(off);
+  L.dq_counts = off;
+  off += 256;
+  L.dq_items = off;
+  off += round256((size_t)qc.items * 16);
+  L.dq_splits = off;
+  off += round256((size_t)qc.splits * 16);
+  L.dq_partial = off;
+  if (n_qt > 0) off += (size_t)kDqMaxSlots * kDqRows * (size_t)d * sizeof(float);
   L.total = off;
   return L;
 }

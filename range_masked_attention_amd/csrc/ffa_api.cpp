@@ -355,6 +355,8 @@ int bwd_planned(const ffa_plan_s* p, const void* q, const void* k, const void* v
   L.alibi_slopes = slopes;
   L.kv_n_entries = p->kv.n_entries;
   L.kv_max_len = p->kv.max_len;
+  L.q_n_entries = p->dq.n_entries;
+  L.q_max_len = p->dq.max_len;
   hipError_t e = ffa::launch_bwd(L, stream);
   if (ws != workspace) (void)hipFreeAsync(ws, stream);
   if (e != hipSuccess) return hip_fail(e, "backward kernel launch");

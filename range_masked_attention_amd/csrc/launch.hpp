@@ -70,6 +70,7 @@ struct BwdLaunch {
   const void* slices;
   const float* alibi_slopes = nullptr;  // device: [hq], or null for no distance bias
   int64_t kv_n_entries = -1, kv_max_len = -1;  // key-side lists, as in FwdLaunch
+  int64_t q_n_entries = -1, q_max_len = -1;    // dQ lists, as in FwdLaunch
 };
 
 int fwd_tile_rows();
@@ -141,7 +142,8 @@ void launch_split(const SplitLaunch& s, hipStream_t stream);
 // the row term D [Tq][hq] fp32, two counters, the dK/dV work items and the
 // split-tile records (capacities in records), and the fp32 partial sums.
 struct BwdWorkspaceLayout {
-  size_t dvec, counts, items, splits, partial, total;
+  size_t dvec, counts, items, splits, partial;
+  size_t dq_counts, dq_items, dq_splits, dq_partial, total;
   int64_t items_cap, splits_cap;
 };
 BwdWorkspaceLayout bwd_workspace_layout(int64_t Tq, int64_t Tk, int hq, int hkv, int d);

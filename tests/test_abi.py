@@ -99,11 +99,13 @@ def test_bwd_validation(lib):
     rc = lib.ffa_bwd(64, 64, 64, 64, 64, 64, 4, 8, 2, 2, 64, ip(qr), ip(kr), ip(ty), 1,
                      0.1, 0.0, 64, 64, 64, None, 0, None)
     assert rc == -1 and "k range" in ffa.ffa_last_error()
-    # workspace: D [Tq][hq] fp32 first; with keys, fp32 partial sums of at most
-    # 512 (run, kv head) pairs of 128 keys x d x {dK, dV}
-    assert lib.ffa_bwd_workspace_size(100, 0, 8, 2, 64) >= 100 * 8 * 4
-    assert lib.ffa_bwd_workspace_size(100, 0, 8, 2, 64) < 100 * 8 * 4 + 64 * 1024
-    assert lib.ffa_bwd_workspace_size(100, 256, 8, 2, 128) >= 100 * 8 * 4 + 512 * 2 * 128 * 128 * 4
+    # workspace: D [Tq][hq] fp32; with keys, fp32 partial dK/dV of at most 512
+    # (run, kv head) pairs of 128 keys x d x 2; with rows, fp32 partial dQ of
+    # at most 512 (run, q head) pairs of 128 rows x d
+    dkv, dq = 512 * 2 * 128 * 4, 512 * 128 * 4  # per unit of d
+    assert 100 * 8 * 4 + dq * 64 <= lib.ffa_bwd_workspace_size(100, 0, 8, 2, 64) < 100 * 8 * 4 + dq * 64 + (1 << 20)
+    assert dkv * 64 <= lib.ffa_bwd_workspace_size(0, 256, 8, 2, 64) < dkv * 64 + (1 << 20)
+    assert lib.ffa_bwd_workspace_size(100, 256, 8, 2, 128) >= 100 * 8 * 4 + (dkv + dq) * 128
     assert lib.ffa_bwd_workspace_size(100, 256, 8, 2, 64) < lib.ffa_bwd_workspace_size(100, 256, 8, 2, 128)
     assert lib.ffa_bwd_workspace_size(0, 0, 8, 2, 64) == 0
     assert lib.ffa_bwd_workspace_size(100, 256, 8, 2, 96) == 0

@@ -90,8 +90,8 @@ def _sink_slices(T, blk, sink, window):
     return (np.array(qr, np.int32), np.array(kr, np.int32), np.array(ty, np.int32))
 
 
-# Key tiles whose lists are cut into several runs (dK/dV partial sums added by
-# a separate pass).  "sink": the 128-key sink tile is seen by all 64 q tiles
+# Tiles whose lists are cut into several runs (partial sums added by a
+# separate pass).  "sink": the 128-key sink tile is seen by all 64 q tiles
 # and is cut into 8 runs, most window tiles into 2.  "cap": 40 key tiles x 8 kv
 # heads, each seen by 64 q tiles: runs of 40 entries would need 640 partial
 # buffers, over the 512 the workspace holds, so the run length doubles and no
@@ -100,6 +100,9 @@ SPLIT_CASES = [
     ("sink", 4096, 4096, 4, 1, 64, 0.0),
     ("sink", 4096, 4096, 8, 2, 128, 30.0),
     ("cap", 4096, 5120, 8, 8, 64, 0.0),
+    # a short query block against a long context: each q tile's dQ list is
+    # 256 key tiles, cut into 4 runs whose fp32 dQ are added in run order
+    ("context", 256, 16384, 4, 1, 128, 0.0),
 ]
 
 
@@ -109,6 +112,8 @@ def test_split_key_tiles_full_compare(case):
     say(f"bwd split key tiles {case}")
     if kind == "sink":
         qr, kr, ty = _sink_slices(Tq, 512, 128, 1024)
+    elif kind == "context":
+        qr, kr, ty = (np.array([[0, Tq]], np.int32), np.array([[0, Tk]], np.int32), np.array([O.FULL], np.int32))
     else:
         qr, kr, ty = (np.array([[0, Tq]], np.int32), np.array([[0, Tk]], np.int32), np.array([O.FULL], np.int32))
     q, k, v, do = W.make_tensors(Tq, Tk, hq, hkv, dd, seed=11)
