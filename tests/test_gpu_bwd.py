@@ -103,6 +103,7 @@ SPLIT_CASES = [
     # a short query block against a long context: each q tile's dQ list is
     # 256 key tiles, cut into 4 runs whose fp32 dQ are added in run order
     ("context", 256, 16384, 4, 1, 128, 0.0),
+    ("context", 200, 12000, 2, 2, 64, 15.0),
 ]
 
 
