@@ -85,7 +85,7 @@ int ffa_fwd(const void* q, const void* k, const void* v,
 /*
  * ffa_bwd_workspace_size -- bytes of device workspace ffa_bwd and
  * ffa_bwd_planned need for these sizes (0 for invalid sizes or Tq == Tk == 0):
- * the fp32 row term D = rowsum(dO * out) [Tq][hq], the work lists of the
+ * the fp32 row term D = rowsum(dO * out) and a copy of lse, [hq][Tq] each, the work lists of the
  * dK/dV and dQ passes, and fp32 partial sums for tiles whose list is cut
  * into several runs (a list much longer than the average, e.g. a key block
  * every query sees or a short query block against a long context): at most

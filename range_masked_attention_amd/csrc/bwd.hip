@@ -13,7 +13,8 @@
 // varlen backward design open (CUTLASS issue #2192); this one is built for
 // the slice plan:
 //
-//  bwd_pre   D for every (row, q head).
+//  bwd_pre   D for every (row, q head), and lse in exp2 units, both stored
+//            head-major ([hq][Tq]) so that a step's 64 rows are contiguous.
 //  bwd_dkdv  one workgroup per (128-key tile, kv head); its 4 waves own 32
 //            keys each and walk the key-side plan (64-row q tiles) for every
 //            q head of the group, accumulating dK^T and dV^T in registers.
@@ -42,12 +43,20 @@ namespace {
 constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------- bwd_pre
+// Thread t takes head t / Tq, row t % Tq: the head-major writes coalesce
+// and each thread reads its own 2D-byte rows of out and dO.  lse2 is lse in
+// exp2 units with -inf (a row that sees nothing) turned into +inf, so that
+// exp2(s - lse2) is 0 there rather than NaN.
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const __bf16* __restrict__ out,
                                                           const __bf16* __restrict__ dout,
-                                                          float* __restrict__ dvec, int64_t n_rows) {
-  const int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (r >= n_rows) return;
+                                                          const float* __restrict__ lse,
+                                                          float* __restrict__ dvec, float* __restrict__ lse2,
+                                                          int64_t Tq, int hq) {
+  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (t >= Tq * hq) return;
+  const int64_t head = t / Tq, row = t - head * Tq;
+  const int64_t r = row * hq + head;
   const u32x4* po = reinterpret_cast<const u32x4*>(out + r * D);
   const u32x4* pd = reinterpret_cast<const u32x4*>(dout + r * D);
   float acc = 0.f;
@@ -60,7 +69,9 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const __bf16* __restr
       acc += __uint_as_float(a[j] & 0xFFFF0000u) * __uint_as_float(b[j] & 0xFFFF0000u);
     }
   }
-  dvec[r] = acc;
+  dvec[t] = acc;
+  const float l = lse[r];
+  lse2[t] = (l == -INFINITY) ? INFINITY : l * 1.4426950408889634f;
 }
 
 // ---------------------------------------------------------------- tiles
@@ -174,7 +185,8 @@ struct BwdArgs {
   const __bf16* v;
   const __bf16* dout;
   const float* lse;
-  const float* dvec;
+  const float* dvec;        // D, head-major [hq][Tq]
+  const float* lse2;        // lse in exp2 units (+inf: nothing visible), head-major
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
@@ -336,8 +348,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       lse_raw = INFINITY;
       d_raw = 0.f;
       if (r < a.Tq) {
-        lse_raw = a.lse[r * a.hq + head];
-        d_raw = a.dvec[r * a.hq + head];
+        lse_raw = a.lse2[(int64_t)head * a.Tq + r];
+        d_raw = a.dvec[(int64_t)head * a.Tq + r];
       }
       // the row's part of the bias, -slope (i - q0), moves into its lse:
       // exp2(t + slope (j - i) - lse) = exp2(t + slope (j - q0) - (lse + slope (i - q0)))
@@ -351,9 +363,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   // the 3- and 2-deep buffers is fixed by its position R in the turn
   auto publish = [&](int slot) {
     if (tid < kDkvRows) {
-      // lse in exp2 units; rows nothing sees have lse = -inf and their P
-      // must be 0, not exp(+inf)
-      s_lse[slot][tid] = (lse_raw == -INFINITY) ? INFINITY : lse_raw * 1.4426950408889634f + bias_row;
+      // lse in exp2 units (+inf for rows nothing sees, so their P is 0)
+      s_lse[slot][tid] = lse_raw + bias_row;
       s_dv[slot][tid] = d_raw;
     }
   };
@@ -640,9 +651,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   }
   float lse2 = INFINITY, dval = 0.f;
   if (row < a.Tq) {
-    const float l = a.lse[(int64_t)row * a.hq + head];
-    lse2 = (l == -INFINITY) ? INFINITY : l * 1.4426950408889634f;
-    dval = a.dvec[(int64_t)row * a.hq + head];
+    lse2 = a.lse2[(int64_t)head * a.Tq + row];
+    dval = a.dvec[(int64_t)head * a.Tq + row];
   }
 
   // distance bias in exp2 units: slope * (j - i) for key j
@@ -813,7 +823,9 @@ hipError_t launch_bwd_t(const BwdLaunch& p, hipStream_t stream) {
   BwdArgs a;
   fill_args(p, &a);
   float* dvec = reinterpret_cast<float*>(ws + L.dvec);
+  float* lse2 = reinterpret_cast<float*>(ws + L.lse2);
   a.dvec = dvec;
+  a.lse2 = lse2;
   a.counts = reinterpret_cast<const int32_t*>(ws + L.counts);
   a.items = reinterpret_cast<const i32x4*>(ws + L.items);
   a.splits = reinterpret_cast<const i32x4*>(ws + L.splits);
@@ -822,7 +834,7 @@ hipError_t launch_bwd_t(const BwdLaunch& p, hipStream_t stream) {
   if (rows > 0)
     hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + kThreads - 1) / kThreads)),
                        dim3(kThreads), 0, stream, static_cast<const __bf16*>(p.out),
-                       static_cast<const __bf16*>(p.dout), dvec, rows);
+                       static_cast<const __bf16*>(p.dout), p.lse, dvec, lse2, p.Tq, p.hq);
   // dK, dV: key tiles cut into runs, one workgroup per (run, kv head), then
   // the sums over the runs of split tiles
   a.row_ptr = p.kv_row_ptr;
@@ -917,6 +929,8 @@ BwdWorkspaceLayout bwd_workspace_layout(int64_t Tq, int64_t Tk, int hq, int hkv,
   const int64_t slot_heads = kDkvMaxSlots;
   size_t off = 0;
   L.dvec = off;
+  off += round256((size_t)(Tq > 0 ? Tq : 0) * (size_t)(hq > 0 ? hq : 0) * sizeof(float));
+  L.lse2 = off;
   off += round256((size_t)(Tq > 0 ? Tq : 0) * (size_t)(hq > 0 ? hq : 0) * sizeof(float));
   L.counts = off;
   off += 256;

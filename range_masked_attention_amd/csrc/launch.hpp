@@ -139,10 +139,10 @@ bool split_possible(int64_t n_entries, int64_t max_len, int steps_per_entry, int
 void launch_split(const SplitLaunch& s, hipStream_t stream);
 
 // Byte offsets of the backward workspace pieces (each 256-byte aligned):
-// the row term D [Tq][hq] fp32, two counters, the dK/dV work items and the
+// the row term D and lse in exp2 units, both [hq][Tq] fp32, two counters, the dK/dV work items and the
 // split-tile records (capacities in records), and the fp32 partial sums.
 struct BwdWorkspaceLayout {
-  size_t dvec, counts, items, splits, partial;
+  size_t dvec, lse2, counts, items, splits, partial;
   size_t dq_counts, dq_items, dq_splits, dq_partial, total;
   int64_t items_cap, splits_cap;
 };
