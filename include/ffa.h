@@ -290,8 +290,10 @@ int ffa_plan_destroy(ffa_plan_t plan, void* stream);
  *            exact count for a slice list.  A build that needs more leaves
  *            the plan empty and sets FFA_PLAN_CAPACITY in its status.
  * workspace  device memory of at least ffa_plan_device_workspace_size()
- *            bytes, 256-byte aligned, owned by the caller, holding the plan;
- *            it must outlive the plan and not be shared with another plan.
+ *            bytes, 256-byte aligned, owned by the caller, holding the plan
+ *            and the forward's scratch (about 32 MiB, as for ffa_plan_create:
+ *            forward calls on one plan must not overlap across streams); it
+ *            must outlive the plan and not be shared with another plan.
  * Validation of Tq, Tk, R, max_entries and the pointers is synchronous (the
  * usual FFA_ERR_* codes).  The slice values are only seen by the kernels: a
  * slice with start > end, a range outside [0, T) or a type other than 0/1
