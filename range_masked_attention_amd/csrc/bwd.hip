@@ -15,14 +15,17 @@
 //
 //  bwd_pre   D for every (row, q head), and lse in exp2 units, both stored
 //            head-major ([hq][Tq]) so that a step's 64 rows are contiguous.
-//  bwd_dkdv  one workgroup per (128-key tile, kv head); its 4 waves own 32
-//            keys each and walk the key-side plan (64-row q tiles) for every
-//            q head of the group, accumulating dK^T and dV^T in registers.
+//  bwd_dkdv  one workgroup per (128-key tile, kv head); its 4 wave pairs own
+//            32 keys each and walk the key-side plan (64-row q tiles) for
+//            every q head of the group, accumulating dK^T and dV^T in
+//            registers.
 //  bwd_dq    one workgroup per (128-row q tile, q head), walking the per-q-
 //            tile list of 64-key tiles and accumulating dQ^T.
-// dQ is recomputed in its own pass instead of being scattered with atomics:
-// no fp32 accumulator buffer, no contention, and the result does not depend
-// on the order in which workgroups finish.
+// A list much longer than the average is cut into runs (split.hip), one
+// workgroup each; runs write fp32 partial sums that bwd_dkdv_reduce and
+// bwd_dq_reduce add in run order.  dQ is recomputed in its own pass instead
+// of being scattered with atomics: no contention, and the result does not
+// depend on the order in which workgroups finish.
 //
 // Tiles of 64 rows are fetched straight into LDS (buffer_load ... lds), one
 // load instruction per 16-byte chunk column: LDS holds a tile column-major by

@@ -4,7 +4,9 @@
 // lanes, each wave owning 32 query rows.  The workgroup walks the plan's list
 // of 64-key tiles for its q tile (the BlockMask-style list of non-masked
 // blocks: FlexAttention paper summary, section 4, block sparsity), merging
-// every slice that reaches the q tile into one online softmax.
+// every slice that reaches the q tile into one online softmax.  A list much
+// longer than the average is cut into runs (split.hip), each walked by its
+// own workgroup, and fwd_combine merges the runs' outputs by their lse.
 //
 // Per k tile, on the matrix cores (bf16 in, fp32 accumulate):
 //   S^T = K * Q^T     keys x queries, so each lane holds one query's scores
