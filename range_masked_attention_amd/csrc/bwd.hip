@@ -397,35 +397,45 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         for (int ks = 0; ks < KS; ++ks) s[qb] = mfma_32x32x16(T::row8(qt, lrow, 32 * qb, 2 * ks), frag[ks], s[qb]);
       }
       // P; element (qb, v) is row 32qb + 8(v/4) + 4hh + v%4, key `key`
-      int lo = 0, hi = kDkvRows;
-      if (ent.meta & 1) {
-        const DevSlice sl = plan_slice(a.slices, ent.meta >> 1);
-        key_rows(sl, key, &lo, &hi);
-        lo -= ent.tile * kDkvRows;
-        hi -= ent.tile * kDkvRows;
-      }
+      // the per-cell mask only on PARTIAL entries (a FULL entry has every
+      // cell visible, tails included), chosen once per step
       u32x4 pw[4];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int v4 = 0; v4 < 4; ++v4) {
-          const int rbase = 32 * qb + 8 * v4 + 4 * hh;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&s_lse[st % 3][rbase]);
-          f32x4 px;
-          float p4[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float th;
-            const float t = score_to_t<SOFTCAP>(a, s[qb][4 * v4 + i], &th);
-            float p = BIAS ? fast_exp2(t + (bias_key - l4[i])) : fast_exp2(t - l4[i]);
-            if (rbase + i < lo || rbase + i >= hi) p = 0.f;
-            p4[i] = p;
-            px[i] = SOFTCAP ? p * (1.0f - th * th) : p;
-          }
-          *reinterpret_cast<f32x4*>(xch + ((qb * 4 + v4) * 64 + lane) * 4) = px;
-          pw[2 * qb + (v4 >> 1)][2 * (v4 & 1)] = pack_bf16x2(p4[0], p4[1]);
-          pw[2 * qb + (v4 >> 1)][2 * (v4 & 1) + 1] = pack_bf16x2(p4[2], p4[3]);
+      auto p_tile = [&](auto partial) {
+        constexpr bool PARTIAL = decltype(partial)::value;
+        int lo = 0, hi = kDkvRows;
+        if constexpr (PARTIAL) {
+          const DevSlice sl = plan_slice(a.slices, ent.meta >> 1);
+          key_rows(sl, key, &lo, &hi);
+          lo -= ent.tile * kDkvRows;
+          hi -= ent.tile * kDkvRows;
         }
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int v4 = 0; v4 < 4; ++v4) {
+            const int rbase = 32 * qb + 8 * v4 + 4 * hh;
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(&s_lse[st % 3][rbase]);
+            f32x4 px;
+            float p4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float th;
+              const float t = score_to_t<SOFTCAP>(a, s[qb][4 * v4 + i], &th);
+              float p = BIAS ? fast_exp2(t + (bias_key - l4[i])) : fast_exp2(t - l4[i]);
+              if constexpr (PARTIAL)
+                if (rbase + i < lo || rbase + i >= hi) p = 0.f;
+              p4[i] = p;
+              px[i] = SOFTCAP ? p * (1.0f - th * th) : p;
+            }
+            *reinterpret_cast<f32x4*>(xch + ((qb * 4 + v4) * 64 + lane) * 4) = px;
+            pw[2 * qb + (v4 >> 1)][2 * (v4 & 1)] = pack_bf16x2(p4[0], p4[1]);
+            pw[2 * qb + (v4 >> 1)][2 * (v4 & 1) + 1] = pack_bf16x2(p4[2], p4[3]);
+          }
+      };
+      if (ent.meta & 1)
+        p_tile(std::true_type{});
+      else
+        p_tile(std::false_type{});
       // dV^T += dO^T P : contraction over the 64 rows
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -692,35 +702,45 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
       }
     }
 
-    int lo = 0, hi = kDqKeys;
-    if (ent.meta & 1) {
-      const DevSlice sl = plan_slice(a.slices, ent.meta >> 1);
-      row_keys(sl, row, &lo, &hi);
-      lo -= ent.tile * kDqKeys + 4 * hh;
-      hi -= ent.tile * kDqKeys + 4 * hh;
-    }
     // exp2 argument offset of the tile: slope (j0 - i) - lse, j0 = first key + 4 hh;
     // register v adds slope * off
     const float base = BIAS ? slope2 * (float)(ent.tile * kDqKeys + 4 * hh - row) - lse2 : 0.f;
+    // dS^T of the tile; the per-cell mask only on PARTIAL entries (a FULL
+    // entry has every cell visible, tails included), chosen once per tile
     u32x4 dw[4];
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      const int kb = t4 >> 1, h8 = (t4 & 1) * 8;
-      float d8[8];
-#pragma unroll
-      for (int e8 = 0; e8 < 8; ++e8) {
-        const int v = h8 + e8;
-        const int off = 32 * kb + 8 * (v >> 2) + (v & 3);
-        float th;
-        const float t = score_to_t<SOFTCAP>(a, s[kb][v], &th);
-        float p = BIAS ? fast_exp2(t + __builtin_fmaf(slope2, (float)off, base)) : fast_exp2(t - lse2);
-        if (off < lo || off >= hi) p = 0.f;
-        float ds = p * (dp[kb][v] - dval);
-        if constexpr (SOFTCAP) ds *= 1.0f - th * th;
-        d8[e8] = ds;
+    auto ds_tile = [&](auto partial) {
+      constexpr bool PARTIAL = decltype(partial)::value;
+      int lo = 0, hi = kDqKeys;
+      if constexpr (PARTIAL) {
+        const DevSlice sl = plan_slice(a.slices, ent.meta >> 1);
+        row_keys(sl, row, &lo, &hi);
+        lo -= ent.tile * kDqKeys + 4 * hh;
+        hi -= ent.tile * kDqKeys + 4 * hh;
       }
-      dw[t4] = pack8(d8);
-    }
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        const int kb = t4 >> 1, h8 = (t4 & 1) * 8;
+        float d8[8];
+#pragma unroll
+        for (int e8 = 0; e8 < 8; ++e8) {
+          const int v = h8 + e8;
+          const int off = 32 * kb + 8 * (v >> 2) + (v & 3);
+          float th;
+          const float t = score_to_t<SOFTCAP>(a, s[kb][v], &th);
+          float p = BIAS ? fast_exp2(t + __builtin_fmaf(slope2, (float)off, base)) : fast_exp2(t - lse2);
+          if constexpr (PARTIAL)
+            if (off < lo || off >= hi) p = 0.f;
+          float ds = p * (dp[kb][v] - dval);
+          if constexpr (SOFTCAP) ds *= 1.0f - th * th;
+          d8[e8] = ds;
+        }
+        dw[t4] = pack8(d8);
+      }
+    };
+    if (ent.meta & 1)
+      ds_tile(std::true_type{});
+    else
+      ds_tile(std::false_type{});
 
     // ---- dQ^T += K^T dS^T : contraction over the 64 keys
 #pragma unroll
