@@ -755,11 +755,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   if (e_begin < e_end) {
     issue(e_begin, k_s0, v_s0);
     dma_barrier();
-    for (int e = e_begin; e < e_end; e += 2) {
+    // whole pairs, then the odd last step: a loop with one exit keeps the
+    // accumulators in place (an exit between the two steps made the
+    // compiler copy them every turn)
+    int e = e_begin;
+    for (; e + 1 < e_end; e += 2) {
       step(e, k_s0, v_s0, k_s1, v_s1);
-      if (e + 1 >= e_end) break;
       step(e + 1, k_s1, v_s1, k_s0, v_s0);
     }
+    if (e < e_end) step(e, k_s0, v_s0, k_s1, v_s1);
   }
 
   if (pslot >= 0) {
