@@ -222,3 +222,22 @@ def test_split_q_tiles_full_compare(case):
     ref_out, ref_lse = O.attention_fwd(to64(q), to64(k), to64(v), qr, kr, ty, scale, cap, alibi_slopes=sl32)
     e_out, e_lse = compare_out_lse(out.cpu(), lse.cpu(), ref_out, ref_lse, name)
     say(f"  out max-abs {e_out:.3e}  lse max-abs {e_lse:.3e}")
+
+
+@pytest.mark.parametrize("Tq,Tk", [(300, 0), (0, 300)])
+def test_empty_token_axis(Tq, Tk):
+    """No keys: every row sees nothing (out 0, lse -inf, dq 0).  No queries:
+    every key is seen by nothing (dk = dv = 0)."""
+    say(f"empty axis Tq={Tq} Tk={Tk}")
+    d = dev()
+    q, k, v, do = W.make_tensors(Tq, Tk, 4, 2, 128, seed=13)
+    qd, kd, vd, od = q.to(d), k.to(d), v.to(d), do.to(d)
+    for qr, kr, ty in (([[0, Tq]], [[0, Tk]], [1]), ([[0, 0], [0, 0]], [[0, 0], [0, 0]], [0, 1]), ([], [], [])):
+        out = torch.full_like(qd, 7.0)
+        lse = torch.full((Tq, 4), 7.0, dtype=torch.float32, device=d)
+        ffa.ffa_fwd(qd, kd, vd, qr, kr, ty, 0.1, 0.0, out=out, lse=lse)
+        dq, dk, dv = (torch.full_like(t, 7.0) for t in (qd, kd, vd))
+        ffa.ffa_bwd(qd, kd, vd, out, lse, od, qr, kr, ty, 0.1, 0.0, dq=dq, dk=dk, dv=dv)
+        torch.cuda.synchronize()
+        assert torch.all(out == 0) and torch.all(lse == float("-inf"))
+        assert torch.all(dq == 0) and torch.all(dk == 0) and torch.all(dv == 0)
