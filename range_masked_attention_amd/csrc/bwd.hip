@@ -46,9 +46,10 @@ namespace {
 constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------- bwd_pre
-// Thread t takes head t / Tq, row t % Tq: the head-major writes coalesce
-// and each thread reads its own 2D-byte rows of out and dO.  lse2 is lse in
-// exp2 units with -inf (a row that sees nothing) turned into +inf, so that
+// Thread r takes (row r / hq, head r % hq), so that a workgroup reads a run
+// of whole rows of out and dO; the two results go to their head-major
+// places (small writes: 8 bytes per row and head).  lse2 is lse in exp2
+// units with -inf (a row that sees nothing) turned into +inf, so that
 // exp2(s - lse2) is 0 there rather than NaN.
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const __bf16* __restrict__ out,
@@ -56,10 +57,10 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const __bf16* __restr
                                                           const float* __restrict__ lse,
                                                           float* __restrict__ dvec, float* __restrict__ lse2,
                                                           int64_t Tq, int hq) {
-  const int64_t t = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (t >= Tq * hq) return;
-  const int64_t head = t / Tq, row = t - head * Tq;
-  const int64_t r = row * hq + head;
+  const int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (r >= Tq * hq) return;
+  const int64_t row = r / hq, head = r - row * hq;
+  const int64_t t = head * Tq + row;
   const u32x4* po = reinterpret_cast<const u32x4*>(out + r * D);
   const u32x4* pd = reinterpret_cast<const u32x4*>(dout + r * D);
   float acc = 0.f;
