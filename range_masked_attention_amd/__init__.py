@@ -15,9 +15,11 @@ softmax_scale None = 1/sqrt(head_dim); softcap 0 = off) and returns
 """
 from __future__ import annotations
 
+import collections
 import ctypes
 import math
 import os
+import threading
 from typing import Optional, Tuple
 
 import numpy as np
@@ -28,7 +30,7 @@ __all__ = [
     "ffa_plan_create", "ffa_fwd_planned", "ffa_bwd_planned", "ffa_plan_destroy",
     "ffa_plan_device_workspace_size", "ffa_plan_create_device", "ffa_plan_refresh", "ffa_plan_status",
     "ffa_plan_export", "FFA_PLAN_BAD_SLICE", "FFA_PLAN_CAPACITY", "flex_flash_attn_func",
-    "alibi_geometric_slopes", "ffa_block_slices", "ffa_fwd_ex", "ffa_bwd_ex", "ffa_fwd_planned_ex", "ffa_bwd_planned_ex",
+    "alibi_geometric_slopes", "ffa_block_slices", "cached_plan", "clear_plan_cache", "ffa_fwd_ex", "ffa_bwd_ex", "ffa_fwd_planned_ex", "ffa_bwd_planned_ex",
 ]
 
 FULL = 0
@@ -336,6 +338,74 @@ def ffa_plan_destroy(plan, device=None) -> None:
         return
     dev_ = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
     _check(load_library().ffa_plan_destroy(plan, torch.cuda.current_stream(dev_).cuda_stream))
+
+
+class _PlanCache:
+    """Plans of recently seen slice lists, per (device, stream, Tq, Tk, slices).
+
+    A plan depends only on the sizes and the slice list, so layers and steps
+    that share a mask can share it: the host planning and upload then happen
+    once instead of on every call.  Keyed by stream as well, because a plan is
+    uploaded on its stream and its forward scratch must not be used by two
+    streams at once.  Least recently used plans are destroyed, in order, on
+    the stream they were made for.
+    """
+
+    def __init__(self, capacity: int):
+        self.capacity = capacity
+        self._plans = collections.OrderedDict()
+        self._lock = threading.Lock()
+        self.hits = 0
+        self.misses = 0
+
+    def get(self, Tq: int, Tk: int, q_ranges, k_ranges, attn_type_map, device):
+        import torch
+        qr, kr, ty = _host_slices(q_ranges, k_ranges, attn_type_map)
+        stream = torch.cuda.current_stream(device).cuda_stream
+        key = (device.index, stream, int(Tq), int(Tk), qr.tobytes(), kr.tobytes(), ty.tobytes())
+        with self._lock:
+            plan = self._plans.get(key)
+            if plan is not None:
+                self._plans.move_to_end(key)
+                self.hits += 1
+                return plan
+        plan = ffa_plan_create(Tq, Tk, qr, kr, ty, device=device)
+        evicted = []
+        with self._lock:
+            self.misses += 1
+            self._plans[key] = plan
+            while len(self._plans) > self.capacity:
+                evicted.append(self._plans.popitem(last=False))
+        for (dev_index, st, *_), old in evicted:
+            _check(load_library().ffa_plan_destroy(old, st))
+        return plan
+
+    def clear(self):
+        with self._lock:
+            items = list(self._plans.items())
+            self._plans.clear()
+        for (dev_index, st, *_), old in items:
+            _check(load_library().ffa_plan_destroy(old, st))
+
+
+_PLAN_CACHE = _PlanCache(int(os.environ.get("FFA_PLAN_CACHE", "16")))
+
+
+def cached_plan(Tq: int, Tk: int, q_ranges, k_ranges, attn_type_map, device=None):
+    """A plan for these slices from the process-wide cache (``FFA_PLAN_CACHE``
+    plans, default 16; 0 turns the cache off and returns None), made with
+    ``ffa_plan_create`` on the current stream of ``device`` when not cached.
+    The cache owns the plan: do not destroy it."""
+    import torch
+    if _PLAN_CACHE.capacity <= 0:
+        return None
+    dev_ = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    return _PLAN_CACHE.get(Tq, Tk, q_ranges, k_ranges, attn_type_map, dev_)
+
+
+def clear_plan_cache() -> None:
+    """Destroy every cached plan (stream-ordered on the streams they were made for)."""
+    _PLAN_CACHE.clear()
 
 
 FFA_PLAN_BAD_SLICE = 1

@@ -15,6 +15,11 @@ through the ctypes binding (slice tensors on the GPU are copied to the host
 there: one synchronisation).  ``lse`` is returned without a gradient, as in the
 eager autograd path.  The optional ``alibi_slopes`` (fp32 [hq] on the GPU: a
 distance bias ``slope[h] * (j - i)`` on the scores) takes no gradient either.
+
+Plans come from the binding's plan cache (``cached_plan``), so a mask shared by
+many layers and steps is planned on the host once; with the cache turned off
+(``FFA_PLAN_CACHE=0``) every call plans for itself through the one-shot entry
+points.
 """
 from __future__ import annotations
 
@@ -22,8 +27,11 @@ from typing import Optional, Tuple
 
 import torch
 
+from . import cached_plan as _cached_plan
 from . import ffa_bwd as _ffa_bwd
+from . import ffa_bwd_planned as _ffa_bwd_planned
 from . import ffa_fwd as _ffa_fwd
+from . import ffa_fwd_planned as _ffa_fwd_planned
 
 NAMESPACE = "ffa_amd"
 
@@ -32,7 +40,10 @@ NAMESPACE = "ffa_amd"
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_ranges: torch.Tensor,
         k_ranges: torch.Tensor, attn_type_map: torch.Tensor, scale: float,
         softcap: float, alibi_slopes: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    return _ffa_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, scale, softcap, alibi_slopes=alibi_slopes)
+    plan = _cached_plan(q.shape[0], k.shape[0], q_ranges, k_ranges, attn_type_map, q.device)
+    if plan is None:
+        return _ffa_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, scale, softcap, alibi_slopes=alibi_slopes)
+    return _ffa_fwd_planned(plan, q, k, v, scale, softcap, alibi_slopes=alibi_slopes)
 
 
 @fwd.register_fake
@@ -46,8 +57,12 @@ def bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o
         lse: torch.Tensor, q_ranges: torch.Tensor, k_ranges: torch.Tensor,
         attn_type_map: torch.Tensor, scale: float, softcap: float,
         alibi_slopes: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    return _ffa_bwd(q, k, v, out, lse, dout.contiguous(), q_ranges, k_ranges, attn_type_map,
-                    scale, softcap, alibi_slopes=alibi_slopes)
+    plan = _cached_plan(q.shape[0], k.shape[0], q_ranges, k_ranges, attn_type_map, q.device)
+    if plan is None:
+        return _ffa_bwd(q, k, v, out, lse, dout.contiguous(), q_ranges, k_ranges, attn_type_map,
+                        scale, softcap, alibi_slopes=alibi_slopes)
+    return _ffa_bwd_planned(plan, q, k, v, out, lse, dout.contiguous(), scale, softcap,
+                            alibi_slopes=alibi_slopes)
 
 
 @bwd.register_fake
