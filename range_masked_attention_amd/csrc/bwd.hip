@@ -161,6 +161,19 @@ __device__ __forceinline__ bf16x8 tr8(const char* t, int lane_off, int db, int t
   return __builtin_bit_cast(bf16x8, x);
 }
 
+// LDS address of tile `t` plus a per-lane offset, as a value the compiler
+// cannot see through.  A read of such a base plus a compile-time offset then
+// takes the offset as the instruction's immediate, also for tiles that sit
+// above the 64 KiB an immediate reaches from address 0; otherwise the
+// compiler keeps a separate address register per read of those tiles.
+__device__ __forceinline__ const char* lane_base(const char* t, int lane_off) {
+  const uint32_t t32 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)t;
+  uint32_t a = t32 + (uint32_t)lane_off;
+  asm volatile("" : "+v"(a));
+  // still an offset from t, so the compiler knows which buffer is read
+  return t + (int)(a - t32);
+}
+
 // Wait for this wave's direct-to-LDS loads, then for the whole workgroup.
 __device__ __forceinline__ void dma_barrier() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -323,6 +336,10 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int n_steps = (e_end - e_begin) * a.grp;
   const int tro = tr_lane_offset<D>(lane);
   const int lrow = T::off(n, hh);
+  // read bases of the tile buffers: producers read Q rows and dO transposed,
+  // consumers Q transposed and dO rows
+  const char* qb3[3];
+  const char* ob2[2];
 
   // step st = (entry e, q head): producers fetch the Q tile, consumers the
   // dO tile; wave 0 also fetches the step's lse and D (first, so that a
@@ -385,8 +402,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         bias_key = const_load<float>(a.slopes, g * a.grp + p_h) * 1.4426950408889634f *
                    (float)(key - ent.tile * kDkvRows);
       advance(p_e, p_h);
-      const char* qt = qbuf(r);
-      const char* ot = obuf(r);
+      const char* qt = qb3[R % 3];  // rows of Q
+      const char* ot = ob2[R % 2];  // transposed dO
       float* xch = xchg[st & 1][pair];
 
       // S = Q K^T : [64 q x 32 keys] as two 32-row blocks
@@ -394,9 +411,11 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         s[qb] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) s[qb] = mfma_32x32x16(T::row8(qt, lrow, 32 * qb, 2 * ks), frag[ks], s[qb]);
       }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) s[qb] = mfma_32x32x16(T::row8(qt, 0, 32 * qb, 2 * ks), frag[ks], s[qb]);
       // P; element (qb, v) is row 32qb + 8(v/4) + 4hh + v%4, key `key`
       // the per-cell mask only on PARTIAL entries (a FULL entry has every
       // cell visible, tails included), chosen once per step
@@ -439,10 +458,10 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         p_tile(std::false_type{});
       // dV^T += dO^T P : contraction over the 64 rows
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4)
-          acc[db] = mfma_32x32x16(tr8<D>(ot, tro, db, t4), __builtin_bit_cast(bf16x8, pw[t4]), acc[db]);
+        for (int db = 0; db < DB; ++db)
+          acc[db] = mfma_32x32x16(tr8<D>(ot, 0, db, t4), __builtin_bit_cast(bf16x8, pw[t4]), acc[db]);
       if (st + 1 < n_steps) publish((st + 1) % 3);
     }
     dma_barrier();
@@ -455,7 +474,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     if (st + 1 < n_steps) issue(obuf(IC<R + 1>{}));
     if (st > 0) {
       const float* xch = xchg[(st - 1) & 1][pair];
-      const char* qt = qbuf(IC<decltype(r)::value + 5>{});  // tile st - 1
+      const char* qt = qb3[(R + 5) % 3];  // transposed Q of step st - 1
       u32x4 dw[4];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
@@ -472,19 +491,21 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         }
       // dK^T += Q^T dS
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
-        for (int t4 = 0; t4 < 4; ++t4)
-          acc[db] = mfma_32x32x16(tr8<D>(qt, tro, db, t4), __builtin_bit_cast(bf16x8, dw[t4]), acc[db]);
+        for (int db = 0; db < DB; ++db)
+          acc[db] = mfma_32x32x16(tr8<D>(qt, 0, db, t4), __builtin_bit_cast(bf16x8, dw[t4]), acc[db]);
     }
     if (st < n_steps) {
-      const char* ot = obuf(r);
+      const char* ot = ob2[R % 2];  // rows of dO
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         dp[qb] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) dp[qb] = mfma_32x32x16(T::row8(ot, lrow, 32 * qb, 2 * ks), frag[ks], dp[qb]);
       }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) dp[qb] = mfma_32x32x16(T::row8(ot, 0, 32 * qb, 2 * ks), frag[ks], dp[qb]);
     }
     dma_barrier();
   };
@@ -495,6 +516,11 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
     dma_barrier();
     // n_steps + 1 steps in both roles, so both pass the same barriers
     if (producer) {
+      qb3[0] = lane_base(q_s0, lrow);
+      qb3[1] = lane_base(q_s1, lrow);
+      qb3[2] = lane_base(q_s2, lrow);
+      ob2[0] = lane_base(o_s0, tro);
+      ob2[1] = lane_base(o_s1, tro);
       for (int st = 0; st <= n_steps; st += 6) {
         pstep(st, IC<0>{});
         if (st + 1 > n_steps) break;
@@ -509,6 +535,11 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
         pstep(st + 5, IC<5>{});
       }
     } else {
+      qb3[0] = lane_base(q_s0, tro);
+      qb3[1] = lane_base(q_s1, tro);
+      qb3[2] = lane_base(q_s2, tro);
+      ob2[0] = lane_base(o_s0, lrow);
+      ob2[1] = lane_base(o_s1, lrow);
       for (int st = 0; st <= n_steps; st += 6) {
         cstep(st, IC<0>{});
         if (st + 1 > n_steps) break;
