@@ -78,102 +78,6 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const __bf16* __restr
   lse2[t] = (l == -INFINITY) ? INFINITY : l * 1.4426950408889634f;
 }
 
-// ---------------------------------------------------------------- tiles
-// A 64-row x D tile in LDS, fetched by direct-to-LDS loads.  One load
-// instruction fills 64 consecutive 16-byte slots (lane L -> slot L); the
-// slots of instruction i start at byte 1088 * i (1024 + 64 bytes padding).
-//   D = 128: instruction i holds rows 4i .. 4i + 3, slot L = row 4i + L % 4,
-//            chunk L / 4, so one instruction reads 4 whole rows from HBM;
-//   D = 64:  instruction i holds chunk i of all 64 rows (slot L = row L).
-// Either way the byte offset of (row, chunk) is linear in row and chunk as
-// long as the row offsets added are multiples of 4 (D = 128) -- see off() --
-// so every read address is a per-lane base plus a compile-time immediate.
-// Row operands (16 lanes, 16 consecutive rows, one chunk) and transposed
-// operands (4 rows x 4 chunks per 32 lanes) both land on 16 distinct
-// 16-byte bank groups: no LDS bank conflicts on the 64 banks.
-template <int D>
-struct ColTile {
-  static constexpr int kChunks = D / 8;
-  static constexpr int kRG = (D == 128) ? 4 : 64;       // rows per instruction group
-  static constexpr int kCS = (D == 128) ? 64 : 1088;    // bytes between chunks
-  static constexpr int kGS = 1088;                      // bytes between row groups
-  static constexpr int kBytes = kChunks * 1088;
-  static_assert(D == 64 || D == 128, "head dim");
-
-  __device__ __forceinline__ static constexpr int off(int row, int chunk) {
-    return (row / kRG) * kGS + chunk * kCS + (row % kRG) * 16;
-  }
-
-  // Fetch rows [0, 64) of a tile whose row r starts at byte r * row_bytes
-  // of resource `r` (rows past the resource read as zeros); wave w issues
-  // instructions w * kChunks / 4 .. +kChunks / 4.
-  __device__ __forceinline__ static void load(__amdgpu_buffer_rsrc_t r, uint32_t row_bytes, char* dst,
-                                              int w, int lane) {
-    constexpr int kPer = kChunks / 4;
-    uint32_t lane_off, step;
-    if constexpr (D == 128) {
-      lane_off = (uint32_t)(lane & 3) * row_bytes + (uint32_t)(lane >> 2) * 16;
-      step = 4 * row_bytes;
-    } else {
-      lane_off = (uint32_t)lane * row_bytes;
-      step = 16;
-    }
-#pragma unroll
-    for (int c = 0; c < kPer; ++c) {
-      const int i = w * kPer + c;  // wave-uniform
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          r, (__attribute__((address_space(3))) void*)(dst + i * 1088), 16, lane_off + (uint32_t)i * step, 0, 0, 0);
-    }
-  }
-  // Row operand: 8 elements (16 bytes) of row r0 + n, chunk c0 + hh, with
-  // lane_row = off(n, hh) and r0 a multiple of 32, c0 even.
-  __device__ __forceinline__ static bf16x8 row8(const char* t, int lane_row, int r0, int c0) {
-    return *reinterpret_cast<const bf16x8*>(t + lane_row + off(r0, c0));
-  }
-};
-
-// Byte offset of this lane's transpose-read source inside a ColTile: the
-// 16-lane group g16 / index sl of lane `lane` points at row 4*hh + sl/4 and
-// 4 dims at 16*(g16 & 1) + 4*(sl & 3).  Adding the block offsets below
-// gives, in each lane, 4 consecutive rows (of the 8 the MFMA k index needs)
-// of one dim: the order of a 32x32 accumulator's rows, so the accumulator's
-// registers can be the other operand directly.
-template <int D>
-__device__ __forceinline__ int tr_lane_offset(int lane) {
-  const int hh = lane >> 5, g16 = lane >> 4, sl = lane & 15;
-  const int col = 16 * (g16 & 1) + 4 * (sl & 3);
-  return ColTile<D>::off(4 * hh + (sl >> 2), col >> 3) + (col & 7) * 2;
-}
-
-// A operand of C[dims x 32] += T^T[dims 32db.. x rows] X[rows x 32]: the
-// transposed tile T, rows 32*(t >> 1) + 16*(t & 1) + {0..3, 8..11} + 4*hh.
-template <int D>
-__device__ __forceinline__ bf16x8 tr8(const char* t, int lane_off, int db, int t4) {
-  typedef short v4s __attribute__((ext_vector_type(4)));
-  const int r0 = 32 * (t4 >> 1) + 16 * (t4 & 1);
-  const char* p = t + lane_off + ColTile<D>::off(r0, 4 * db);
-  const char* p8 = t + lane_off + ColTile<D>::off(r0 + 8, 4 * db);
-  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(const_cast<char*>(p)));
-  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(const_cast<char*>(p8)));
-  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-  u32x4 x;
-  x[0] = l2[0]; x[1] = l2[1]; x[2] = h2[0]; x[3] = h2[1];
-  return __builtin_bit_cast(bf16x8, x);
-}
-
-// LDS address of tile `t` plus a per-lane offset, as a value the compiler
-// cannot see through.  A read of such a base plus a compile-time offset then
-// takes the offset as the instruction's immediate, also for tiles that sit
-// above the 64 KiB an immediate reaches from address 0; otherwise the
-// compiler keeps a separate address register per read of those tiles.
-__device__ __forceinline__ const char* lane_base(const char* t, int lane_off) {
-  const uint32_t t32 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)t;
-  uint32_t a = t32 + (uint32_t)lane_off;
-  asm volatile("" : "+v"(a));
-  // still an offset from t, so the compiler knows which buffer is read
-  return t + (int)(a - t32);
-}
-
 // Wait for this wave's direct-to-LDS loads, then for the whole workgroup.
 __device__ __forceinline__ void dma_barrier() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

@@ -225,16 +225,19 @@ template <int D, bool INIT = false>
 __device__ __forceinline__ void qk_tile(const __bf16* kl, const bf16x8* qf, int n, int hh, f32x16* s) {
   using Smem = FwdSmem<D>;
   const int swz = Smem::k_swz(n);  // rows n and 32 + n share it
+  if constexpr (!INIT) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+  }
+  // the two blocks' accumulator chains take turns
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    if constexpr (!INIT) s[b] = f32x16{};
+  for (int ks = 0; ks < D / 16; ++ks)
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
+    for (int b = 0; b < 2; ++b) {
       const int byte = (32 * b + n) * Smem::kRowBytes + (((2 * ks + hh) ^ swz) * 16);
       const bf16x8 kf = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(kl) + byte);
       s[b] = mfma_32x32x16(kf, qf[ks], s[b]);
     }
-  }
 }
 
 // Softcap in exp2 units: cap*log2(e) * tanh(scale * s / cap), plus with BIAS
@@ -252,14 +255,16 @@ __device__ __forceinline__ void softcap_tile(const FwdArgs& a, f32x16* s, float 
     }
 }
 
-// Row max over this lane's 32 scores and the other half-wave's 32.
+// Row max over this lane's 32 scores and the other half-wave's 32 (the
+// halves trade their partial maxima by a lane swap, not through LDS).
 __device__ __forceinline__ float tile_max(const f32x16* s) {
   float mx = -INFINITY;
 #pragma unroll
   for (int b = 0; b < 2; ++b)
 #pragma unroll
     for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[b][v]);
-  return fmaxf(mx, __shfl_xor(mx, 32));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Invisible cells of a PARTIAL tile become -inf (cell (row, key) of slice sl).
@@ -343,7 +348,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int i = 0; i < DB; ++i) o[i] = f32x16{};
   float m_run = -INFINITY;  // running row max, in the units fed to score_mult
-  float l_part = 0.f;       // this half-wave's share of the row sum
+  float l4[4] = {0.f, 0.f, 0.f, 0.f};  // this half-wave's share of the row sum, four chains
 
   // V^T fragments by transpose reads: lane (group g16, index sl) points at
   // key row v_krow (+ block offsets), 4 dims at v_col
@@ -363,6 +368,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
     f32x16 sa[2], sb[2];
     scores(kb0, entry(0).tile, sa);
     float mx_cur = tile_max(sa);
+    // entries of walk positions j, j + 1 and j + 2 (the last one past the
+    // end) for step j.  Later entries arrive by vector loads issued with a
+    // step's fetches, so the wait for those fetches covers them; a scalar
+    // load of the plan would be waited for at its first use, a scalar cache
+    // miss in most steps.
+    DevEntry e0 = entry(0);
+    DevEntry e1 = entry(min(1, n_tiles - 1));
+    DevEntry e2 = entry(min(2, n_tiles - 1));
+    const __amdgpu_buffer_rsrc_t ers = make_rsrc(a.entries, (int64_t)e_end * 8);
     __syncthreads();  // K0's buffer is refilled in the first step
 
     // One pipeline step on tile j whose scores are in s_cur.  K_j sits in
@@ -372,7 +386,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
                     const __bf16* vcur, __bf16* vnext, auto more_tag) {
       constexpr bool MORE = decltype(more_tag)::value;
       // ---- tile j: mask (PARTIAL only) and the running max
-      const DevEntry ent = entry(j);
+      const DevEntry ent = e0;
       if (ent.meta & 1) {
         mask_tile(plan_slice(a.slices, ent.meta >> 1), ent.tile, row, hh, s_cur);
         mx_cur = tile_max(s_cur);
@@ -386,7 +400,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
         // rows that have seen nothing yet: -inf - -inf would be NaN); a row
         // whose first visible key arrives gets exp2(-inf) = 0
         const float alpha = (m_new == m_run) ? 1.0f : fast_exp2((m_run - m_new) * a.score_mult);
-        l_part *= alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) l4[i] *= alpha;
 #pragma unroll
         for (int i = 0; i < DB; ++i) o[i] *= alpha;
         m_run = m_new;
@@ -395,13 +410,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
 
       // ---- A: S_{j+1} = K_{j+1} Q^T on the matrix cores, while
       //      B: the VALU turns tile j into exp2 weights
+      // (raised wave priority: the other workgroup's wave on this SIMD gets
+      // the issue slots this phase leaves)
+      i32x2 ev;
       if constexpr (MORE) {
-        // direct loads for later tiles, K two ahead and V one ahead, issued
-        // among the QK products (the schedule below spreads them); past the
-        // last tile the K fetch reloads the last tile into a buffer nobody
-        // reads again, so every step issues the same loads
-        dma.load_k(entry(min(j + 2, n_tiles - 1)).tile, kcur, w);
-        const int next_tile = entry(j + 1).tile;
+        __builtin_amdgcn_s_setprio(1);
+        // entry of walk position j + 3, then direct loads for later tiles,
+        // K two ahead and V one ahead, issued among the QK products (the
+        // schedule below spreads them); past the last tile the K fetch
+        // reloads the last tile into a buffer nobody reads again, so every
+        // step issues the same loads
+        const int x3 = min(j + 3, n_tiles - 1);
+        ev = __builtin_amdgcn_raw_buffer_load_b64(ers, 0, (down ? e_end - 1 - x3 : e_begin + x3) * 8, 0);
+        dma.load_k(e2.tile, kcur, w);
+        const int next_tile = e1.tile;
         dma.load_v(next_tile, vnext, w);
         if constexpr (BIAS && !SOFTCAP) {
           bias_tile(sigma, next_tile, d0, s_next);
@@ -410,8 +432,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
           qk_tile<D>(knext, qf, n, hh, s_next);
         }
       }
+      // fp32 sum of the unrounded weights (the lse must hold to 1e-3 even
+      // for rows with a handful of keys), four independent chains
       u32x4 pw[4];
-      float rs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int b = t >> 1, h8 = (t & 1) * 8;
@@ -419,21 +442,32 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int e8 = 0; e8 < 8; ++e8) {
           p[e8] = fast_exp2(__builtin_fmaf(s_cur[b][h8 + e8], a.score_mult, neg));
-          rs[e8 & 3] += p[e8];
+          l4[e8 & 3] += p[e8];
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) pw[t][i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);
       }
-      // fp32 sum of the unrounded weights (the lse must hold to 1e-3 even
-      // for rows with a handful of keys), four independent chains
-      l_part += (rs[0] + rs[1]) + (rs[2] + rs[3]);
 
+      if constexpr (MORE) {
+        // Instruction order for the block above: the K reads run 4 ahead of
+        // the QK products, and the softmax VALU fills the shadow of each MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          if (i < 2 * TileDma<D>::kPerThread + 1)
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // entry load, direct-to-LDS fetches
+          if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, SOFTCAP ? 5 : 7, 0);  // VALU
+        }
+        __builtin_amdgcn_s_setprio(0);
+      }
       // ---- C: O^T += V_j^T P_j^T (V^T fragments by transpose reads), while
       //      B': softcap and the unmasked row max of tile j+1
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int db = 0; db < DB; ++db) {
           const int kb = 32 * (t >> 1) + 16 * (t & 1) + v_krow;
           const int col_byte = 2 * (32 * db + v_col);
           const int byte = kb * Smem::kRowBytes + (((col_byte >> 4) ^ v_sw) << 4) + (col_byte & 15);
@@ -445,31 +479,25 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
           o[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, pw[t]), o[db]);
         }
       if constexpr (MORE) {
-        if constexpr (SOFTCAP) softcap_tile<BIAS>(a, s_next, sigma, entry(j + 1).tile, d0);
+        if constexpr (SOFTCAP) softcap_tile<BIAS>(a, s_next, sigma, e1.tile, d0);
         mx_cur = tile_max(s_next);
-        // Instruction order for the block above: the K reads run 4 ahead of
-        // the QK products, and the softmax VALU fills the shadow of each
-        // MFMA; then the V transpose reads run 8 ahead of the PV products,
-        // with the row max of the next tile in their shadows.
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS read
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          if (i < 2 * TileDma<D>::kPerThread)
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // direct-to-LDS fetch
-          if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, SOFTCAP ? 5 : 7, 0);  // VALU
-        }
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        // Instruction order for the block above: the V transpose reads run 8
+        // ahead of the PV products, with the row max of the next tile in
+        // their shadows.
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // DS read
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, SOFTCAP ? 8 : 2, 0);
         }
-        // K_{j+2} and V_{j+1} have landed, and every wave is done reading
-        // K_{j+1} and V_j, whose buffers the next steps refill
+        // K_{j+2}, V_{j+1} and the entry have landed, and every wave is done
+        // reading K_{j+1} and V_j, whose buffers the next steps refill
         dma_barrier();
+        e0 = e1;
+        e1 = e2;
+        e2.tile = __builtin_amdgcn_readfirstlane(ev[0]);
+        e2.meta = __builtin_amdgcn_readfirstlane(ev[1]);
       }
     };
     using More = std::integral_constant<bool, true>;
@@ -491,6 +519,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   }
 
   // ---- epilogue: normalise once in fp32, round to bf16 once
+  const float l_part = (l4[0] + l4[1]) + (l4[2] + l4[3]);
   const float l = l_part + __shfl_xor(l_part, 32);
   const float inv = l > 0.f ? 1.0f / l : 0.f;
   if (item.slot >= 0) {
