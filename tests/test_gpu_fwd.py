@@ -241,3 +241,30 @@ def test_empty_token_axis(Tq, Tk):
         torch.cuda.synchronize()
         assert torch.all(out == 0) and torch.all(lse == float("-inf"))
         assert torch.all(dq == 0) and torch.all(dk == 0) and torch.all(dv == 0)
+
+
+# key-tile lists of 1 to 5 tiles (64 keys a tile, ragged last tile), walked
+# upwards and, with positive distance-bias slopes, downwards: the forward
+# carries the entries of the next positions and prefetches the one after,
+# clamped at the end of the list
+@pytest.mark.parametrize("Tk", [40, 100, 170, 230, 300])
+@pytest.mark.parametrize("walk", ["up", "down"])
+def test_short_key_lists(Tk, walk):
+    say(f"fwd short key list Tk={Tk} walk={walk}")
+    Tq, hq, hkv, d = 200, 4, 2, 128
+    q, k, v, _ = W.make_tensors(Tq, Tk, hq, hkv, d, seed=Tk, with_dout=False)
+    qr = np.array([[0, Tq], [0, 0]], dtype=np.int32)
+    kr = np.array([[0, Tk], [0, 0]], dtype=np.int32)
+    ty = np.array([0, 0], dtype=np.int32)
+    scale = 0.125
+    dv_ = dev()
+    if walk == "up":
+        out, lse = run_fwd(q, k, v, qr, kr, ty, scale, 0.0, dv_)
+        slopes = None
+    else:
+        st = torch.full((hq,), 0.05, dtype=torch.float32, device=dv_)
+        out, lse = ffa.ffa_fwd_ex(q.to(dv_), k.to(dv_), v.to(dv_), qr, kr, ty, scale, 0.0, st)
+        torch.cuda.synchronize()
+        slopes = st.double().cpu().numpy()
+    ref_out, ref_lse = O.attention_fwd(to64(q), to64(k), to64(v), qr, kr, ty, scale, 0.0, alibi_slopes=slopes)
+    compare_out_lse(out.cpu(), lse.cpu(), ref_out, ref_lse, f"Tk {Tk} {walk}")
