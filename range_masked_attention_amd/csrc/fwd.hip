@@ -368,11 +368,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
     f32x16 sa[2], sb[2];
     scores(kb0, entry(0).tile, sa);
     float mx_cur = tile_max(sa);
-    // entries of walk positions j, j + 1 and j + 2 (the last one past the
-    // end) for step j.  Later entries arrive by vector loads issued with a
-    // step's fetches, so the wait for those fetches covers them; a scalar
-    // load of the plan would be waited for at its first use, a scalar cache
-    // miss in most steps.
+    // entries of walk positions j, j + 1 and j + 2 for step j (positions
+    // past the end of the list repeat its last entry).  Later entries arrive
+    // by vector loads issued with a step's fetches, so the step's closing
+    // wait for those fetches covers them; a scalar load of the plan would be
+    // waited for inside the step, which also drains the LDS reads in flight,
+    // and it misses the scalar cache every few steps.
     DevEntry e0 = entry(0);
     DevEntry e1 = entry(min(1, n_tiles - 1));
     DevEntry e2 = entry(min(2, n_tiles - 1));
