@@ -126,7 +126,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; pass --gpus 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU only; pass --gpus 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
