@@ -274,3 +274,23 @@ def test_guard_band():
         assert torch.equal(g, r)
     for buf in bufs[n_in:]:
         assert torch.isnan(buf[:G].float()).all() and torch.isnan(buf[-G:].float()).all()
+
+
+# short lists on both sides: key-tile lists of 1 to 5 tiles (dQ walks them)
+# and q-tile lists of 1 to 2 tiles (dK/dV walks those, one step per q head),
+# ragged last tiles, a causal and a full slice
+@pytest.mark.parametrize("Tk", [40, 100, 170, 230, 300])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_short_lists(Tk, causal):
+    say(f"bwd short lists Tk={Tk} causal={causal}")
+    Tq, hq, hkv, d = 150, 4, 2, 128
+    q, k, v, do = W.make_tensors(Tq, Tk, hq, hkv, d, seed=500 + Tk + causal)
+    qr = np.array([[0, Tq], [0, 0]], dtype=np.int32)
+    kr = np.array([[0, Tk], [0, 0]], dtype=np.int32)
+    ty = np.array([causal, 0], dtype=np.int32)
+    scale = 0.125
+    dq, dk, dv = _bwd_gpu(q, k, v, do, qr, kr, ty, scale, 0.0, dev())
+    rq, rk, rv, mags = O.attention_bwd(to64(q), to64(k), to64(v), to64(do), qr, kr, ty, scale,
+                                       magnitudes=True)
+    for (n, g, r), m in zip((("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)), mags):
+        _cmp(n, g, r, f"Tk {Tk} causal {causal}", m)
