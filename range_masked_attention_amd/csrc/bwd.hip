@@ -78,12 +78,6 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const __bf16* __restr
   lse2[t] = (l == -INFINITY) ? INFINITY : l * 1.4426950408889634f;
 }
 
-// Wait for this wave's direct-to-LDS loads, then for the whole workgroup.
-__device__ __forceinline__ void dma_barrier() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-}
-
 // Row range of slice `sl` that key j sees: [lo, hi) (empty if hi <= lo).
 __device__ __forceinline__ void key_rows(const DevSlice& sl, int j, int* lo, int* hi) {
   *lo = sl.qs;

@@ -183,4 +183,10 @@ __device__ __forceinline__ const char* lane_base(const char* t, int lane_off) {
   return t + (int)(a - t32);
 }
 
+// Wait for this wave's direct-to-LDS loads, then for the whole workgroup.
+__device__ __forceinline__ void dma_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
 }  // namespace ffa

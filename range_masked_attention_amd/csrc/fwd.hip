@@ -190,12 +190,6 @@ struct TileDma {
   __device__ __forceinline__ void load_v(int ktile, __bf16* dst, int w) const { load<false>(ktile, dst, w); }
 };
 
-// Wait for this wave's direct-to-LDS loads, then for the whole workgroup.
-__device__ __forceinline__ void dma_barrier() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-}
-
 // Transpose read of a row-major tile: in each 16-lane group, lane i receives
 // element i % 4 of the 8-byte chunks addressed by lanes 4r + i / 4, r = 0..3.
 __device__ __forceinline__ u32x2 lds_read_tr16(const __bf16* p) {
