@@ -35,6 +35,10 @@
  *    softcap >= 0 and finite (0 = off).  Tq, Tk >= 0 and every tensor must be
  *    below 2^31 elements.
  *  - Device pointers must be 16-byte aligned.
+ *  - Environment: FFA_DEBUG=1 makes planning reject slice lists in which two
+ *    slices cover one cell (FFA_ERR_INVALID_ARG); FFA_INJECT_NOMEM=1 makes
+ *    every host-side planning step fail with FFA_ERR_NOMEM, for testing a
+ *    caller's handling of that error.
  *  - stream is a hipStream_t (NULL = the default stream).  Calls enqueue work
  *    and return; argument errors are reported synchronously before any GPU
  *    work is enqueued.  The return value is FFA_OK or a negative FFA_ERR_*;

@@ -95,8 +95,15 @@ def slice_cells(sl, rows, cols):
 
 def visibility(slices, rows, cols):
     """Multiplicity matrix M[len(rows), len(cols)]: how many slices cover each cell."""
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
     M = np.zeros((len(rows), len(cols)), dtype=np.int32)
     for sl in slices:
+        _, qs, qe, ks, ke, _t = sl
+        # a slice whose rectangle misses these rows or these columns adds
+        # nothing; skipping it only saves the work of adding zeros
+        if not (np.any((rows >= qs) & (rows < qe)) and np.any((cols >= ks) & (cols < ke))):
+            continue
         M += slice_cells(sl, rows, cols)
     return M
 
@@ -113,13 +120,14 @@ def visible_count(slices, Tq: int, Tk: int, block: int = 1024) -> int:
 # --------------------------------------------------------------------------
 # forward
 # --------------------------------------------------------------------------
-def _row_block_attention(q, k, v, slices, scale, softcap, rows, Tk, alibi_slopes=None):
+def _row_block_attention(q, k, v, slices, scale, softcap, rows, Tk, alibi_slopes=None, heads=None):
     """Scores, probabilities, output and lse for one block of rows.
 
     Returns (cols, vis, s, p, out, lse) per q head, where ``cols`` are the key
     columns that any row of the block can see (found on the materialised
     mask), ``s`` the masked scores (-inf where invisible) and ``p`` the
-    softmax probabilities.
+    softmax probabilities.  ``heads`` (a set of q heads, or None for all)
+    limits the work to those heads; the others get None.
     """
     hq, d = q.shape[1], q.shape[2]
     hkv = k.shape[1]
@@ -133,7 +141,7 @@ def _row_block_attention(q, k, v, slices, scale, softcap, rows, Tk, alibi_slopes
     res = []
     for h in range(hq):
         g = h // grp
-        if cols.size == 0:
+        if cols.size == 0 or (heads is not None and h not in heads):
             res.append(None)
             continue
         u = scale * (q[rows, h, :] @ k[cols, g, :].T)
@@ -162,13 +170,29 @@ def _slopes(alibi_slopes, hq):
     return a
 
 
+def _head_sets(hq, hkv, kv_heads):
+    """(q heads, kv heads) to compute: every head when kv_heads is None, else
+    the listed kv heads and the q heads that read them, in increasing order."""
+    grp = hq // hkv
+    if kv_heads is None:
+        return list(range(hq)), list(range(hkv))
+    kvh = sorted(set(int(g) for g in kv_heads))
+    if any(g < 0 or g >= hkv for g in kvh):
+        raise ValueError("kv_heads out of range")
+    return [h for h in range(hq) if h // grp in kvh], kvh
+
+
 def attention_fwd(q, k, v, q_ranges, k_ranges, types, scale, softcap=0.0,
-                  rows=None, block=256, alibi_slopes=None):
+                  rows=None, block=256, alibi_slopes=None, kv_heads=None):
     """Forward pass: ``out [n, hq, d]`` and ``lse [n, hq]`` for ``rows``.
 
     ``q`` is [Tq, hq, d], ``k`` and ``v`` are [Tk, hkv, d] (float64 arrays).
     ``rows`` selects which query rows to compute (all rows when None).
     ``alibi_slopes`` ([hq] or None): the distance bias described above.
+    ``kv_heads`` (None = all) computes only the q heads that read the listed
+    kv heads; the head axis of the results then holds those q heads in
+    increasing order.  Every head is computed independently, so this only
+    leaves work out.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -181,17 +205,19 @@ def attention_fwd(q, k, v, q_ranges, k_ranges, types, scale, softcap=0.0,
         raise ValueError("softcap must be >= 0")
     slices = normalise_slices(q_ranges, k_ranges, types, Tq, Tk)
     slopes = _slopes(alibi_slopes, hq)
+    qheads, _ = _head_sets(hq, k.shape[1], kv_heads)
+    hpos = {h: i for i, h in enumerate(qheads)}
     rows = np.arange(Tq) if rows is None else np.asarray(rows, dtype=np.int64)
-    out = np.zeros((rows.size, hq, d))
-    lse = np.full((rows.size, hq), -np.inf)
+    out = np.zeros((rows.size, len(qheads), d))
+    lse = np.full((rows.size, len(qheads)), -np.inf)
     for b0 in range(0, rows.size, block):
         rb = rows[b0:b0 + block]
-        _, _, res = _row_block_attention(q, k, v, slices, scale, softcap, rb, Tk, slopes)
+        _, _, res = _row_block_attention(q, k, v, slices, scale, softcap, rb, Tk, slopes, set(qheads))
         for h, r in enumerate(res):
             if r is None:
                 continue
-            out[b0:b0 + rb.size, h, :] = r[2]
-            lse[b0:b0 + rb.size, h] = r[3]
+            out[b0:b0 + rb.size, hpos[h], :] = r[2]
+            lse[b0:b0 + rb.size, hpos[h]] = r[3]
     return out, lse
 
 
@@ -199,7 +225,8 @@ def attention_fwd(q, k, v, q_ranges, k_ranges, types, scale, softcap=0.0,
 # backward
 # --------------------------------------------------------------------------
 def attention_bwd(q, k, v, dout, q_ranges, k_ranges, types, scale, softcap=0.0,
-                  rows=None, keys=None, block=256, magnitudes=False, alibi_slopes=None):
+                  rows=None, keys=None, block=256, magnitudes=False, alibi_slopes=None,
+                  kv_heads=None):
     """Gradients of ``sum(dout * out)``: dq at ``rows``, dk and dv at ``keys``.
 
     Chain rule through the forward above, in the usual flash-attention form:
@@ -210,6 +237,9 @@ def attention_bwd(q, k, v, dout, q_ranges, k_ranges, types, scale, softcap=0.0,
     else in these formulas.
     GQA: dk and dv of a kv head sum over the q heads that read it.
     Returns (dq [len(rows), hq, d], dk [len(keys), hkv, d], dv [len(keys), hkv, d]).
+    ``kv_heads`` (None = all) computes only the listed kv heads and the q
+    heads that read them (every one of them, so dk and dv of a listed kv head
+    are complete); the head axes then hold those heads in increasing order.
 
     With ``magnitudes=True`` it also returns, per gradient element, the scale
     of the rounding error an implementation in rounded arithmetic can carry:
@@ -227,6 +257,9 @@ def attention_bwd(q, k, v, dout, q_ranges, k_ranges, types, scale, softcap=0.0,
     grp = hq // hkv
     slices = normalise_slices(q_ranges, k_ranges, types, Tq, Tk)
     slopes = _slopes(alibi_slopes, hq)
+    qheads, kvheads = _head_sets(hq, hkv, kv_heads)
+    hpos = {h: i for i, h in enumerate(qheads)}
+    gpos = {g: i for i, g in enumerate(kvheads)}
     rows = np.arange(Tq) if rows is None else np.asarray(rows, dtype=np.int64)
     keys = np.arange(Tk) if keys is None else np.asarray(keys, dtype=np.int64)
 
@@ -244,22 +277,23 @@ def attention_bwd(q, k, v, dout, q_ranges, k_ranges, types, scale, softcap=0.0,
     dq_pos[rows] = np.arange(rows.size)
     work = np.nonzero(sees_key | want_dq)[0]
 
-    dq = np.zeros((rows.size, hq, d))
-    dk = np.zeros((keys.size, hkv, d))
-    dv = np.zeros((keys.size, hkv, d))
+    dq = np.zeros((rows.size, len(qheads), d))
+    dk = np.zeros((keys.size, len(kvheads), d))
+    dv = np.zeros((keys.size, len(kvheads), d))
     if magnitudes:
         dq_m, dk_m, dv_m = np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv)
     for b0 in range(0, work.size, block):
         rb = work[b0:b0 + block]
-        cols, vis, res = _row_block_attention(q, k, v, slices, scale, softcap, rb, Tk, slopes)
+        cols, vis, res = _row_block_attention(q, k, v, slices, scale, softcap, rb, Tk, slopes, set(qheads))
         if cols.size == 0:
             continue
         kp = key_pos[cols]
         kmask = kp >= 0
         dq_rows = dq_pos[rb]
         dq_mask = dq_rows >= 0
-        for h in range(hq):
+        for h in qheads:
             g = h // grp
+            hi, gi = hpos[h], gpos[g]
             s, p, out, lse, u = res[h]
             do = dout[rb, h, :]
             D = (do * out).sum(axis=1)
@@ -270,18 +304,18 @@ def attention_bwd(q, k, v, dout, q_ranges, k_ranges, types, scale, softcap=0.0,
             else:
                 dU = dS
             if dq_mask.any():
-                dq[dq_rows[dq_mask], h, :] += scale * (dU[dq_mask] @ k[cols, g, :])
+                dq[dq_rows[dq_mask], hi, :] += scale * (dU[dq_mask] @ k[cols, g, :])
             if kmask.any():
-                dv[kp[kmask], g, :] += p[:, kmask].T @ do
-                dk[kp[kmask], g, :] += scale * (dU[:, kmask].T @ q[rb, h, :])
+                dv[kp[kmask], gi, :] += p[:, kmask].T @ do
+                dk[kp[kmask], gi, :] += scale * (dU[:, kmask].T @ q[rb, h, :])
             if magnitudes:
                 A = (np.abs(do) * (np.abs(out) + p @ np.abs(v[cols, g, :]))).sum(axis=1)
                 dU_abs = np.abs(dU) + p * A[:, None]
                 if dq_mask.any():
-                    dq_m[dq_rows[dq_mask], h, :] += scale * (dU_abs[dq_mask] @ np.abs(k[cols, g, :]))
+                    dq_m[dq_rows[dq_mask], hi, :] += scale * (dU_abs[dq_mask] @ np.abs(k[cols, g, :]))
                 if kmask.any():
-                    dv_m[kp[kmask], g, :] += p[:, kmask].T @ np.abs(do)
-                    dk_m[kp[kmask], g, :] += scale * (dU_abs[:, kmask].T @ np.abs(q[rb, h, :]))
+                    dv_m[kp[kmask], gi, :] += p[:, kmask].T @ np.abs(do)
+                    dk_m[kp[kmask], gi, :] += scale * (dU_abs[:, kmask].T @ np.abs(q[rb, h, :]))
     if magnitudes:
         return dq, dk, dv, (dq_m, dk_m, dv_m)
     return dq, dk, dv

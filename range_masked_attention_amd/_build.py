@@ -2,8 +2,8 @@
 
 ``python -m range_masked_attention_amd._build`` compiles every source under
 ``csrc/`` and links ``_lib/libffa.so``.  Objects go to ``_build/`` at the repo
-root.  The host planner is also built as a standalone sanitizer-instrumented
-test driver when ``sanitize=True`` (CPU only, plain g++).
+root.  ``build_planner_sanitized`` builds the host planner into a standalone
+sanitizer-instrumented test driver (CPU only, plain g++).
 """
 from __future__ import annotations
 
@@ -70,10 +70,11 @@ def build(verbose: bool = False) -> str:
 
 
 def build_planner_sanitized(out: str) -> str:
-    """Host-only planner test driver with ASan/UBSan (g++, no GPU code)."""
-    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-omit-frame-pointer",
-           "-I", CSRC, os.path.join(CSRC, "planner.cpp"),
-           os.path.join(ROOT, "tests", "planner_driver.cpp"), "-o", out]
+    """Host-only planner test driver (tests/native/planner_driver.cpp) with
+    AddressSanitizer and UndefinedBehaviorSanitizer: plain g++, no GPU code."""
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-fno-omit-frame-pointer", "-I", CSRC, os.path.join(CSRC, "planner.cpp"),
+           os.path.join(ROOT, "tests", "native", "planner_driver.cpp"), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"sanitizer build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

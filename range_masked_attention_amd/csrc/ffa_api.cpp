@@ -34,6 +34,14 @@ bool debug_checks() {
   return s && *s && std::strcmp(s, "0") != 0;
 }
 
+// Fault injection for the error path: with FFA_INJECT_NOMEM set (to anything
+// but "0"), every host-side planning step fails as if the host allocator had
+// run out, so callers can test their FFA_ERR_NOMEM handling.
+void maybe_inject_nomem() {
+  const char* s = std::getenv("FFA_INJECT_NOMEM");
+  if (s && *s && std::strcmp(s, "0") != 0) throw std::bad_alloc();
+}
+
 // ---------------------------------------------------------------- validation
 std::string check_sizes(int64_t Tq, int64_t Tk) {
   if (Tq < 0 || Tk < 0) return "Tq and Tk must be >= 0";
@@ -218,6 +226,7 @@ int plan_create(int64_t Tq, int64_t Tk, const int32_t* qr, const int32_t* kr, co
   for (size_t i = 0; i < slices.size(); ++i) p->slice_index[i] = slices[i].r;
   std::vector<unsigned char> img;
   try {
+    maybe_inject_nomem();
     img.resize(align16((slices.size() + 1) * sizeof(ffa::HostDevSlice)), 0);
     auto* sl = reinterpret_cast<ffa::HostDevSlice*>(img.data());
     for (size_t i = 0; i < slices.size(); ++i)
@@ -445,6 +454,7 @@ int64_t ffa_plan_host(int64_t Tq, int64_t Tk, const int32_t* q_ranges, const int
   if (!m.empty()) return fail(FFA_ERR_INVALID_ARG, m);
   ffa::Plan plan;
   try {
+    maybe_inject_nomem();
     ffa::build_plan(slices, Tq, Tk, bm, bn, transpose != 0, &plan);
   } catch (const std::bad_alloc&) {
     return fail(FFA_ERR_NOMEM, "out of host memory while planning");
@@ -471,6 +481,7 @@ int64_t ffa_block_slices(int64_t Tq, int64_t Tk, int block_q, int block_k, const
   if (!m.empty()) return fail(FFA_ERR_INVALID_ARG, m);
   std::vector<ffa::RangePair> sl;
   try {
+    maybe_inject_nomem();
     m = ffa::block_slices(Tq, Tk, block_q, block_k, kv_num_blocks, kv_indices, max_blocks, &sl);
   } catch (const std::bad_alloc&) {
     return fail(FFA_ERR_NOMEM, "out of host memory while converting blocks");

@@ -28,3 +28,27 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """Write the parity record of the GPU comparisons made in this session
+    (nothing when none ran) to $FFA_PARITY_RECORD, by default
+    gpurun_out/parity_record.json under the repository root."""
+    gu = sys.modules.get("gpu_util")
+    rec = getattr(gu, "PARITY", None) if gu is not None else None
+    if not rec:
+        return
+    import json
+    import platform
+
+    path = os.environ.get("FFA_PARITY_RECORD", os.path.join(ROOT, "gpurun_out", "parity_record.json"))
+    os.makedirs(os.path.dirname(path) or ".", exist_ok=True)
+    worst = {}
+    for r in rec:
+        k = r["output"]
+        if k not in worst or r["max_abs"] > worst[k]["max_abs"]:
+            worst[k] = r
+    doc = {"host": platform.node(), "exitstatus": int(exitstatus), "n_comparisons": len(rec),
+           "worst_per_output": worst, "comparisons": rec}
+    with open(path, "w") as f:
+        json.dump(doc, f, indent=1)

@@ -138,3 +138,22 @@ def test_alibi_slopes_validation(lib):
     rc = lib.ffa_bwd_ex(64, 64, 64, 64, 64, 64, 4, 4, 2, 2, 64, ip(qr), ip(kr), ip(ty), 1,
                         0.1, 0.0, 66, 64, 64, 64, None, 0, None)
     assert rc == -1 and "alibi_slopes" in ffa.ffa_last_error()
+
+
+def test_injected_host_allocation_failure_is_nomem(lib, monkeypatch):
+    """FFA_INJECT_NOMEM makes every host planning step fail as if memory ran
+    out: the calls return FFA_ERR_NOMEM with a message, and work again once
+    it is cleared."""
+    qr, kr, ty = [[0, 100]], [[0, 100]], [1]
+    monkeypatch.setenv("FFA_INJECT_NOMEM", "1")
+    with pytest.raises(ffa.FfaError, match="host memory") as e:
+        ffa.ffa_plan_host(100, 100, qr, kr, ty, 64, 64)
+    assert e.value.code == -4
+    with pytest.raises(ffa.FfaError, match="host memory") as e:
+        ffa.ffa_block_slices([1, 1], [[0], [1]], 128, 128, 64, 64)
+    assert e.value.code == -4
+    monkeypatch.setenv("FFA_INJECT_NOMEM", "0")
+    rp, ent, order = ffa.ffa_plan_host(100, 100, qr, kr, ty, 64, 64)
+    assert len(ent) == 3
+    qs, ks, ts = ffa.ffa_block_slices([1, 1], [[0], [1]], 128, 128, 64, 64)
+    assert len(ts) == 2

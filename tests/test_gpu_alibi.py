@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_util import GRAD_TOL_ABS, GRAD_TOL_REL, O, compare_out_lse, dev, ffa, say, to64
+from gpu_util import O, check_grad, compare_out_lse, dev, ffa, say, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -22,13 +22,7 @@ def _slopes(rng, hq, kind):
 
 
 def _cmp(name, got, ref, ctx, mag):
-    got = got.double().cpu().numpy()
-    if not got.size:
-        return 0.0
-    diff = np.abs(got - ref)
-    excess = float((diff - GRAD_TOL_ABS - GRAD_TOL_REL * (np.abs(ref) + mag)).max())
-    assert excess <= 0.0, f"{ctx}: {name} max-abs {float(diff.max())}"
-    return float(diff.max())
+    return check_grad(name, got, ref, ctx, mag)
 
 
 CASES = [

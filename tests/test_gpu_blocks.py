@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import workloads as W
-from gpu_util import GRAD_TOL_ABS, GRAD_TOL_REL, O, compare_out_lse, dev, ffa, say, to64
+from gpu_util import O, check_grad, compare_out_lse, dev, ffa, say, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -61,11 +61,6 @@ def test_block_list_fwd_bwd(case):
     pqr, pkr, pty = O.block_slices_plain(num, idx, blk, blk, T, T)
     rq, rk, rv, mags = O.attention_bwd(to64(q), to64(k), to64(v), to64(do), pqr, pkr, pty, scale, cap,
                                        magnitudes=True)
-    errs = []
-    for (n, g, r), m in zip((("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)), mags):
-        got = g.double().cpu().numpy()
-        diff = np.abs(got - r)
-        assert float((diff - GRAD_TOL_ABS - GRAD_TOL_REL * (np.abs(r) + m)).max()) <= 0.0, \
-            f"{case}: {n} max-abs {float(diff.max())}"
-        errs.append(float(diff.max()))
+    errs = [check_grad(n, g, r, str(case), m)
+            for (n, g, r), m in zip((("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)), mags)]
     say(f"  {qr.shape[0]} slices; out {e_out:.3e} lse {e_lse:.3e} dq/dk/dv {errs[0]:.3e} {errs[1]:.3e} {errs[2]:.3e}")

@@ -1,8 +1,8 @@
 """Forward parity: the HIP path (through the C ABI) against the fp64 oracle.
 
-Small configurations are compared element by element over the whole output;
-the full-size configurations on sampled rows (the oracle computes those rows
-one block at a time) plus properties that hold at any size.
+Configurations 1-3 (up to 16384 tokens) are compared element by element over
+the whole output; the two largest on sampled rows (the oracle computes those
+rows one block at a time) plus properties that hold at any size.
 """
 import numpy as np
 import pytest
@@ -15,7 +15,7 @@ from gpu_util import (LSE_TOL, OUT_TOL, O, compare_out_lse, dev, ffa, run_fwd, s
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("n", [1, 2])
+@pytest.mark.parametrize("n", [1, 2, 3])
 def test_config_full_compare(n):
     w = W.config(n)
     say(f"fwd full compare config {n} ({w.name})")
@@ -27,7 +27,7 @@ def test_config_full_compare(n):
     say(f"  out max-abs {e_out:.3e}  lse max-abs {e_lse:.3e}")
 
 
-@pytest.mark.parametrize("n", [3, 4, 5])
+@pytest.mark.parametrize("n", [4, 5])
 def test_config_sampled_rows(n):
     w = W.config(n)
     say(f"fwd sampled-row compare config {n} ({w.name}) at full size")

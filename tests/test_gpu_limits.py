@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import GRAD_TOL_ABS, GRAD_TOL_REL, O, compare_out_lse, dev, ffa, say, to64
+from gpu_util import O, check_grad, compare_out_lse, dev, ffa, say, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -52,9 +52,7 @@ def test_keys_at_the_element_limit():
                                        magnitudes=True)
     sel = torch.from_numpy(keys).to(dv_)
     for n, got, ref, m in (("dq", dq, rq, mags[0]), ("dk", dk[sel], rk, mags[1]), ("dv", dv[sel], rv, mags[2])):
-        diff = np.abs(got.double().cpu().numpy() - ref)
-        assert float((diff - GRAD_TOL_ABS - GRAD_TOL_REL * (np.abs(ref) + m)).max()) <= 0.0, \
-            f"limits: {n} max-abs {float(diff.max())}"
+        check_grad(n, got, ref, "limits", m)
     # every other key: exactly zero gradient
     for t in (dk, dv):
         t[sel] = 0

@@ -338,6 +338,66 @@ def test_backward_sampled_matches_full():
     np.testing.assert_allclose(sv, dv[keys], rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("cap", [0.0, 2.0])
+def test_kv_head_subset_matches_autograd_on_those_heads(cap):
+    """kv_heads=[g] computes only kv head g and the q heads reading it: the
+    same numbers torch autograd gives on a problem that has only those heads
+    (dk, dv of g sum over exactly those q heads), and the same as the rows of
+    the all-heads result."""
+    rng = np.random.default_rng(19)
+    Tq, Tk, hq, hkv, d = 40, 52, 6, 3, 8
+    grp = hq // hkv
+    qr, kr, ty = W.random_slices(rng, Tq, Tk, max_slices=5, n_dummies=1)
+    q, k, v = _rand((Tq, hq, d), rng), _rand((Tk, hkv, d), rng), _rand((Tk, hkv, d), rng)
+    do = _rand((Tq, hq, d), rng)
+    g = 1
+    hs = list(range(g * grp, (g + 1) * grp))
+    out_s, lse_s = O.attention_fwd(q, k, v, qr, kr, ty, 0.45, cap, kv_heads=[g])
+    dq_s, dk_s, dv_s = O.attention_bwd(q, k, v, do, qr, kr, ty, 0.45, cap, kv_heads=[g])
+    assert out_s.shape == (Tq, grp, d) and dk_s.shape == (Tk, 1, d)
+    # against autograd on the sub-problem (q heads hs, kv head g alone)
+    vis = torch.from_numpy(O.visibility(O.normalise_slices(qr, kr, ty, Tq, Tk),
+                                        np.arange(Tq), np.arange(Tk)) > 0)
+    tq = torch.from_numpy(q[:, hs]).requires_grad_()
+    tk = torch.from_numpy(k[:, [g]]).requires_grad_()
+    tv = torch.from_numpy(v[:, [g]]).requires_grad_()
+    u = 0.45 * torch.einsum("ihc,jc->hij", tq, tk[:, 0])
+    sc = cap * torch.tanh(u / cap) if cap else u
+    sc = sc.masked_fill(~vis[None], float("-inf"))
+    has = vis.any(dim=1)
+    p = torch.softmax(torch.where(has[None, :, None], sc, torch.zeros_like(sc)), dim=-1)
+    p = torch.where(vis[None], p, torch.zeros_like(p))
+    out = torch.einsum("hij,jc->ihc", p, tv[:, 0])
+    np.testing.assert_allclose(out_s, out.detach().numpy(), rtol=1e-11, atol=1e-12)
+    (out * torch.from_numpy(do[:, hs])).sum().backward()
+    np.testing.assert_allclose(dq_s, tq.grad.numpy(), rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(dk_s, tk.grad.numpy(), rtol=1e-10, atol=1e-11)
+    np.testing.assert_allclose(dv_s, tv.grad.numpy(), rtol=1e-10, atol=1e-11)
+    # and the all-heads result restricted to those heads, bitwise
+    out_a, lse_a = O.attention_fwd(q, k, v, qr, kr, ty, 0.45, cap)
+    dq_a, dk_a, dv_a = O.attention_bwd(q, k, v, do, qr, kr, ty, 0.45, cap)
+    assert np.array_equal(out_s, out_a[:, hs]) and np.array_equal(lse_s, lse_a[:, hs])
+    assert np.array_equal(dq_s, dq_a[:, hs])
+    assert np.array_equal(dk_s, dk_a[:, [g]]) and np.array_equal(dv_s, dv_a[:, [g]])
+
+
+def test_visibility_skips_only_slices_that_add_nothing():
+    """The visibility matrix of a row/column window equals the window cut out
+    of the whole matrix, cell by cell against the brute-force rule."""
+    rng = np.random.default_rng(20)
+    T = 60
+    qr, kr, ty = W.random_slices(rng, T, T, max_slices=6, n_dummies=2)
+    sl = O.normalise_slices(qr, kr, ty, T, T)
+    full = O.visibility(sl, np.arange(T), np.arange(T))
+    for r0, r1, c0, c1 in ((0, 10, 0, 60), (17, 33, 5, 41), (50, 60, 50, 60), (30, 31, 0, 1)):
+        rows, cols = np.arange(r0, r1), np.arange(c0, c1)
+        win = O.visibility(sl, rows, cols)
+        assert np.array_equal(win, full[r0:r1, c0:c1])
+        for i in range(r0, r1):
+            for j in range(c0, c1):
+                assert bool(win[i - r0, j - c0]) == _brute_visible(i, j, qr, kr, ty)
+
+
 # ---------------------------------------------------------------- tile lists
 def _brute_tiles(qr, kr, ty, Tq, Tk, BM, BN):
     out = set()

@@ -54,10 +54,10 @@ def _check_structure(row_ptr, ent, order, qr, kr):
 @pytest.mark.parametrize("transpose", [False, True])
 def test_random_slices_match_oracle(transpose):
     rng = np.random.default_rng(100 + transpose)
-    for trial in range(60):
+    for trial in range(80):
         Tq, Tk = int(rng.integers(1, 300)), int(rng.integers(1, 300))
         qr, kr, ty = W.random_slices(rng, Tq, Tk, max_slices=6, n_dummies=int(rng.integers(0, 4)))
-        bm, bn = [(128, 64), (64, 64), (16, 32), (32, 16)][trial % 4]
+        bm, bn = [(128, 64), (64, 64), (16, 32), (32, 16), (64, 128)][trial % 5]
         got, row_ptr, ent, order = _plan_set(Tq, Tk, qr, kr, ty, bm, bn, transpose)
         assert got == O.tile_set(qr, kr, ty, Tq, Tk, bm, bn)
         _check_structure(row_ptr, ent, order, qr, kr)
@@ -67,7 +67,9 @@ def test_random_slices_match_oracle(transpose):
 def test_configs_match_oracle(n):
     w = W.config(n)
     qr, kr, ty = w.slices()
-    for bm, bn, tr in [(128, 64, False), (64, 64, True)]:
+    # (128, 64): the forward's and the dQ pass's q-tile lists; (64, 128,
+    # transposed): the dK/dV pass's key-tile lists, as the kernels use them
+    for bm, bn, tr in [(128, 64, False), (64, 64, True), (64, 128, True)]:
         got, *_ = _plan_set(w.Tq, w.Tk, qr, kr, ty, bm, bn, tr)
         assert got == O.tile_set(qr, kr, ty, w.Tq, w.Tk, bm, bn)
 
