@@ -147,6 +147,10 @@ def main():
     qd, kd, vd, od = q.to(dev), k.to(dev), v.to(dev), do.to(dev)
     out = torch.empty_like(qd)
     lse = torch.empty((w.Tq, w.hq), dtype=torch.float32, device=dev)
+    # a training step runs the training forward, which saves a record (out's
+    # rounding residual, v's fp16 copy) for the backward
+    saved = (torch.empty(ffa.ffa_saved_size(w.Tq, w.Tk, w.hq, w.hkv, w.d), dtype=torch.uint8, device=dev)
+             if do_bwd else None)
     dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
     ws = torch.empty(max(ffa.ffa_bwd_workspace_size(w.Tq, w.Tk, w.hq, w.hkv, w.d), 16), dtype=torch.uint8, device=dev)
     qr, kr, ty = w.slices()
@@ -172,12 +176,13 @@ def main():
         t_plan = time.perf_counter() - t_plan
         if events:
             events[0].record(stream)
-        ffa.ffa_fwd_planned(plan, qd, kd, vd, w.scale, w.softcap, out=out, lse=lse, alibi_slopes=slopes)
+        ffa.ffa_fwd_planned(plan, qd, kd, vd, w.scale, w.softcap, out=out, lse=lse, alibi_slopes=slopes,
+                            saved=saved)
         if events:
             events[1].record(stream)
         if do_bwd:
             ffa.ffa_bwd_planned(plan, qd, kd, vd, out, lse, od, w.scale, w.softcap,
-                                dq=dq, dk=dk, dv=dv, workspace=ws, alibi_slopes=slopes)
+                                dq=dq, dk=dk, dv=dv, workspace=ws, alibi_slopes=slopes, saved=saved)
             if events:
                 events[2].record(stream)
         ffa.ffa_plan_destroy(plan)
@@ -238,7 +243,8 @@ def main():
                         f"hq={w.hq} hkv={w.hkv} d={w.d} softcap={w.softcap}"
                         + (", ALiBi slopes" if args.alibi else ""),
             "tokens": w.Tq, "hq": w.hq, "hkv": w.hkv, "head_dim": w.d,
-            "visible_pairs": pairs, "step": "plan + fwd" + (" + bwd" if do_bwd else ""),
+            "visible_pairs": pairs,
+            "step": "plan + fwd" + (" (training forward, saved record) + bwd" if do_bwd else ""),
         },
         "fwd_ms": round(fwd_ms, 4),
         "fwd_frac_of_bf16_peak": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),

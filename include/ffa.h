@@ -95,8 +95,11 @@ int ffa_fwd(const void* q, const void* k, const void* v,
  * every query sees or a short query block against a long context): at most
  * 512 runs x kv heads of 128 keys x d x 2 (present when Tk > 0) plus 512
  * runs x q heads of 128 rows x d (present when Tq > 0), 96 MiB in all at
- * d = 128.  The contents need no initialisation and are scratch after the
- * call.
+ * d = 128; fp16 copies of q, k and dO (2 bytes per element each); and
+ * room for re-running the forward when no saved record is given (a record of
+ * ffa_saved_size bytes, out and lse).  At the 64K-token, 32/8-head, d = 128
+ * size that is about 2.3 GB.  The contents need no initialisation and are
+ * scratch after the call.
  */
 size_t ffa_bwd_workspace_size(int64_t Tq, int64_t Tk, int hq, int hkv, int d);
 
@@ -111,6 +114,16 @@ size_t ffa_bwd_workspace_size(int64_t Tq, int64_t Tk, int hq, int hkv, int d);
  * ffa_bwd_workspace_size(Tq, Tk, hq, hkv, d) bytes (or NULL: then the
  * library allocates it on `stream`).  Deterministic: the same inputs give
  * the same bits, whatever the order in which workgroups run.
+ *
+ * Precision.  The products run on the matrix cores with fp16 operands
+ * (11 significant bits) and fp32 accumulation: q, k, v and dout are copied
+ * to fp16, each times the power of two that maps its largest |x| onto
+ * fp16's range (exact), and P and dS are rounded to fp16 for the second
+ * products.  The row term D = rowsum(dout * out) needs out more precisely
+ * than bf16 holds it: ffa_bwd (no saved record) re-runs the forward into the
+ * workspace in its training form (see ffa_fwd_ex, `saved`), which costs one
+ * forward pass; ffa_bwd_ex takes the record a training forward saved and
+ * skips that.
  */
 int ffa_bwd(const void* q, const void* k, const void* v,
             const void* out, const float* lse, const void* dout,
@@ -136,17 +149,40 @@ int ffa_bwd(const void* q, const void* k, const void* v,
  * lse includes the bias.  The bias is formed as slope * (j - i) in fp32 from
  * the exact integer j - i; where every visible key of a row is far from it
  * (|slope * (j - i)| in the thousands), lse itself is large and carries fp32
- * rounding of that size.  Errors as for the entry points without _ex.
+ * rounding of that size.
+ *
+ * Training forward (saved record).  A forward whose backward will follow
+ * can save what that backward needs:
+ *   saved         DEVICE memory of ffa_saved_size(Tq, Tk, hq, hkv, d) bytes,
+ *                 16-byte aligned, or NULL (the plain forward).  With it the
+ *                 forward first copies v to fp16 (times the power of two
+ *                 that maps its range onto fp16's: exact) into the record,
+ *                 runs P V with P in fp16 (11 significant bits, not bf16's
+ *                 8), and stores out's bf16 rounding residual bf16(x - out)
+ *                 for each fp32 result x; out and lse are written as usual
+ *                 (out may differ from the plain forward's in the last bit,
+ *                 being more accurate).
+ * The _ex backward takes the record (NULL: re-run the training forward to
+ * get one, see ffa_bwd) and forms D = rowsum(dout * (out + residual)) from
+ * it, reusing the fp16 v.  A record belongs to the q, k, v, slices, scale,
+ * softcap and slopes of its forward.  Errors as for the entry points without
+ * _ex.
  */
 int ffa_fwd_ex(const void* q, const void* k, const void* v,
                int64_t Tq, int64_t Tk, int hq, int hkv, int d,
                const int32_t* q_ranges, const int32_t* k_ranges,
                const int32_t* attn_type_map, int R,
                float scale, float softcap, const float* alibi_slopes,
-               void* out, float* lse, void* stream);
+               void* out, float* lse, void* saved, void* stream);
+
+/* Bytes of the training forward's saved record (0 for invalid sizes): a
+ * 256-byte header, out's residual (2 bytes per element of q) and the fp16
+ * copy of v (2 bytes per element of v), each 256-byte aligned. */
+size_t ffa_saved_size(int64_t Tq, int64_t Tk, int hq, int hkv, int d);
 
 int ffa_bwd_ex(const void* q, const void* k, const void* v,
-               const void* out, const float* lse, const void* dout,
+               const void* out, const float* lse, const void* saved,
+               const void* dout,
                int64_t Tq, int64_t Tk, int hq, int hkv, int d,
                const int32_t* q_ranges, const int32_t* k_ranges,
                const int32_t* attn_type_map, int R,
@@ -252,17 +288,21 @@ int ffa_bwd_planned(ffa_plan_t plan,
                     void* dq, void* dk, void* dv,
                     void* workspace, size_t workspace_bytes, void* stream);
 
-/* ffa_fwd_planned / ffa_bwd_planned with the distance bias of ffa_fwd_ex
- * (alibi_slopes: device, hq fp32 slopes, or NULL). */
+/* ffa_fwd_planned / ffa_bwd_planned with the distance bias and the saved
+ * record of ffa_fwd_ex / ffa_bwd_ex (alibi_slopes: device, hq fp32 slopes,
+ * or NULL; saved: device, ffa_saved_size bytes, or NULL).  Without a record
+ * the backward re-runs the forward on the plan (so it uses the plan's
+ * forward scratch: see ffa_plan_create). */
 int ffa_fwd_planned_ex(ffa_plan_t plan,
                        const void* q, const void* k, const void* v,
                        int hq, int hkv, int d, float scale, float softcap,
                        const float* alibi_slopes,
-                       void* out, float* lse, void* stream);
+                       void* out, float* lse, void* saved, void* stream);
 
 int ffa_bwd_planned_ex(ffa_plan_t plan,
                        const void* q, const void* k, const void* v,
-                       const void* out, const float* lse, const void* dout,
+                       const void* out, const float* lse, const void* saved,
+                       const void* dout,
                        int hq, int hkv, int d, float scale, float softcap,
                        const float* alibi_slopes,
                        void* dq, void* dk, void* dv,

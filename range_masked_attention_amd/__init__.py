@@ -30,7 +30,7 @@ __all__ = [
     "ffa_plan_create", "ffa_fwd_planned", "ffa_bwd_planned", "ffa_plan_destroy",
     "ffa_plan_device_workspace_size", "ffa_plan_create_device", "ffa_plan_refresh", "ffa_plan_status",
     "ffa_plan_export", "FFA_PLAN_BAD_SLICE", "FFA_PLAN_CAPACITY", "flex_flash_attn_func",
-    "alibi_geometric_slopes", "ffa_block_slices", "cached_plan", "clear_plan_cache", "ffa_fwd_ex", "ffa_bwd_ex", "ffa_fwd_planned_ex", "ffa_bwd_planned_ex",
+    "alibi_geometric_slopes", "ffa_block_slices", "cached_plan", "clear_plan_cache", "ffa_fwd_ex", "ffa_bwd_ex", "ffa_saved_size", "ffa_fwd_planned_ex", "ffa_bwd_planned_ex",
 ]
 
 FULL = 0
@@ -72,11 +72,13 @@ def load_library():
                             i32, f32, f32, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.ffa_bwd.restype = ctypes.c_int
     lib.ffa_fwd_ex.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, ip32, ip32, ip32, i32,
-                               f32, f32, vp, vp, vp, vp]
+                               f32, f32, vp, vp, vp, vp, vp]
     lib.ffa_fwd_ex.restype = ctypes.c_int
-    lib.ffa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, ip32, ip32, ip32,
+    lib.ffa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, ip32, ip32, ip32,
                                i32, f32, f32, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.ffa_bwd_ex.restype = ctypes.c_int
+    lib.ffa_saved_size.argtypes = [i64, i64, i32, i32, i32]
+    lib.ffa_saved_size.restype = ctypes.c_size_t
     lib.ffa_bwd_workspace_size.argtypes = [i64, i64, i32, i32, i32]
     lib.ffa_bwd_workspace_size.restype = ctypes.c_size_t
     lib.ffa_plan_host.argtypes = [i64, i64, ip32, ip32, ip32, i32, i32, i32, i32,
@@ -91,9 +93,9 @@ def load_library():
     lib.ffa_bwd_planned.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, f32,
                                     vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.ffa_bwd_planned.restype = ctypes.c_int
-    lib.ffa_fwd_planned_ex.argtypes = [vp, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp, vp, vp]
+    lib.ffa_fwd_planned_ex.argtypes = [vp, vp, vp, vp, i32, i32, i32, f32, f32, vp, vp, vp, vp, vp]
     lib.ffa_fwd_planned_ex.restype = ctypes.c_int
-    lib.ffa_bwd_planned_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, vp,
+    lib.ffa_bwd_planned_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, f32, f32, vp,
                                        vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.ffa_bwd_planned_ex.restype = ctypes.c_int
     lib.ffa_plan_destroy.argtypes = [vp, vp]
@@ -191,11 +193,33 @@ def _slopes_ptr(slopes, hq: int, device):
     return slopes.data_ptr()
 
 
-def ffa_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, scale: float, softcap: float = 0.0,
-            out=None, lse=None, alibi_slopes=None):
-    """C ABI ``ffa_fwd`` (``ffa_fwd_ex`` with ``alibi_slopes``) on torch tensors.
+def ffa_saved_size(Tq: int, Tk: int, hq: int, hkv: int, d: int) -> int:
+    """C ABI ``ffa_saved_size``: bytes of the training forward's saved record."""
+    return int(load_library().ffa_saved_size(Tq, Tk, hq, hkv, d))
 
-    Returns (out [Tq,hq,d] bf16, lse [Tq,hq] fp32).
+
+def _saved_tensor(saved, train, q, k):
+    """The saved record to use: the caller's uint8 tensor, a new one (train=True), or None."""
+    import torch
+    need = ffa_saved_size(q.shape[0], k.shape[0], q.shape[1], k.shape[1], q.shape[2])
+    if saved is None and train:
+        saved = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if saved is not None:
+        if not isinstance(saved, torch.Tensor) or saved.dtype != torch.uint8 or not saved.is_cuda \
+                or not saved.is_contiguous():
+            raise TypeError("saved must be a contiguous uint8 tensor on the GPU")
+        if saved.numel() < need:
+            raise ValueError(f"saved needs {need} bytes (ffa_saved_size), got {saved.numel()}")
+    return saved
+
+
+def ffa_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, scale: float, softcap: float = 0.0,
+            out=None, lse=None, alibi_slopes=None, saved=None, train: bool = False):
+    """C ABI ``ffa_fwd`` (``ffa_fwd_ex`` with ``alibi_slopes`` or a saved record) on torch tensors.
+
+    Returns (out [Tq,hq,d] bf16, lse [Tq,hq] fp32); with ``train=True`` or a
+    ``saved`` tensor (uint8, ``ffa_saved_size`` bytes) it runs the training
+    forward, which fills the record for ``ffa_bwd``, and returns it third.
     """
     import torch
     lib = load_library()
@@ -213,14 +237,19 @@ def ffa_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, scale: float, softcap: f
     _check_tensor("lse", lse, torch.float32, 2)
     if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (Tq, hq):
         raise ValueError("out must be shaped like q and lse [Tq, hq]")
+    saved = _saved_tensor(saved, train, q, k)
     qr, kr, ty = _host_slices(q_ranges, k_ranges, attn_type_map)
     sp = _slopes_ptr(alibi_slopes, hq, q.device)
     head = (q.data_ptr(), k.data_ptr(), v.data_ptr(), Tq, Tk, hq, hkv, d,
             _iptr(qr), _iptr(kr), _iptr(ty), qr.shape[0], float(scale), float(softcap))
-    tail = (out.data_ptr(), lse.data_ptr(), _stream_handle(q))
-    rc = lib.ffa_fwd(*head, *tail) if sp is None else lib.ffa_fwd_ex(*head, sp, *tail)
+    st = _stream_handle(q)
+    if sp is None and saved is None:
+        rc = lib.ffa_fwd(*head, out.data_ptr(), lse.data_ptr(), st)
+    else:
+        rc = lib.ffa_fwd_ex(*head, sp, out.data_ptr(), lse.data_ptr(),
+                            saved.data_ptr() if saved is not None else None, st)
     _check(rc)
-    return out, lse
+    return (out, lse) if saved is None else (out, lse, saved)
 
 
 def ffa_bwd_workspace_size(Tq: int, Tk: int, hq: int, hkv: int, d: int) -> int:
@@ -229,10 +258,13 @@ def ffa_bwd_workspace_size(Tq: int, Tk: int, hq: int, hkv: int, d: int) -> int:
 
 
 def ffa_bwd(q, k, v, out, lse, dout, q_ranges, k_ranges, attn_type_map, scale: float,
-            softcap: float = 0.0, dq=None, dk=None, dv=None, workspace=None, alibi_slopes=None):
-    """C ABI ``ffa_bwd`` (``ffa_bwd_ex`` with ``alibi_slopes``) on torch tensors.
+            softcap: float = 0.0, dq=None, dk=None, dv=None, workspace=None, alibi_slopes=None,
+            saved=None):
+    """C ABI ``ffa_bwd`` (``ffa_bwd_ex`` with ``alibi_slopes`` or ``saved``) on torch tensors.
 
-    Returns (dq, dk, dv) in bf16.
+    ``saved``: the record a training forward (``train=True``) filled; without
+    it the library re-runs the training forward to get one.  Returns (dq, dk,
+    dv) in bf16.
     """
     import torch
     lib = load_library()
@@ -255,13 +287,17 @@ def ffa_bwd(q, k, v, out, lse, dout, q_ranges, k_ranges, attn_type_map, scale: f
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    saved = _saved_tensor(saved, False, q, k)
     qr, kr, ty = _host_slices(q_ranges, k_ranges, attn_type_map)
     sp = _slopes_ptr(alibi_slopes, hq, q.device)
-    head = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-            dout.data_ptr(), Tq, Tk, hq, hkv, d, _iptr(qr), _iptr(kr), _iptr(ty),
-            qr.shape[0], float(scale), float(softcap))
+    sizes = (Tq, Tk, hq, hkv, d, _iptr(qr), _iptr(kr), _iptr(ty), qr.shape[0], float(scale), float(softcap))
     tail = (dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_len, _stream_handle(q))
-    rc = lib.ffa_bwd(*head, *tail) if sp is None else lib.ffa_bwd_ex(*head, sp, *tail)
+    qkv = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
+    if sp is None and saved is None:
+        rc = lib.ffa_bwd(*qkv, dout.data_ptr(), *sizes, *tail)
+    else:
+        rc = lib.ffa_bwd_ex(*qkv, saved.data_ptr() if saved is not None else None, dout.data_ptr(),
+                            *sizes, sp, *tail)
     _check(rc)
     return dq, dk, dv
 
@@ -491,8 +527,9 @@ def ffa_plan_export(plan, which: int, device=None):
 
 
 def ffa_fwd_planned(plan, q, k, v, scale: float, softcap: float = 0.0, out=None, lse=None,
-                    alibi_slopes=None):
-    """C ABI ``ffa_fwd_planned`` (``_ex`` with ``alibi_slopes``): the forward kernel alone."""
+                    alibi_slopes=None, saved=None, train: bool = False):
+    """C ABI ``ffa_fwd_planned`` (``_ex`` with ``alibi_slopes`` or a saved record): the
+    forward kernels alone.  Returns (out, lse), plus the record as in ``ffa_fwd``."""
     import torch
     lib = load_library()
     for nm, t in (("q", q), ("k", k), ("v", v)):
@@ -503,16 +540,22 @@ def ffa_fwd_planned(plan, q, k, v, scale: float, softcap: float = 0.0, out=None,
     lse = torch.empty((Tq, hq), dtype=torch.float32, device=q.device) if lse is None else lse
     _check_tensor("out", out, torch.bfloat16, 3)
     _check_tensor("lse", lse, torch.float32, 2)
+    saved = _saved_tensor(saved, train, q, k)
     sp = _slopes_ptr(alibi_slopes, hq, q.device)
     head = (plan, q.data_ptr(), k.data_ptr(), v.data_ptr(), hq, hkv, d, float(scale), float(softcap))
-    tail = (out.data_ptr(), lse.data_ptr(), _stream_handle(q))
-    _check(lib.ffa_fwd_planned(*head, *tail) if sp is None else lib.ffa_fwd_planned_ex(*head, sp, *tail))
-    return out, lse
+    st = _stream_handle(q)
+    if sp is None and saved is None:
+        _check(lib.ffa_fwd_planned(*head, out.data_ptr(), lse.data_ptr(), st))
+    else:
+        _check(lib.ffa_fwd_planned_ex(*head, sp, out.data_ptr(), lse.data_ptr(),
+                                      saved.data_ptr() if saved is not None else None, st))
+    return (out, lse) if saved is None else (out, lse, saved)
 
 
 def ffa_bwd_planned(plan, q, k, v, out, lse, dout, scale: float, softcap: float = 0.0,
-                    dq=None, dk=None, dv=None, workspace=None, alibi_slopes=None):
-    """C ABI ``ffa_bwd_planned`` (``_ex`` with ``alibi_slopes``): the backward kernels alone."""
+                    dq=None, dk=None, dv=None, workspace=None, alibi_slopes=None, saved=None):
+    """C ABI ``ffa_bwd_planned`` (``_ex`` with ``alibi_slopes`` or ``saved``): the
+    backward kernels alone (plus a training-forward re-run when ``saved`` is None)."""
     import torch
     lib = load_library()
     for nm, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
@@ -528,38 +571,47 @@ def ffa_bwd_planned(plan, q, k, v, out, lse, dout, scale: float, softcap: float 
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    saved = _saved_tensor(saved, False, q, k)
     sp = _slopes_ptr(alibi_slopes, hq, q.device)
-    head = (plan, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-            dout.data_ptr(), hq, hkv, d, float(scale), float(softcap))
+    qkv = (plan, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
+    sizes = (hq, hkv, d, float(scale), float(softcap))
     tail = (dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_len, _stream_handle(q))
-    _check(lib.ffa_bwd_planned(*head, *tail) if sp is None else lib.ffa_bwd_planned_ex(*head, sp, *tail))
+    if sp is None and saved is None:
+        _check(lib.ffa_bwd_planned(*qkv, dout.data_ptr(), *sizes, *tail))
+    else:
+        _check(lib.ffa_bwd_planned_ex(*qkv, saved.data_ptr() if saved is not None else None,
+                                      dout.data_ptr(), *sizes, sp, *tail))
     return dq, dk, dv
 
 
 def ffa_fwd_ex(q, k, v, q_ranges, k_ranges, attn_type_map, scale: float, softcap: float,
-               alibi_slopes, out=None, lse=None):
-    """C ABI ``ffa_fwd_ex``: ``ffa_fwd`` with a distance bias (``alibi_slopes``: fp32 [hq] or None)."""
+               alibi_slopes, out=None, lse=None, saved=None, train: bool = False):
+    """C ABI ``ffa_fwd_ex``: ``ffa_fwd`` with a distance bias (``alibi_slopes``: fp32 [hq] or None)
+    and the optional saved record."""
     return ffa_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, scale, softcap, out=out, lse=lse,
-                   alibi_slopes=alibi_slopes)
+                   alibi_slopes=alibi_slopes, saved=saved, train=train)
 
 
 def ffa_bwd_ex(q, k, v, out, lse, dout, q_ranges, k_ranges, attn_type_map, scale: float,
-               softcap: float, alibi_slopes, dq=None, dk=None, dv=None, workspace=None):
-    """C ABI ``ffa_bwd_ex``: ``ffa_bwd`` with a distance bias (``alibi_slopes``: fp32 [hq] or None)."""
+               softcap: float, alibi_slopes, dq=None, dk=None, dv=None, workspace=None, saved=None):
+    """C ABI ``ffa_bwd_ex``: ``ffa_bwd`` with a distance bias (``alibi_slopes``: fp32 [hq] or None)
+    and the training forward's ``saved`` record."""
     return ffa_bwd(q, k, v, out, lse, dout, q_ranges, k_ranges, attn_type_map, scale, softcap,
-                   dq=dq, dk=dk, dv=dv, workspace=workspace, alibi_slopes=alibi_slopes)
+                   dq=dq, dk=dk, dv=dv, workspace=workspace, alibi_slopes=alibi_slopes, saved=saved)
 
 
-def ffa_fwd_planned_ex(plan, q, k, v, scale: float, softcap: float, alibi_slopes, out=None, lse=None):
-    """C ABI ``ffa_fwd_planned_ex``: ``ffa_fwd_planned`` with a distance bias."""
-    return ffa_fwd_planned(plan, q, k, v, scale, softcap, out=out, lse=lse, alibi_slopes=alibi_slopes)
+def ffa_fwd_planned_ex(plan, q, k, v, scale: float, softcap: float, alibi_slopes, out=None, lse=None,
+                       saved=None, train: bool = False):
+    """C ABI ``ffa_fwd_planned_ex``: ``ffa_fwd_planned`` with a distance bias and the saved record."""
+    return ffa_fwd_planned(plan, q, k, v, scale, softcap, out=out, lse=lse, alibi_slopes=alibi_slopes,
+                           saved=saved, train=train)
 
 
 def ffa_bwd_planned_ex(plan, q, k, v, out, lse, dout, scale: float, softcap: float, alibi_slopes,
-                       dq=None, dk=None, dv=None, workspace=None):
-    """C ABI ``ffa_bwd_planned_ex``: ``ffa_bwd_planned`` with a distance bias."""
+                       dq=None, dk=None, dv=None, workspace=None, saved=None):
+    """C ABI ``ffa_bwd_planned_ex``: ``ffa_bwd_planned`` with a distance bias and the saved record."""
     return ffa_bwd_planned(plan, q, k, v, out, lse, dout, scale, softcap, dq=dq, dk=dk, dv=dv,
-                           workspace=workspace, alibi_slopes=alibi_slopes)
+                           workspace=workspace, alibi_slopes=alibi_slopes, saved=saved)
 
 
 def flex_flash_attn_func(q, k, v, q_ranges, k_ranges, attn_type_map,
@@ -587,9 +639,13 @@ def flex_flash_attn_func(q, k, v, q_ranges, k_ranges, attn_type_map,
 
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(q.shape[-1])
-    return torch.ops.ffa_amd.fwd(q, k, v, as_tensor(q_ranges), as_tensor(k_ranges),
-                                 as_tensor(attn_type_map), float(softmax_scale), float(softcap),
-                                 alibi_slopes)
+    # the training forward (which saves a record for the backward) when a
+    # backward may follow
+    train = torch.is_grad_enabled() and any(t.requires_grad for t in (q, k, v))
+    out, lse, _ = torch.ops.ffa_amd.fwd(q, k, v, as_tensor(q_ranges), as_tensor(k_ranges),
+                                        as_tensor(attn_type_map), float(softmax_scale), float(softcap),
+                                        alibi_slopes, train)
+    return out, lse
 
 
 # Register the custom operators (ffa_amd::fwd, ffa_amd::bwd) on import, so

@@ -13,8 +13,13 @@
 // varlen backward design open (CUTLASS issue #2192); this one is built for
 // the slice plan:
 //
-//  bwd_pre   D for every (row, q head), and lse in exp2 units, both stored
-//            head-major ([hq][Tq]) so that a step's 64 rows are contiguous.
+//  bwd_prep  (after the range pass of convert.hip over q, k and dO)
+//            fp16 copies of q and dO, each times the power of two that maps
+//            its range onto fp16's (k's comes from convert.hip, v's with the
+//            record the training forward saved); D for every (row, q head)
+//            from dO and the forward's output with its rounding residual,
+//            and lse in exp2 units, both stored head-major ([hq][Tq]) so
+//            that a step's 64 rows are contiguous.
 //  bwd_dkdv  one workgroup per (128-key tile, kv head); its 4 wave pairs own
 //            32 keys each and walk the key-side plan (64-row q tiles) for
 //            every q head of the group, accumulating dK^T and dV^T in
@@ -27,6 +32,16 @@
 // of being scattered with atomics: no contention, and the result does not
 // depend on the order in which workgroups finish.
 //
+// Precision: the products run on fp16 operands (11 significant bits; bf16
+// has 8) at the same matrix-core rate, so P and dS enter them with 2^-11
+// relative rounding instead of 2^-8.  The fp16 copies of q, k, v and dO are
+// exact (bf16 values times a power of two, inside fp16's normal range up to
+// values below 2^-14 of the largest, which round at 2^-25 of it), and the
+// powers of two come back out exactly in the score multiplier and the final
+// scaling of dq, dk and dv.  D is formed from out plus its rounding
+// residual, from a forward whose P V product also ran in fp16, so it carries
+// neither out's bf16 rounding nor a bf16 rounding of P.
+//
 // Tiles of 64 rows are fetched straight into LDS (buffer_load ... lds), one
 // load instruction per 16-byte chunk column: LDS holds a tile column-major by
 // chunk, 64 rows x 16 bytes per column plus 64 bytes of padding.  Row-wise
@@ -34,6 +49,7 @@
 // operands come from transpose reads (ds_read_b64_tr_b16) hitting 4 columns
 // 16 banks apart: neither conflicts on the 64 LDS banks.  Tiles are double
 // buffered, with one barrier per step.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -45,37 +61,56 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// ---------------------------------------------------------------- bwd_pre
-// Thread r takes (row r / hq, head r % hq), so that a workgroup reads a run
-// of whole rows of out and dO; the two results go to their head-major
-// places (small writes: 8 bytes per row and head).  lse2 is lse in exp2
-// units with -inf (a row that sees nothing) turned into +inf, so that
-// exp2(s - lse2) is 0 there rather than NaN.
+// ---------------------------------------------------------------- bwd_prep
+// D * sdo * sv for every (row, head), lse in exp2 units, and the fp16 copies
+// of q and dO (convert.hip's scaling).  D / 8 lanes per (row, head), one
+// 16-byte chunk each, so a wave reads whole rows; lse2 turns -inf (a row that
+// sees nothing) into +inf, so that exp2(s - lse2) is 0 there rather than NaN.
+// D = rowsum(dO * (out + out_lo)) in fp32, out_lo being the rounding
+// residual the training forward saved.  Thread 0 also writes the four scales
+// [q, k, v, dO] for the kernels after it.
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(const __bf16* __restrict__ out,
-                                                          const __bf16* __restrict__ dout,
-                                                          const float* __restrict__ lse,
-                                                          float* __restrict__ dvec, float* __restrict__ lse2,
+__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const u32x4* __restrict__ q, const u32x4* __restrict__ out,
+                                                          const u32x4* __restrict__ out_lo,
+                                                          const u32x4* __restrict__ dout, const float* __restrict__ lse,
+                                                          const uint32_t* __restrict__ range,
+                                                          const uint32_t* __restrict__ vwords, u32x4* __restrict__ q16,
+                                                          u32x4* __restrict__ do16, float* __restrict__ dvec,
+                                                          float* __restrict__ lse2, float* __restrict__ scales,
                                                           int64_t Tq, int hq) {
-  const int64_t r = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (r >= Tq * hq) return;
-  const int64_t row = r / hq, head = r - row * hq;
-  const int64_t t = head * Tq + row;
-  const u32x4* po = reinterpret_cast<const u32x4*>(out + r * D);
-  const u32x4* pd = reinterpret_cast<const u32x4*>(dout + r * D);
+  constexpr int kL = D / 8;  // lanes per (row, head)
+  const float sq = range_scale(range[kRgQ], kRangeQ), sk = range_scale(range[kRgK], kRangeK);
+  const float sv = range_scale(vwords[kRgV], kRangeV), sdo = range_scale(range[kRgDO], kRangeDO);
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i == 0) {
+    scales[kRgQ] = sq;
+    scales[kRgK] = sk;
+    scales[kRgV] = sv;
+    scales[kRgDO] = sdo;
+  }
+  const int64_t r = i / kL;  // (row, head) = (r / hq, r % hq)
+  const bool live = r < Tq * hq;
   float acc = 0.f;
-#pragma unroll
-  for (int c = 0; c < D / 8; ++c) {
-    const u32x4 a = po[c], b = pd[c];
+  if (live) {
+    const u32x4 a = out[i], b = out_lo[i], g = dout[i];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      acc += __uint_as_float(a[j] << 16) * __uint_as_float(b[j] << 16);
-      acc += __uint_as_float(a[j] & 0xFFFF0000u) * __uint_as_float(b[j] & 0xFFFF0000u);
+      const float d0 = __uint_as_float(g[j] << 16), d1 = __uint_as_float(g[j] & 0xFFFF0000u);
+      acc += d0 * (__uint_as_float(a[j] << 16) + __uint_as_float(b[j] << 16));
+      acc += d1 * (__uint_as_float(a[j] & 0xFFFF0000u) + __uint_as_float(b[j] & 0xFFFF0000u));
     }
+    q16[i] = to_f16x8(q[i], sq);
+    do16[i] = to_f16x8(g, sdo);
   }
-  dvec[t] = acc;
-  const float l = lse[r];
-  lse2[t] = (l == -INFINITY) ? INFINITY : l * 1.4426950408889634f;
+#pragma unroll
+  for (int o = 1; o < kL; o <<= 1) acc += __shfl_xor(acc, o);
+  if (live && (i % kL) == 0) {
+    const int64_t row = r / hq, head = r - row * hq;
+    const int64_t t = head * Tq + row;
+    dvec[t] = acc * sdo * sv;
+    const float l = lse[r];
+    lse2[t] = (l == -INFINITY) ? INFINITY : l * 1.4426950408889634f;
+  }
 }
 
 // Row range of slice `sl` that key j sees: [lo, hi) (empty if hi <= lo).
@@ -94,11 +129,15 @@ __device__ __forceinline__ void row_keys(const DevSlice& sl, int i, int* lo, int
   if (i < sl.qs || i >= sl.qe) *hi = *lo;
 }
 
+// q, k, v and dout point at the fp16 copies (16-bit lanes carried in bf16
+// vector types; the fp16 products read them as fp16); `scales` holds their
+// powers of two, [q, k, v, dO].
 struct BwdArgs {
   const __bf16* q;
   const __bf16* k;
   const __bf16* v;
   const __bf16* dout;
+  const float* scales;
   const float* lse;
   const float* dvec;        // D, head-major [hq][Tq]
   const float* lse2;        // lse in exp2 units (+inf: nothing visible), head-major
@@ -139,8 +178,21 @@ __device__ __forceinline__ float score_to_t(const BwdArgs& a, float s, float* th
 __device__ __forceinline__ u32x4 pack8(const float* p) {
   u32x4 w;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);
+  for (int i = 0; i < 4; ++i) w[i] = pack_f16x2(p[2 * i], p[2 * i + 1]);
   return w;
+}
+
+// The operand scales folded into the score multipliers: s' = sq sk s, so
+// the multipliers that turn raw scores into exponent (or tanh) units take
+// 1 / (sq sk).  Powers of two: exact.
+__device__ __forceinline__ void fold_scales(BwdArgs* a, float* sq, float* sk, float* sv, float* sdo) {
+  *sq = const_load<float>(a->scales, 0);
+  *sk = const_load<float>(a->scales, 1);
+  *sv = const_load<float>(a->scales, 2);
+  *sdo = const_load<float>(a->scales, 3);
+  const float inv = 1.0f / (*sq * *sk);
+  a->score_mult *= inv;
+  a->cap_in *= inv;
 }
 
 // ---------------------------------------------------------------- bwd_dkdv
@@ -165,8 +217,11 @@ template <int R>
 using IC = std::integral_constant<int, R>;
 
 template <int D, bool SOFTCAP, bool BIAS>
-__global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a0) {
   using T = ColTile<D>;
+  BwdArgs a = a0;
+  float sq, sk, sv, sdo;
+  fold_scales(&a, &sq, &sk, &sv, &sdo);
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int kXchg = kDkvRows * 32;  // fp32 P of one pair and step (floats)
   __shared__ __attribute__((aligned(1024))) char q_s0[T::kBytes];
@@ -313,7 +368,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) s[qb] = mfma_32x32x16(T::row8(qt, 0, 32 * qb, 2 * ks), frag[ks], s[qb]);
+        for (int qb = 0; qb < 2; ++qb) s[qb] = mfma_32x32x16_f16(T::row8(qt, 0, 32 * qb, 2 * ks), frag[ks], s[qb]);
       // P; element (qb, v) is row 32qb + 8(v/4) + 4hh + v%4, key `key`
       // the per-cell mask only on PARTIAL entries (a FULL entry has every
       // cell visible, tails included), chosen once per step
@@ -346,8 +401,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
               px[i] = SOFTCAP ? p * (1.0f - th * th) : p;
             }
             *reinterpret_cast<f32x4*>(xch + ((qb * 4 + v4) * 64 + lane) * 4) = px;
-            pw[2 * qb + (v4 >> 1)][2 * (v4 & 1)] = pack_bf16x2(p4[0], p4[1]);
-            pw[2 * qb + (v4 >> 1)][2 * (v4 & 1) + 1] = pack_bf16x2(p4[2], p4[3]);
+            pw[2 * qb + (v4 >> 1)][2 * (v4 & 1)] = pack_f16x2(p4[0], p4[1]);
+            pw[2 * qb + (v4 >> 1)][2 * (v4 & 1) + 1] = pack_f16x2(p4[2], p4[3]);
           }
       };
       if (ent.meta & 1)
@@ -359,7 +414,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          acc[db] = mfma_32x32x16(tr8<D>(ot, 0, db, t4), __builtin_bit_cast(bf16x8, pw[t4]), acc[db]);
+          acc[db] = mfma_32x32x16_f16(tr8<D>(ot, 0, db, t4), __builtin_bit_cast(bf16x8, pw[t4]), acc[db]);
       if (st + 1 < n_steps) publish((st + 1) % 3);
     }
     dma_barrier();
@@ -384,15 +439,15 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
           float ds[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) ds[i] = px[i] * (dp[qb][4 * v4 + i] - d4[i]);
-          dw[2 * qb + (v4 >> 1)][2 * (v4 & 1)] = pack_bf16x2(ds[0], ds[1]);
-          dw[2 * qb + (v4 >> 1)][2 * (v4 & 1) + 1] = pack_bf16x2(ds[2], ds[3]);
+          dw[2 * qb + (v4 >> 1)][2 * (v4 & 1)] = pack_f16x2(ds[0], ds[1]);
+          dw[2 * qb + (v4 >> 1)][2 * (v4 & 1) + 1] = pack_f16x2(ds[2], ds[3]);
         }
       // dK^T += Q^T dS
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          acc[db] = mfma_32x32x16(tr8<D>(qt, 0, db, t4), __builtin_bit_cast(bf16x8, dw[t4]), acc[db]);
+          acc[db] = mfma_32x32x16_f16(tr8<D>(qt, 0, db, t4), __builtin_bit_cast(bf16x8, dw[t4]), acc[db]);
     }
     if (st < n_steps) {
       const char* ot = ob2[R % 2];  // rows of dO
@@ -403,7 +458,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) dp[qb] = mfma_32x32x16(T::row8(ot, 0, 32 * qb, 2 * ks), frag[ks], dp[qb]);
+        for (int qb = 0; qb < 2; ++qb) dp[qb] = mfma_32x32x16_f16(T::row8(ot, 0, 32 * qb, 2 * ks), frag[ks], dp[qb]);
     }
     dma_barrier();
   };
@@ -473,7 +528,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
   } else if (key < a.Tk) {
     const int64_t off = ((int64_t)key * a.hkv + g) * D;
     __bf16* dst = producer ? a.dv : a.dk;
-    const float mul = producer ? 1.0f : a.scale;
+    // dV^T accumulated sdo dV; dK^T accumulated sdo sv sq dK / scale
+    const float mul = producer ? 1.0f / sdo : a.scale / (sdo * sv * sq);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -501,7 +557,10 @@ constexpr int kDkvMaxSlots = 512;  // partial buffers: runs of split tiles x kv 
 // Sum of the partial dK^T / dV^T of a split tile's runs, in run order, to
 // bf16 dK (times the softmax scale) and dV.
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_reduce_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_reduce_kernel(BwdArgs a0) {
+  BwdArgs a = a0;
+  float sq, sk, sv, sdo;
+  fold_scales(&a, &sq, &sk, &sv, &sdo);
   const int u = blockIdx.x;
   const int s = u / a.hkv, g = u % a.hkv;
   if (s >= plan_i32(a.counts, 1)) return;
@@ -516,7 +575,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_reduce_kernel(BwdArgs a) {
     const int r = is_v ? i - kDkvKeys * D : i;
     const int key = kt * kDkvKeys + r / D, dim = r % D;
     if (key < a.Tk) {
-      const float mul = is_v ? 1.0f : a.scale;
+      const float mul = is_v ? 1.0f / sdo : a.scale / (sdo * sv * sq);
       u32x2 w;
       w[0] = pack_bf16x2(mul * sum[0], mul * sum[1]);
       w[1] = pack_bf16x2(mul * sum[2], mul * sum[3]);
@@ -539,8 +598,13 @@ constexpr int kDqMinSteps = 64;
 constexpr int kDqMaxSlots = 512;  // partial buffers: runs of split tiles x q heads
 
 template <int D, bool SOFTCAP, bool BIAS>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a0) {
   using T = ColTile<D>;
+  BwdArgs a = a0;
+  float sq, sk, sv, sdo;
+  fold_scales(&a, &sq, &sk, &sv, &sdo);
+  // dQ^T accumulates sdo sv sk dQ / scale
+  const float out_mul = a.scale / (sdo * sv * sk);
   constexpr int KS = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(1024))) char k_s0[T::kBytes];
   __shared__ __attribute__((aligned(1024))) char k_s1[T::kBytes];
@@ -627,8 +691,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
       dp[kb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        s[kb] = mfma_32x32x16(T::row8(kt, lrow, 32 * kb, 2 * ks), qf[ks], s[kb]);
-        dp[kb] = mfma_32x32x16(T::row8(vt, lrow, 32 * kb, 2 * ks), of[ks], dp[kb]);
+        s[kb] = mfma_32x32x16_f16(T::row8(kt, lrow, 32 * kb, 2 * ks), qf[ks], s[kb]);
+        dp[kb] = mfma_32x32x16_f16(T::row8(vt, lrow, 32 * kb, 2 * ks), of[ks], dp[kb]);
       }
     }
 
@@ -677,7 +741,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4)
-        acc[db] = mfma_32x32x16(tr8<D>(kt, tro, db, t4), __builtin_bit_cast(bf16x8, dw[t4]), acc[db]);
+        acc[db] = mfma_32x32x16_f16(tr8<D>(kt, tro, db, t4), __builtin_bit_cast(bf16x8, dw[t4]), acc[db]);
 
     dma_barrier();
   };
@@ -704,10 +768,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         f32x4 x;
-        x[0] = a.scale * acc[db][4 * j + 0];
-        x[1] = a.scale * acc[db][4 * j + 1];
-        x[2] = a.scale * acc[db][4 * j + 2];
-        x[3] = a.scale * acc[db][4 * j + 3];
+        x[0] = out_mul * acc[db][4 * j + 0];
+        x[1] = out_mul * acc[db][4 * j + 1];
+        x[2] = out_mul * acc[db][4 * j + 2];
+        x[3] = out_mul * acc[db][4 * j + 3];
         *reinterpret_cast<f32x4*>(prow + 32 * db + 8 * j + 4 * hh) = x;
       }
   } else if (row < a.Tq) {
@@ -717,8 +781,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         u32x2 w2;
-        w2[0] = pack_bf16x2(a.scale * acc[db][4 * j + 0], a.scale * acc[db][4 * j + 1]);
-        w2[1] = pack_bf16x2(a.scale * acc[db][4 * j + 2], a.scale * acc[db][4 * j + 3]);
+        w2[0] = pack_bf16x2(out_mul * acc[db][4 * j + 0], out_mul * acc[db][4 * j + 1]);
+        w2[1] = pack_bf16x2(out_mul * acc[db][4 * j + 2], out_mul * acc[db][4 * j + 3]);
         *reinterpret_cast<u32x2*>(drow + 32 * db + 8 * j + 4 * hh) = w2;
       }
   }
@@ -745,11 +809,13 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_reduce_kernel(BwdArgs a) {
   }
 }
 
-void fill_args(const BwdLaunch& p, BwdArgs* a) {
-  a->q = static_cast<const __bf16*>(p.q);
-  a->k = static_cast<const __bf16*>(p.k);
-  a->v = static_cast<const __bf16*>(p.v);
-  a->dout = static_cast<const __bf16*>(p.dout);
+void fill_args(const BwdLaunch& p, const BwdWorkspaceLayout& L, BwdArgs* a) {
+  unsigned char* ws = static_cast<unsigned char*>(p.workspace);
+  a->q = reinterpret_cast<const __bf16*>(ws + L.q16);
+  a->k = reinterpret_cast<const __bf16*>(ws + L.k16);
+  a->v = nullptr;  // the saved record's fp16 copy of v, set by the launch
+  a->dout = reinterpret_cast<const __bf16*>(ws + L.do16);
+  a->scales = reinterpret_cast<const float*>(ws + L.range + 16);
   a->lse = p.lse;
   a->dq = static_cast<__bf16*>(p.dq);
   a->dk = static_cast<__bf16*>(p.dk);
@@ -778,7 +844,7 @@ hipError_t launch_bwd_t(const BwdLaunch& p, hipStream_t stream) {
   unsigned char* ws = static_cast<unsigned char*>(p.workspace);
   const int64_t rows = p.Tq * p.hq;
   BwdArgs a;
-  fill_args(p, &a);
+  fill_args(p, L, &a);
   float* dvec = reinterpret_cast<float*>(ws + L.dvec);
   float* lse2 = reinterpret_cast<float*>(ws + L.lse2);
   a.dvec = dvec;
@@ -788,10 +854,38 @@ hipError_t launch_bwd_t(const BwdLaunch& p, hipStream_t stream) {
   a.splits = reinterpret_cast<const i32x4*>(ws + L.splits);
   a.partial = reinterpret_cast<float*>(ws + L.partial);
   a.slopes = p.alibi_slopes;
-  if (rows > 0)
-    hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)((rows + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, stream, static_cast<const __bf16*>(p.out),
-                       static_cast<const __bf16*>(p.dout), p.lse, dvec, lse2, p.Tq, p.hq);
+  // ranges of q, k, dO (v's and its fp16 copy come with the saved record);
+  // the fp16 copies; D and lse in exp2 units
+  const SavedLayout S = saved_layout(p.Tq, p.Tk, p.hq, p.hkv, D);
+  const unsigned char* saved = static_cast<const unsigned char*>(p.saved);
+  uint32_t* range = reinterpret_cast<uint32_t*>(ws + L.range);
+  const int64_t nq = rows * D / 8, nk = p.Tk * p.hkv * D / 8;  // 16-byte chunks
+  launch_range_clear(range, 8, stream);
+  RangeJob job{};
+  job.n = 3;
+  job.src[0] = p.q;
+  job.chunks[0] = nq;
+  job.word[0] = kRgQ;
+  job.src[1] = p.dout;
+  job.chunks[1] = nq;
+  job.word[1] = kRgDO;
+  job.src[2] = p.k;
+  job.chunks[2] = nk;
+  job.word[2] = kRgK;
+  job.words = range;
+  launch_range_max(job, stream);
+  {
+    // also writes the scales (thread 0), so it runs even without rows
+    const int64_t blocks = std::max<int64_t>((nq + kThreads - 1) / kThreads, 1);
+    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                       static_cast<const u32x4*>(p.q), static_cast<const u32x4*>(p.out),
+                       reinterpret_cast<const u32x4*>(saved + S.out_lo), static_cast<const u32x4*>(p.dout), p.lse,
+                       range, reinterpret_cast<const uint32_t*>(saved + S.words),
+                       reinterpret_cast<u32x4*>(ws + L.q16), reinterpret_cast<u32x4*>(ws + L.do16), dvec, lse2,
+                       reinterpret_cast<float*>(ws + L.range + 16), p.Tq, p.hq);
+  }
+  launch_convert(p.k, ws + L.k16, nk, range, kRgK, kRangeK, stream);
+  a.v = reinterpret_cast<const __bf16*>(saved + S.v16);
   // dK, dV: key tiles cut into runs, one workgroup per (run, kv head), then
   // the sums over the runs of split tiles
   a.row_ptr = p.kv_row_ptr;
@@ -910,6 +1004,25 @@ BwdWorkspaceLayout bwd_workspace_layout(int64_t Tq, int64_t Tk, int hq, int hkv,
   off += round256((size_t)qc.splits * 16);
   L.dq_partial = off;
   if (n_qt > 0) off += (size_t)kDqMaxSlots * kDqRows * (size_t)d * sizeof(float);
+  // range words and scales of the fp16 copies, the copies of q, dO and k,
+  // and the forward re-run's saved record, out and lse
+  const size_t nq = (size_t)(Tq > 0 ? Tq : 0) * (size_t)(hq > 0 ? hq : 0) * (size_t)d;
+  const size_t nk = (size_t)(Tk > 0 ? Tk : 0) * (size_t)(hkv > 0 ? hkv : 0) * (size_t)d;
+  off = round256(off);
+  L.range = off;
+  off += 256;
+  L.q16 = off;
+  off += round256(nq * 2);
+  L.do16 = off;
+  off += round256(nq * 2);
+  L.k16 = off;
+  off += round256(nk * 2);
+  L.re_saved = off;
+  off += round256(saved_layout(Tq, Tk, hq, hkv, d).total);
+  L.re_out = off;
+  off += round256(nq * 2);
+  L.re_lse = off;
+  off += round256((size_t)(Tq > 0 ? Tq : 0) * (size_t)(hq > 0 ? hq : 0) * sizeof(float));
   L.total = off;
   return L;
 }

@@ -10,6 +10,8 @@ namespace ffa {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
@@ -35,6 +37,13 @@ struct DevEntry {
 // holds column (l % 32), rows 8 * (v / 4) + 4 * (l / 32) + (v % 4), v = 0..15.
 __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// The same product with fp16 operands (same rate, 11 significant bits
+// instead of 8).  Operands are passed as raw 16-bit lanes.
+__device__ __forceinline__ f32x16 mfma_32x32x16_f16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                0, 0, 0);
 }
 
 // Buffer resource over [base, base + bytes): loads past the end return 0,
@@ -83,6 +92,53 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   p[0] = (__bf16)lo;
   p[1] = (__bf16)hi;
   return __builtin_bit_cast(uint32_t, p);
+}
+
+// Two fp32 values to fp16, round to nearest even, packed low | high << 16.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f16x2 p;
+  p[0] = (_Float16)lo;
+  p[1] = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, p);
+}
+
+// bf16 bits of x rounded to nearest even, and the bf16 bits of what that
+// rounding left out (x - hi, rounded again): together 16 significant bits.
+__device__ __forceinline__ void split_bf16(float x, uint16_t* hi, uint16_t* lo) {
+  const __bf16 h = (__bf16)x;
+  const float r = x - (float)h;
+  *hi = __builtin_bit_cast(uint16_t, h);
+  *lo = __builtin_bit_cast(uint16_t, (__bf16)r);
+}
+
+// Power of two s with max_abs * s in [2^(L-1), 2^L) (s = 1 for 0), from the
+// fp32 bits of a non-negative finite max_abs: it maps a tensor's range onto
+// fp16's (exact scaling; clamped to 2^-100 .. 2^100).
+__device__ __forceinline__ float range_scale(uint32_t max_bits, int L) {
+  if (max_bits == 0) return 1.0f;
+  int e = (int)(max_bits >> 23);  // biased exponent; subnormals count as 2^-126
+  if (e == 0) e = 1;
+  // max < 2^(e - 126), so s = 2^(L - (e - 126)) gives max * s < 2^L
+  int se = L - (e - 126);
+  se = se < -100 ? -100 : (se > 100 ? 100 : se);
+  return __uint_as_float((uint32_t)(se + 127) << 23);
+}
+
+// Range bounds L (largest |x| mapped into [2^(L-1), 2^L)) of the fp16
+// operand copies: 15 for q and k; for v and dO 4 and 3, which also keep
+// |dS| = P |dP - D| below 2^15 in the backward (|dP| <= d max|dO| max|v| <
+// 128 * 2^7, and |D| <= max |dP| since D is a convex combination of a row's
+// dP).  Word slots of the ranges in a range-word array.
+constexpr int kRangeQ = 15, kRangeK = 15, kRangeV = 4, kRangeDO = 3;
+enum { kRgQ = 0, kRgK = 1, kRgV = 2, kRgDO = 3 };
+
+// 8 bf16 values times s (a power of two) to fp16, round to nearest even.
+__device__ __forceinline__ u32x4 to_f16x8(u32x4 w, float s) {
+  u32x4 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    r[j] = pack_f16x2(__uint_as_float(w[j] << 16) * s, __uint_as_float(w[j] & 0xFFFF0000u) * s);
+  return r;
 }
 
 // ---------------------------------------------------------------- LDS tiles

@@ -297,18 +297,19 @@ int check_slopes(const float* slopes) {
 
 int fwd_planned(const ffa_plan_s* p, const void* q, const void* k, const void* v, int hq, int hkv,
                 int d, float scale, float softcap, const float* slopes, void* out, float* lse,
-                hipStream_t stream) {
+                void* saved, hipStream_t stream) {
   if (!(p->want & kWantFwd)) return fail(FFA_ERR_INVALID_ARG, "plan was built without the forward lists");
   int rc = check_heads(p->Tq, p->Tk, hq, hkv, d, scale, softcap);
   if (rc != FFA_OK) return rc;
   const bool has_q = p->Tq > 0, has_k = p->Tk > 0;
   if ((rc = check_ptr(q, has_q, "q")) || (rc = check_ptr(out, has_q, "out")) ||
       (rc = check_ptr(lse, has_q, "lse")) || (rc = check_ptr(k, has_k, "k")) ||
-      (rc = check_ptr(v, has_k, "v")) || (rc = check_slopes(slopes)))
+      (rc = check_ptr(v, has_k, "v")) || (rc = check_slopes(slopes)) ||
+      (saved && (rc = check_ptr(saved, true, "saved"))))
     return rc;
   if (p->Tq == 0) return FFA_OK;
   ffa::FwdLaunch L;
-  L.q = q; L.k = k; L.v = v; L.out = out; L.lse = lse;
+  L.q = q; L.k = k; L.v = v; L.out = out; L.lse = lse; L.saved = saved;
   L.Tq = p->Tq; L.Tk = p->Tk; L.hq = hq; L.hkv = hkv; L.d = d;
   L.scale = scale; L.softcap = softcap;
   L.row_ptr = reinterpret_cast<const int32_t*>(p->dev + p->fwd.off_row_ptr);
@@ -325,10 +326,12 @@ int fwd_planned(const ffa_plan_s* p, const void* q, const void* k, const void* v
 }
 
 int bwd_planned(const ffa_plan_s* p, const void* q, const void* k, const void* v, const void* out,
-                const float* lse, const void* dout, int hq, int hkv, int d, float scale, float softcap,
-                const float* slopes, void* dq, void* dk, void* dv, void* workspace,
+                const float* lse, const void* saved, const void* dout, int hq, int hkv, int d, float scale,
+                float softcap, const float* slopes, void* dq, void* dk, void* dv, void* workspace,
                 size_t workspace_bytes, hipStream_t stream) {
   if (!(p->want & kWantBwd)) return fail(FFA_ERR_INVALID_ARG, "plan was built without the backward lists");
+  if (!saved && !(p->want & kWantFwd))
+    return fail(FFA_ERR_INVALID_ARG, "without a saved record the plan needs the forward lists (to re-run the forward)");
   int rc = check_heads(p->Tq, p->Tk, hq, hkv, d, scale, softcap);
   if (rc != FFA_OK) return rc;
   const bool has_q = p->Tq > 0, has_k = p->Tk > 0;
@@ -336,7 +339,8 @@ int bwd_planned(const ffa_plan_s* p, const void* q, const void* k, const void* v
       (rc = check_ptr(lse, has_q, "lse")) || (rc = check_ptr(dout, has_q, "dout")) ||
       (rc = check_ptr(dq, has_q, "dq")) || (rc = check_ptr(k, has_k, "k")) ||
       (rc = check_ptr(v, has_k, "v")) || (rc = check_ptr(dk, has_k, "dk")) ||
-      (rc = check_ptr(dv, has_k, "dv")) || (rc = check_slopes(slopes)))
+      (rc = check_ptr(dv, has_k, "dv")) || (rc = check_slopes(slopes)) ||
+      (saved && (rc = check_ptr(saved, true, "saved"))))
     return rc;
   const size_t need = ffa_bwd_workspace_size(p->Tq, p->Tk, hq, hkv, d);
   if (workspace && workspace_bytes < need)
@@ -349,8 +353,30 @@ int bwd_planned(const ffa_plan_s* p, const void* q, const void* k, const void* v
     hipError_t e = hipMallocAsync(&ws, need, stream);
     if (e != hipSuccess) return fail(FFA_ERR_NOMEM, std::string("hipMallocAsync(workspace): ") + hipGetErrorString(e));
   }
+  const ffa::BwdWorkspaceLayout WL = ffa::bwd_workspace_layout(p->Tq, p->Tk, hq, hkv, d);
+  if (!saved) {
+    // no record from the caller: re-run the training forward into the
+    // workspace to get one (its out and lse are the caller's bits again)
+    unsigned char* b = static_cast<unsigned char*>(ws);
+    void* re_saved = b + WL.re_saved;
+    if (p->Tq > 0) {
+      rc = fwd_planned(p, q, k, v, hq, hkv, d, scale, softcap, slopes, b + WL.re_out,
+                       reinterpret_cast<float*>(b + WL.re_lse), re_saved, stream);
+      if (rc != FFA_OK) {
+        if (ws != workspace) (void)hipFreeAsync(ws, stream);
+        return rc;
+      }
+      out = b + WL.re_out;
+    } else if (p->Tk > 0) {
+      // no rows: the record is only read for v's copy, which nothing uses;
+      // give its range word a defined value
+      const ffa::SavedLayout S = ffa::saved_layout(p->Tq, p->Tk, hq, hkv, d);
+      ffa::launch_range_clear(reinterpret_cast<uint32_t*>(b + WL.re_saved + S.words), 4, stream);
+    }
+    saved = re_saved;
+  }
   ffa::BwdLaunch L;
-  L.q = q; L.k = k; L.v = v; L.out = out; L.lse = lse; L.dout = dout;
+  L.q = q; L.k = k; L.v = v; L.out = out; L.saved = saved; L.lse = lse; L.dout = dout;
   L.dq = dq; L.dk = dk; L.dv = dv; L.workspace = ws;
   L.Tq = p->Tq; L.Tk = p->Tk; L.hq = hq; L.hkv = hkv; L.d = d;
   L.scale = scale; L.softcap = softcap;
@@ -511,47 +537,47 @@ int ffa_plan_destroy(ffa_plan_t plan, void* stream) {
 
 int ffa_fwd_planned_ex(ffa_plan_t plan, const void* q, const void* k, const void* v, int hq, int hkv,
                        int d, float scale, float softcap, const float* alibi_slopes, void* out,
-                       float* lse, void* stream) {
+                       float* lse, void* saved, void* stream) {
   g_err.clear();
   if (!plan) return fail(FFA_ERR_INVALID_ARG, "plan must not be NULL");
-  return fwd_planned(plan, q, k, v, hq, hkv, d, scale, softcap, alibi_slopes, out, lse,
+  return fwd_planned(plan, q, k, v, hq, hkv, d, scale, softcap, alibi_slopes, out, lse, saved,
                      static_cast<hipStream_t>(stream));
 }
 
 int ffa_fwd_planned(ffa_plan_t plan, const void* q, const void* k, const void* v, int hq, int hkv,
                     int d, float scale, float softcap, void* out, float* lse, void* stream) {
-  return ffa_fwd_planned_ex(plan, q, k, v, hq, hkv, d, scale, softcap, nullptr, out, lse, stream);
+  return ffa_fwd_planned_ex(plan, q, k, v, hq, hkv, d, scale, softcap, nullptr, out, lse, nullptr, stream);
 }
 
 int ffa_bwd_planned_ex(ffa_plan_t plan, const void* q, const void* k, const void* v, const void* out,
-                       const float* lse, const void* dout, int hq, int hkv, int d, float scale,
-                       float softcap, const float* alibi_slopes, void* dq, void* dk, void* dv,
+                       const float* lse, const void* saved, const void* dout, int hq, int hkv, int d,
+                       float scale, float softcap, const float* alibi_slopes, void* dq, void* dk, void* dv,
                        void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   if (!plan) return fail(FFA_ERR_INVALID_ARG, "plan must not be NULL");
-  return bwd_planned(plan, q, k, v, out, lse, dout, hq, hkv, d, scale, softcap, alibi_slopes, dq, dk,
-                     dv, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+  return bwd_planned(plan, q, k, v, out, lse, saved, dout, hq, hkv, d, scale, softcap, alibi_slopes, dq,
+                     dk, dv, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 int ffa_bwd_planned(ffa_plan_t plan, const void* q, const void* k, const void* v, const void* out,
                     const float* lse, const void* dout, int hq, int hkv, int d, float scale,
                     float softcap, void* dq, void* dk, void* dv, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  return ffa_bwd_planned_ex(plan, q, k, v, out, lse, dout, hq, hkv, d, scale, softcap, nullptr, dq, dk,
-                            dv, workspace, workspace_bytes, stream);
+  return ffa_bwd_planned_ex(plan, q, k, v, out, lse, nullptr, dout, hq, hkv, d, scale, softcap, nullptr, dq,
+                            dk, dv, workspace, workspace_bytes, stream);
 }
 
 int ffa_fwd(const void* q, const void* k, const void* v, int64_t Tq, int64_t Tk, int hq, int hkv,
             int d, const int32_t* q_ranges, const int32_t* k_ranges, const int32_t* attn_type_map,
             int R, float scale, float softcap, void* out, float* lse, void* stream) {
   return ffa_fwd_ex(q, k, v, Tq, Tk, hq, hkv, d, q_ranges, k_ranges, attn_type_map, R, scale, softcap,
-                    nullptr, out, lse, stream);
+                    nullptr, out, lse, nullptr, stream);
 }
 
 int ffa_fwd_ex(const void* q, const void* k, const void* v, int64_t Tq, int64_t Tk, int hq, int hkv,
                int d, const int32_t* q_ranges, const int32_t* k_ranges, const int32_t* attn_type_map,
                int R, float scale, float softcap, const float* alibi_slopes, void* out, float* lse,
-               void* stream) {
+               void* saved, void* stream) {
   g_err.clear();
   std::string m = check_sizes(Tq, Tk);
   if (!m.empty()) return fail(FFA_ERR_INVALID_ARG, m);
@@ -561,18 +587,24 @@ int ffa_fwd_ex(const void* q, const void* k, const void* v, int64_t Tq, int64_t 
   const bool has_q = Tq > 0, has_k = Tk > 0;
   if ((rc = check_ptr(q, has_q, "q")) || (rc = check_ptr(out, has_q, "out")) ||
       (rc = check_ptr(lse, has_q, "lse")) || (rc = check_ptr(k, has_k, "k")) ||
-      (rc = check_ptr(v, has_k, "v")) || (rc = check_slopes(alibi_slopes)))
+      (rc = check_ptr(v, has_k, "v")) || (rc = check_slopes(alibi_slopes)) ||
+      (saved && (rc = check_ptr(saved, true, "saved"))))
     return rc;
   if (Tq == 0) return FFA_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   ffa_plan_s* p = nullptr;
   rc = plan_create(Tq, Tk, q_ranges, k_ranges, attn_type_map, R, kWantFwd, st, &p);
   if (rc != FFA_OK) return rc;
-  rc = fwd_planned(p, q, k, v, hq, hkv, d, scale, softcap, alibi_slopes, out, lse, st);
+  rc = fwd_planned(p, q, k, v, hq, hkv, d, scale, softcap, alibi_slopes, out, lse, saved, st);
   const std::string err = g_err;
   const int rc2 = plan_destroy(p, st);
   if (rc != FFA_OK) return fail(rc, err);
   return rc2;
+}
+
+size_t ffa_saved_size(int64_t Tq, int64_t Tk, int hq, int hkv, int d) {
+  if (Tq < 0 || Tk < 0 || hq <= 0 || hkv <= 0 || (d != 64 && d != 128)) return 0;
+  return ffa::saved_layout(Tq, Tk, hq, hkv, d).total;
 }
 
 size_t ffa_bwd_workspace_size(int64_t Tq, int64_t Tk, int hq, int hkv, int d) {
@@ -586,12 +618,12 @@ int ffa_bwd(const void* q, const void* k, const void* v, const void* out, const 
             const int32_t* q_ranges, const int32_t* k_ranges, const int32_t* attn_type_map, int R,
             float scale, float softcap, void* dq, void* dk, void* dv, void* workspace,
             size_t workspace_bytes, void* stream) {
-  return ffa_bwd_ex(q, k, v, out, lse, dout, Tq, Tk, hq, hkv, d, q_ranges, k_ranges, attn_type_map, R,
-                    scale, softcap, nullptr, dq, dk, dv, workspace, workspace_bytes, stream);
+  return ffa_bwd_ex(q, k, v, out, lse, nullptr, dout, Tq, Tk, hq, hkv, d, q_ranges, k_ranges, attn_type_map,
+                    R, scale, softcap, nullptr, dq, dk, dv, workspace, workspace_bytes, stream);
 }
 
 int ffa_bwd_ex(const void* q, const void* k, const void* v, const void* out, const float* lse,
-               const void* dout, int64_t Tq, int64_t Tk, int hq, int hkv, int d,
+               const void* saved, const void* dout, int64_t Tq, int64_t Tk, int hq, int hkv, int d,
                const int32_t* q_ranges, const int32_t* k_ranges, const int32_t* attn_type_map, int R,
                float scale, float softcap, const float* alibi_slopes, void* dq, void* dk, void* dv,
                void* workspace, size_t workspace_bytes, void* stream) {
@@ -606,16 +638,19 @@ int ffa_bwd_ex(const void* q, const void* k, const void* v, const void* out, con
       (rc = check_ptr(lse, has_q, "lse")) || (rc = check_ptr(dout, has_q, "dout")) ||
       (rc = check_ptr(dq, has_q, "dq")) || (rc = check_ptr(k, has_k, "k")) ||
       (rc = check_ptr(v, has_k, "v")) || (rc = check_ptr(dk, has_k, "dk")) ||
-      (rc = check_ptr(dv, has_k, "dv")) || (rc = check_slopes(alibi_slopes)))
+      (rc = check_ptr(dv, has_k, "dv")) || (rc = check_slopes(alibi_slopes)) ||
+      (saved && (rc = check_ptr(saved, true, "saved"))))
     return rc;
   if (workspace && workspace_bytes < ffa_bwd_workspace_size(Tq, Tk, hq, hkv, d))
     return fail(FFA_ERR_INVALID_ARG, "workspace is smaller than ffa_bwd_workspace_size()");
   if (Tq == 0 && Tk == 0) return FFA_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   ffa_plan_s* p = nullptr;
-  rc = plan_create(Tq, Tk, q_ranges, k_ranges, attn_type_map, R, kWantBwd, st, &p);
+  // without a saved record the forward is re-run, which needs its lists too
+  rc = plan_create(Tq, Tk, q_ranges, k_ranges, attn_type_map, R, saved ? kWantBwd : (kWantFwd | kWantBwd), st,
+                   &p);
   if (rc != FFA_OK) return rc;
-  rc = bwd_planned(p, q, k, v, out, lse, dout, hq, hkv, d, scale, softcap, alibi_slopes, dq, dk, dv,
+  rc = bwd_planned(p, q, k, v, out, lse, saved, dout, hq, hkv, d, scale, softcap, alibi_slopes, dq, dk, dv,
                    workspace, workspace_bytes, st);
   const std::string err = g_err;
   const int rc2 = plan_destroy(p, st);

@@ -68,6 +68,8 @@ struct FwdArgs {
   const __bf16* v;
   __bf16* out;
   float* lse;
+  __bf16* out_lo;           // rounding residual of out (training forward), or null
+  const uint32_t* v_words;  // training forward: range words of v (v is then its fp16 copy)
   const DevEntry* entries;  // grouped by q tile
   const DevSlice* slices;
   const int32_t* row_ptr;   // [n_qtiles + 1]
@@ -278,7 +280,11 @@ __device__ __forceinline__ void mask_tile(const DevSlice& sl, int ktile, int row
     }
 }
 
-template <int D, bool SOFTCAP, bool BIAS>
+// F16 (the training forward): v is the fp16 copy of v times its range scale
+// s_v, P enters the P V product in fp16 (11 significant bits instead of 8),
+// and the epilogue divides by s_v as well; the output then carries P's
+// rounding at 2^-12 instead of 2^-9, which the backward's row term D needs.
+template <int D, bool SOFTCAP, bool BIAS, bool F16>
 __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   using Smem = FwdSmem<D>;
   constexpr int KS = D / 16;  // k steps of the QK^T contraction
@@ -440,7 +446,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
           l4[e8 & 3] += p[e8];
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pw[t][i] = pack_bf16x2(p[2 * i], p[2 * i + 1]);
+        for (int i = 0; i < 4; ++i) pw[t][i] = F16 ? pack_f16x2(p[2 * i], p[2 * i + 1]) : pack_bf16x2(p[2 * i], p[2 * i + 1]);
       }
 
       if constexpr (MORE) {
@@ -471,7 +477,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
           const u32x2 hi4 = lds_read_tr16(vp + 8 * D);
           u32x4 av;
           av[0] = lo4[0]; av[1] = lo4[1]; av[2] = hi4[0]; av[3] = hi4[1];
-          o[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, pw[t]), o[db]);
+          if constexpr (F16)
+            o[db] = mfma_32x32x16_f16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, pw[t]), o[db]);
+          else
+            o[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, pw[t]), o[db]);
         }
       if constexpr (MORE) {
         if constexpr (SOFTCAP) softcap_tile<BIAS>(a, s_next, sigma, e1.tile, d0);
@@ -516,7 +525,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   // ---- epilogue: normalise once in fp32, round to bf16 once
   const float l_part = (l4[0] + l4[1]) + (l4[2] + l4[3]);
   const float l = l_part + __shfl_xor(l_part, 32);
-  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  float inv = l > 0.f ? 1.0f / l : 0.f;
+  if constexpr (F16) inv *= 1.0f / range_scale(const_load<uint32_t>(a.v_words, kRgV), kRangeV);
   if (item.slot >= 0) {
     // one run of a split q tile: fp32 output and lse for fwd_combine
     const int64_t pr = ((int64_t)item.slot * a.hq + head) * kBM + (row - q0);
@@ -535,16 +545,36 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
     if (hh == 0)
       a.partial_lse[pr] = l > 0.f ? (m_run * a.score_mult + fast_log2(l)) * 0.69314718055994531f : -INFINITY;
   } else if (row < a.Tq) {
-    __bf16* orow = a.out + ((int64_t)row * a.hq + head) * D;
+    const int64_t oo = ((int64_t)row * a.hq + head) * D;
+    if (a.out_lo) {
+      // out and what its rounding to bf16 left out (the backward forms
+      // rowsum(dO * out) from both)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x2 w2;
-        w2[0] = pack_bf16x2(o[db][4 * j + 0] * inv, o[db][4 * j + 1] * inv);
-        w2[1] = pack_bf16x2(o[db][4 * j + 2] * inv, o[db][4 * j + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * j + 4 * hh) = w2;
-      }
+        for (int j = 0; j < 4; ++j) {
+          uint16_t h[4], l[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) split_bf16(o[db][4 * j + i] * inv, &h[i], &l[i]);
+          u32x2 w2, r2;
+          w2[0] = h[0] | (uint32_t)h[1] << 16;
+          w2[1] = h[2] | (uint32_t)h[3] << 16;
+          r2[0] = l[0] | (uint32_t)l[1] << 16;
+          r2[1] = l[2] | (uint32_t)l[3] << 16;
+          *reinterpret_cast<u32x2*>(a.out + oo + 32 * db + 8 * j + 4 * hh) = w2;
+          *reinterpret_cast<u32x2*>(a.out_lo + oo + 32 * db + 8 * j + 4 * hh) = r2;
+        }
+    } else {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          u32x2 w2;
+          w2[0] = pack_bf16x2(o[db][4 * j + 0] * inv, o[db][4 * j + 1] * inv);
+          w2[1] = pack_bf16x2(o[db][4 * j + 2] * inv, o[db][4 * j + 3] * inv);
+          *reinterpret_cast<u32x2*>(a.out + oo + 32 * db + 8 * j + 4 * hh) = w2;
+        }
+    }
     if (hh == 0) {
       const float lse = l > 0.f ? (m_run * a.score_mult + fast_log2(l)) * 0.69314718055994531f : -INFINITY;
       a.lse[(int64_t)row * a.hq + head] = lse;
@@ -582,15 +612,24 @@ __global__ __launch_bounds__(kThreads) void fwd_combine_kernel(FwdArgs a) {
       }
     }
     const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+    uint16_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split_bf16(acc[i] * inv, &h[i], &l[i]);
     u32x2 w2;
-    w2[0] = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-    w2[1] = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    w2[0] = h[0] | (uint32_t)h[1] << 16;
+    w2[1] = h[2] | (uint32_t)h[3] << 16;
     *reinterpret_cast<u32x2*>(a.out + (row * a.hq + head) * D + 4 * c) = w2;
+    if (a.out_lo) {
+      u32x2 r2;
+      r2[0] = l[0] | (uint32_t)l[1] << 16;
+      r2[1] = l[2] | (uint32_t)l[3] << 16;
+      *reinterpret_cast<u32x2*>(a.out_lo + (row * a.hq + head) * D + 4 * c) = r2;
+    }
     if (c == 0) a.lse[row * a.hq + head] = sum > 0.f ? m + fast_log2(sum) * 0.69314718055994531f : -INFINITY;
   }
 }
 
-template <int D, bool SC, bool BIAS>
+template <int D, bool SC, bool BIAS, bool F16>
 hipError_t launch_fwd_t(const FwdLaunch& p, hipStream_t stream) {
   FwdArgs a;
   a.q = static_cast<const __bf16*>(p.q);
@@ -598,6 +637,28 @@ hipError_t launch_fwd_t(const FwdLaunch& p, hipStream_t stream) {
   a.v = static_cast<const __bf16*>(p.v);
   a.out = static_cast<__bf16*>(p.out);
   a.lse = p.lse;
+  a.out_lo = nullptr;
+  a.v_words = nullptr;
+  if constexpr (F16) {
+    // the record for the backward: v's range, its fp16 copy (read below as
+    // v), out's rounding residual
+    const SavedLayout S = saved_layout(p.Tq, p.Tk, p.hq, p.hkv, D);
+    unsigned char* sv = static_cast<unsigned char*>(p.saved);
+    uint32_t* words = reinterpret_cast<uint32_t*>(sv + S.words);
+    const int64_t nk = p.Tk * p.hkv * D / 8;
+    launch_range_clear(words, 4, stream);
+    RangeJob job{};
+    job.n = 1;
+    job.src[0] = p.v;
+    job.chunks[0] = nk;
+    job.word[0] = kRgV;
+    job.words = words;
+    launch_range_max(job, stream);
+    launch_convert(p.v, sv + S.v16, nk, words, kRgV, kRangeV, stream);
+    a.v = reinterpret_cast<const __bf16*>(sv + S.v16);
+    a.out_lo = reinterpret_cast<__bf16*>(sv + S.out_lo);
+    a.v_words = words;
+  }
   a.entries = reinterpret_cast<const DevEntry*>(p.entries);
   a.slices = reinterpret_cast<const DevSlice*>(p.slices);
   a.row_ptr = p.row_ptr;
@@ -636,7 +697,7 @@ hipError_t launch_fwd_t(const FwdLaunch& p, hipStream_t stream) {
     a.direct = 1;
     a.n_units = (int32_t)(n_qt * p.hkv);
     const int64_t n_wg = ((a.n_units + 7) / 8) * 8 * (int64_t)a.grp;
-    hipLaunchKernelGGL((fwd_kernel<D, SC, BIAS>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<D, SC, BIAS, F16>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
   }
   a.direct = 0;
@@ -658,7 +719,7 @@ hipError_t launch_fwd_t(const FwdLaunch& p, hipStream_t stream) {
   launch_split(sp, stream);
   const int64_t n_units = caps.items * p.hkv;
   const int64_t n_wg = ((n_units + 7) / 8) * 8 * (int64_t)a.grp;
-  hipLaunchKernelGGL((fwd_kernel<D, SC, BIAS>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((fwd_kernel<D, SC, BIAS, F16>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream, a);
   hipLaunchKernelGGL((fwd_combine_kernel<D>), dim3((unsigned)(caps.splits * p.hq)), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
@@ -691,11 +752,16 @@ FwdScratchLayout fwd_scratch_layout(int64_t Tq) {
 int fwd_tile_rows() { return kBM; }
 int fwd_tile_cols() { return kBN; }
 
+template <int D, bool F16>
+hipError_t launch_fwd_df(const FwdLaunch& p, hipStream_t stream) {
+  const bool sc = p.softcap > 0.f, bias = p.alibi_slopes != nullptr;
+  if (bias) return sc ? launch_fwd_t<D, true, true, F16>(p, stream) : launch_fwd_t<D, false, true, F16>(p, stream);
+  return sc ? launch_fwd_t<D, true, false, F16>(p, stream) : launch_fwd_t<D, false, false, F16>(p, stream);
+}
+
 template <int D>
 hipError_t launch_fwd_d(const FwdLaunch& p, hipStream_t stream) {
-  const bool sc = p.softcap > 0.f, bias = p.alibi_slopes != nullptr;
-  if (bias) return sc ? launch_fwd_t<D, true, true>(p, stream) : launch_fwd_t<D, false, true>(p, stream);
-  return sc ? launch_fwd_t<D, true, false>(p, stream) : launch_fwd_t<D, false, false>(p, stream);
+  return p.saved ? launch_fwd_df<D, true>(p, stream) : launch_fwd_df<D, false>(p, stream);
 }
 
 hipError_t launch_fwd(const FwdLaunch& p, hipStream_t stream) {

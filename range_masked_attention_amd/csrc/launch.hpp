@@ -15,12 +15,36 @@ struct HostDevEntry {
   int32_t meta;  // slice << 1 | partial
 };
 
+// What the training forward saves for the backward (device memory of
+// saved_layout(...).total bytes): range words (word kRgV: fp32 bits of
+// max |v|), out's bf16 rounding residual [Tq][hq][d], and the fp16 copy of v
+// [Tk][hkv][d] that the forward's P V product read (times its range scale).
+struct SavedLayout {
+  size_t words, out_lo, v16, total;
+};
+SavedLayout saved_layout(int64_t Tq, int64_t Tk, int hq, int hkv, int d);
+
+// fp16 operand copies (convert.hip): largest |x| of up to four bf16 tensors
+// into range words, then copies scaled by their range scale.
+struct RangeJob {
+  int n;
+  const void* src[4];
+  int64_t chunks[4];  // 16-byte chunks of each tensor
+  int word[4];        // its word slot
+  uint32_t* words;
+};
+void launch_range_clear(uint32_t* words, int n, hipStream_t stream);
+void launch_range_max(const RangeJob& job, hipStream_t stream);
+void launch_convert(const void* src, void* dst, int64_t chunks, const uint32_t* words, int word, int L,
+                    hipStream_t stream);
+
 struct FwdLaunch {
   const void* q;
   const void* k;
   const void* v;
   void* out;
   float* lse;
+  void* saved = nullptr;  // device, saved_layout(): filled for the backward (P V then runs in fp16), or null
   int64_t Tq, Tk;
   int hq, hkv, d;
   float scale, softcap;
@@ -50,6 +74,7 @@ struct BwdLaunch {
   const void* k;
   const void* v;
   const void* out;
+  const void* saved;  // device, saved_layout(): the training forward's record (never null here)
   const float* lse;
   const void* dout;
   void* dq;
@@ -140,10 +165,15 @@ void launch_split(const SplitLaunch& s, hipStream_t stream);
 
 // Byte offsets of the backward workspace pieces (each 256-byte aligned):
 // the row term D and lse in exp2 units, both [hq][Tq] fp32, two counters, the dK/dV work items and the
-// split-tile records (capacities in records), and the fp32 partial sums.
+// split-tile records (capacities in records), and the fp32 partial sums;
+// the range words and scales of the fp16 operand copies, the copies
+// themselves (q16, do16 [Tq][hq][d], k16 [Tk][hkv][d]; v's comes with the
+// saved record), and room for a forward re-run (its saved record, out and
+// lse) when the caller has no saved record.
 struct BwdWorkspaceLayout {
   size_t dvec, lse2, counts, items, splits, partial;
-  size_t dq_counts, dq_items, dq_splits, dq_partial, total;
+  size_t dq_counts, dq_items, dq_splits, dq_partial;
+  size_t range, q16, k16, do16, re_saved, re_out, re_lse, total;
   int64_t items_cap, splits_cap;
 };
 BwdWorkspaceLayout bwd_workspace_layout(int64_t Tq, int64_t Tk, int hq, int hkv, int d);

@@ -7,8 +7,12 @@ count.  The flash-attention pull request "Add torch.compile support to flash
 attention 3" shows the mechanism: register the kernels as custom operators with
 fake implementations (output shapes only) and an autograd formula.
 
-Here ``ffa_amd::fwd`` returns ``(out, lse)`` and ``ffa_amd::bwd`` returns
-``(dq, dk, dv)``.  The compiler treats both as opaque; their fake
+Here ``ffa_amd::fwd`` returns ``(out, lse, saved)`` and ``ffa_amd::bwd`` returns
+``(dq, dk, dv)``.  ``saved`` is the training forward's record for the backward
+(out's bf16 rounding residual, for the row term D = rowsum(dO * out), and the
+fp16 copy of v): a uint8 tensor, filled only when ``train`` is true (a backward
+may follow), else empty, and then the backward re-runs the training forward
+to get one.  The compiler treats both as opaque; their fake
 implementations depend only on tensor shapes, so one compiled graph serves every
 slice list of the same padded length.  The real implementations call the C ABI
 through the ctypes binding (slice tensors on the GPU are copied to the host
@@ -36,54 +40,66 @@ from . import ffa_fwd_planned as _ffa_fwd_planned
 NAMESPACE = "ffa_amd"
 
 
+def _saved_bytes(q, k):
+    from . import ffa_saved_size
+    return max(ffa_saved_size(q.shape[0], k.shape[0], q.shape[1], k.shape[1], q.shape[2]), 16)
+
+
 @torch.library.custom_op(f"{NAMESPACE}::fwd", mutates_args=(), device_types="cuda")
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_ranges: torch.Tensor,
         k_ranges: torch.Tensor, attn_type_map: torch.Tensor, scale: float,
-        softcap: float, alibi_slopes: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+        softcap: float, alibi_slopes: Optional[torch.Tensor] = None,
+        train: bool = False) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     plan = _cached_plan(q.shape[0], k.shape[0], q_ranges, k_ranges, attn_type_map, q.device)
     if plan is None:
-        return _ffa_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, scale, softcap, alibi_slopes=alibi_slopes)
-    return _ffa_fwd_planned(plan, q, k, v, scale, softcap, alibi_slopes=alibi_slopes)
+        r = _ffa_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, scale, softcap, alibi_slopes=alibi_slopes,
+                     train=train)
+    else:
+        r = _ffa_fwd_planned(plan, q, k, v, scale, softcap, alibi_slopes=alibi_slopes, train=train)
+    return (r[0], r[1], r[2] if train else q.new_empty((0,), dtype=torch.uint8))
 
 
 @fwd.register_fake
-def _fwd_fake(q, k, v, q_ranges, k_ranges, attn_type_map, scale, softcap, alibi_slopes=None):
+def _fwd_fake(q, k, v, q_ranges, k_ranges, attn_type_map, scale, softcap, alibi_slopes=None, train=False):
     torch._check(q.dim() == 3 and k.dim() == 3 and v.dim() == 3, lambda: "q, k, v must be [T, heads, d]")
-    return torch.empty_like(q), q.new_empty((q.shape[0], q.shape[1]), dtype=torch.float32)
+    n = _saved_bytes(q, k) if train else 0
+    return (torch.empty_like(q), q.new_empty((q.shape[0], q.shape[1]), dtype=torch.float32),
+            q.new_empty((n,), dtype=torch.uint8))
 
 
 @torch.library.custom_op(f"{NAMESPACE}::bwd", mutates_args=(), device_types="cuda")
 def bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
-        lse: torch.Tensor, q_ranges: torch.Tensor, k_ranges: torch.Tensor,
+        lse: torch.Tensor, saved: torch.Tensor, q_ranges: torch.Tensor, k_ranges: torch.Tensor,
         attn_type_map: torch.Tensor, scale: float, softcap: float,
         alibi_slopes: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    rec = saved if saved.numel() else None
     plan = _cached_plan(q.shape[0], k.shape[0], q_ranges, k_ranges, attn_type_map, q.device)
     if plan is None:
         return _ffa_bwd(q, k, v, out, lse, dout.contiguous(), q_ranges, k_ranges, attn_type_map,
-                        scale, softcap, alibi_slopes=alibi_slopes)
+                        scale, softcap, alibi_slopes=alibi_slopes, saved=rec)
     return _ffa_bwd_planned(plan, q, k, v, out, lse, dout.contiguous(), scale, softcap,
-                            alibi_slopes=alibi_slopes)
+                            alibi_slopes=alibi_slopes, saved=rec)
 
 
 @bwd.register_fake
-def _bwd_fake(dout, q, k, v, out, lse, q_ranges, k_ranges, attn_type_map, scale, softcap,
+def _bwd_fake(dout, q, k, v, out, lse, saved, q_ranges, k_ranges, attn_type_map, scale, softcap,
               alibi_slopes=None):
     return torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
 
 
 def _setup_context(ctx, inputs, output):
-    q, k, v, q_ranges, k_ranges, attn_type_map, scale, softcap, alibi_slopes = inputs
-    out, lse = output
-    ctx.save_for_backward(q, k, v, out, lse, q_ranges, k_ranges, attn_type_map, alibi_slopes)
+    q, k, v, q_ranges, k_ranges, attn_type_map, scale, softcap, alibi_slopes, train = inputs
+    out, lse, saved = output
+    ctx.save_for_backward(q, k, v, out, lse, saved, q_ranges, k_ranges, attn_type_map, alibi_slopes)
     ctx.scale, ctx.softcap = scale, softcap
-    ctx.mark_non_differentiable(lse)
+    ctx.mark_non_differentiable(lse, saved)
 
 
-def _backward(ctx, dout, dlse):
-    q, k, v, out, lse, q_ranges, k_ranges, attn_type_map, alibi_slopes = ctx.saved_tensors
-    dq, dk, dv = bwd(dout, q, k, v, out, lse, q_ranges, k_ranges, attn_type_map, ctx.scale, ctx.softcap,
-                     alibi_slopes)
-    return dq, dk, dv, None, None, None, None, None, None
+def _backward(ctx, dout, dlse, dsaved):
+    q, k, v, out, lse, saved, q_ranges, k_ranges, attn_type_map, alibi_slopes = ctx.saved_tensors
+    dq, dk, dv = bwd(dout, q, k, v, out, lse, saved, q_ranges, k_ranges, attn_type_map, ctx.scale,
+                     ctx.softcap, alibi_slopes)
+    return dq, dk, dv, None, None, None, None, None, None, None
 
 
 fwd.register_autograd(_backward, setup_context=_setup_context)

@@ -43,12 +43,14 @@ def pytest_sessionfinish(session, exitstatus):
 
     path = os.environ.get("FFA_PARITY_RECORD", os.path.join(ROOT, "gpurun_out", "parity_record.json"))
     os.makedirs(os.path.dirname(path) or ".", exist_ok=True)
-    worst = {}
+    worst, closest = {}, {}
     for r in rec:
         k = r["output"]
         if k not in worst or r["max_abs"] > worst[k]["max_abs"]:
             worst[k] = r
+        if k not in closest or r["excess"] > closest[k]["excess"]:
+            closest[k] = r
     doc = {"host": platform.node(), "exitstatus": int(exitstatus), "n_comparisons": len(rec),
-           "worst_per_output": worst, "comparisons": rec}
+           "largest_error_per_output": worst, "closest_to_bound_per_output": closest, "comparisons": rec}
     with open(path, "w") as f:
         json.dump(doc, f, indent=1)

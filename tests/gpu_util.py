@@ -55,12 +55,14 @@ def _test_id():
     return os.environ.get("PYTEST_CURRENT_TEST", "?").split(" (")[0]
 
 
-def record(ctx, name, err, ref_max, tol, n):
-    """Add one comparison to the parity record."""
+def record(ctx, name, err, ref_max, tol, n, excess):
+    """Add one comparison to the parity record: the max-abs error, max |ref|,
+    their ratio, and the largest (error - bound) over the elements (<= 0
+    passes)."""
     PARITY.append({
         "test": _test_id(), "ctx": str(ctx), "output": name, "max_abs": float(err),
         "max_ref": float(ref_max), "rel_to_max_ref": float(err / ref_max) if ref_max > 0 else 0.0,
-        "tol": tol, "n": int(n),
+        "tol": tol, "excess": float(excess), "n": int(n),
     })
 
 
@@ -81,8 +83,10 @@ def compare_out_lse(out, lse, ref_out, ref_lse, ctx=""):
     fin = ~inf_ref
     err_lse = float(np.abs(lse[fin] - ref_lse[fin]).max()) if fin.any() else 0.0
     err_out = float(np.abs(out - ref_out).max()) if out.size else 0.0
-    record(ctx, "out", err_out, float(np.abs(ref_out).max()) if out.size else 0.0, OUT_TOL, out.size)
-    record(ctx, "lse", err_lse, float(np.abs(ref_lse[fin]).max()) if fin.any() else 0.0, LSE_TOL, int(fin.sum()))
+    record(ctx, "out", err_out, float(np.abs(ref_out).max()) if out.size else 0.0, OUT_TOL, out.size,
+           err_out - OUT_TOL)
+    record(ctx, "lse", err_lse, float(np.abs(ref_lse[fin]).max()) if fin.any() else 0.0, LSE_TOL, int(fin.sum()),
+           err_lse - LSE_TOL)
     assert np.all(out[inf_ref] == 0.0), f"{ctx}: rows with no visible key must be 0"
     assert err_out <= OUT_TOL, f"{ctx}: out max-abs {err_out}"
     assert err_lse <= LSE_TOL, f"{ctx}: lse max-abs {err_lse}"
@@ -110,11 +114,11 @@ def check_grad(name, got, ref, ctx="", mag=None):
     diff = np.abs(got - ref)
     err = float(diff.max())
     ref_max = float(np.abs(ref).max())
-    record(ctx, name, err, ref_max, GRAD_TOL_ABS, got.size)
+    excess = float((diff - grad_tol(ref)).max())
+    record(ctx, name, err, ref_max, "2e-2 + 2^-8 |ref| where |ref| >= 4", got.size, excess)
     if mag is not None:
         budget = float((diff / (2.0 ** -8 * np.asarray(mag) + 1e-30)).max())
         PARITY[-1]["err_over_term_budget"] = budget
-    excess = float((diff - grad_tol(ref)).max())
     assert excess <= 0.0, f"{ctx}: {name} max-abs {err} (max |ref| {ref_max})"
     return err
 

@@ -101,10 +101,15 @@ def test_bwd_validation(lib):
     assert rc == -1 and "k range" in ffa.ffa_last_error()
     # workspace: D [Tq][hq] fp32; with keys, fp32 partial dK/dV of at most 512
     # (run, kv head) pairs of 128 keys x d x 2; with rows, fp32 partial dQ of
-    # at most 512 (run, q head) pairs of 128 rows x d
+    # at most 512 (run, q head) pairs of 128 rows x d; fp16 copies of q, dO
+    # (rows) and k (keys); the forward re-run's out and saved record (out's
+    # residual, v's fp16 copy)
     dkv, dq = 512 * 2 * 128 * 4, 512 * 128 * 4  # per unit of d
-    assert 100 * 8 * 4 + dq * 64 <= lib.ffa_bwd_workspace_size(100, 0, 8, 2, 64) < 100 * 8 * 4 + dq * 64 + (1 << 20)
-    assert dkv * 64 <= lib.ffa_bwd_workspace_size(0, 256, 8, 2, 64) < dkv * 64 + (1 << 20)
+    rows = 100 * 8 * 64 * 2 * 4  # q16, do16, out, residual at d = 64
+    assert 100 * 8 * 4 + dq * 64 + rows <= lib.ffa_bwd_workspace_size(100, 0, 8, 2, 64) \
+        < 100 * 8 * 4 + dq * 64 + rows + (1 << 20)
+    keys = 256 * 2 * 64 * 2 * 2  # k16, the record's v16
+    assert dkv * 64 + keys <= lib.ffa_bwd_workspace_size(0, 256, 8, 2, 64) < dkv * 64 + keys + (1 << 20)
     assert lib.ffa_bwd_workspace_size(100, 256, 8, 2, 128) >= 100 * 8 * 4 + (dkv + dq) * 128
     assert lib.ffa_bwd_workspace_size(100, 256, 8, 2, 64) < lib.ffa_bwd_workspace_size(100, 256, 8, 2, 128)
     assert lib.ffa_bwd_workspace_size(0, 0, 8, 2, 64) == 0
@@ -133,27 +138,25 @@ def test_alibi_slopes_validation(lib):
     """A misaligned slope pointer is rejected before any GPU work."""
     ip = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     qr = np.array([[0, 4]], np.int32); kr = np.array([[0, 4]], np.int32); ty = np.array([1], np.int32)
-    rc = lib.ffa_fwd_ex(64, 64, 64, 4, 4, 2, 2, 64, ip(qr), ip(kr), ip(ty), 1, 0.1, 0.0, 66, 64, 64, None)
+    rc = lib.ffa_fwd_ex(64, 64, 64, 4, 4, 2, 2, 64, ip(qr), ip(kr), ip(ty), 1, 0.1, 0.0, 66, 64, 64, None,
+                        None)
     assert rc == -1 and "alibi_slopes" in ffa.ffa_last_error()
-    rc = lib.ffa_bwd_ex(64, 64, 64, 64, 64, 64, 4, 4, 2, 2, 64, ip(qr), ip(kr), ip(ty), 1,
+    rc = lib.ffa_bwd_ex(64, 64, 64, 64, 64, None, 64, 4, 4, 2, 2, 64, ip(qr), ip(kr), ip(ty), 1,
                         0.1, 0.0, 66, 64, 64, 64, None, 0, None)
     assert rc == -1 and "alibi_slopes" in ffa.ffa_last_error()
 
 
-def test_injected_host_allocation_failure_is_nomem(lib, monkeypatch):
-    """FFA_INJECT_NOMEM makes every host planning step fail as if memory ran
-    out: the calls return FFA_ERR_NOMEM with a message, and work again once
-    it is cleared."""
-    qr, kr, ty = [[0, 100]], [[0, 100]], [1]
-    monkeypatch.setenv("FFA_INJECT_NOMEM", "1")
-    with pytest.raises(ffa.FfaError, match="host memory") as e:
-        ffa.ffa_plan_host(100, 100, qr, kr, ty, 64, 64)
-    assert e.value.code == -4
-    with pytest.raises(ffa.FfaError, match="host memory") as e:
-        ffa.ffa_block_slices([1, 1], [[0], [1]], 128, 128, 64, 64)
-    assert e.value.code == -4
-    monkeypatch.setenv("FFA_INJECT_NOMEM", "0")
-    rp, ent, order = ffa.ffa_plan_host(100, 100, qr, kr, ty, 64, 64)
-    assert len(ent) == 3
-    qs, ks, ts = ffa.ffa_block_slices([1, 1], [[0], [1]], 128, 128, 64, 64)
-    assert len(ts) == 2
+def test_saved_record_validation(lib):
+    """A misaligned saved-record pointer is rejected before any GPU work, and
+    the record's size is its header plus 2 bytes per element of q and of v."""
+    ip = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    qr = np.array([[0, 4]], np.int32); kr = np.array([[0, 4]], np.int32); ty = np.array([1], np.int32)
+    rc = lib.ffa_fwd_ex(64, 64, 64, 4, 4, 2, 2, 64, ip(qr), ip(kr), ip(ty), 1, 0.1, 0.0, None, 64, 64, 72,
+                        None)
+    assert rc == -1 and "saved" in ffa.ffa_last_error()
+    rc = lib.ffa_bwd_ex(64, 64, 64, 64, 64, 72, 64, 4, 4, 2, 2, 64, ip(qr), ip(kr), ip(ty), 1,
+                        0.1, 0.0, None, 64, 64, 64, None, 0, None)
+    assert rc == -1 and "saved" in ffa.ffa_last_error()
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert lib.ffa_saved_size(100, 300, 8, 2, 128) == 256 + r256(100 * 8 * 128 * 2) + r256(300 * 2 * 128 * 2)
+    assert lib.ffa_saved_size(100, 300, 8, 2, 96) == 0

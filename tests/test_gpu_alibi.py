@@ -114,7 +114,8 @@ def test_full_size_sampled(n):
 
 
 def test_planned_and_autograd_paths():
-    """The planned entry points and flex_flash_attn_func give the one-shot bits."""
+    """The planned entry points and flex_flash_attn_func (which runs the
+    training forward when gradients are wanted) give the one-shot bits."""
     w = W.config(1)
     say("alibi planned + autograd")
     q, k, v, do = W.workload_tensors(w, with_dout=True)
@@ -122,12 +123,12 @@ def test_planned_and_autograd_paths():
     qr, kr, ty = w.slices()
     st = torch.tensor([0.5, -0.25], dtype=torch.float32, device=d)
     qd, kd, vd, od = q.to(d), k.to(d), v.to(d), do.to(d)
-    o0, l0 = ffa.ffa_fwd_ex(qd, kd, vd, qr, kr, ty, w.scale, 0.0, st)
-    g0 = ffa.ffa_bwd_ex(qd, kd, vd, o0, l0, od, qr, kr, ty, w.scale, 0.0, st)
+    o0, l0, r0 = ffa.ffa_fwd_ex(qd, kd, vd, qr, kr, ty, w.scale, 0.0, st, train=True)
+    g0 = ffa.ffa_bwd_ex(qd, kd, vd, o0, l0, od, qr, kr, ty, w.scale, 0.0, st, saved=r0)
     plan = ffa.ffa_plan_create(w.Tq, w.Tk, qr, kr, ty)
     try:
-        o1, l1 = ffa.ffa_fwd_planned_ex(plan, qd, kd, vd, w.scale, 0.0, st)
-        g1 = ffa.ffa_bwd_planned_ex(plan, qd, kd, vd, o1, l1, od, w.scale, 0.0, st)
+        o1, l1, r1 = ffa.ffa_fwd_planned_ex(plan, qd, kd, vd, w.scale, 0.0, st, train=True)
+        g1 = ffa.ffa_bwd_planned_ex(plan, qd, kd, vd, o1, l1, od, w.scale, 0.0, st, saved=r1)
     finally:
         ffa.ffa_plan_destroy(plan)
     qa, ka, va = (t.clone().requires_grad_() for t in (qd, kd, vd))

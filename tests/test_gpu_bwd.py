@@ -19,10 +19,17 @@ from gpu_util import O, check_grad, dev, ffa, say, to64
 pytestmark = pytest.mark.gpu
 
 
-def _bwd_gpu(q, k, v, do, qr, kr, ty, scale, cap, d):
+def _bwd_gpu(q, k, v, do, qr, kr, ty, scale, cap, d, train=True):
+    """Forward then backward through the C ABI; with `train` the training
+    forward saves its record and the backward takes it (ffa_*_ex), else the
+    plain entry points (the backward re-runs the training forward for it)."""
     qd, kd, vd, od = q.to(d), k.to(d), v.to(d), do.to(d)
-    out, lse = ffa.ffa_fwd(qd, kd, vd, qr, kr, ty, scale, cap)
-    dq, dk, dv = ffa.ffa_bwd(qd, kd, vd, out, lse, od, qr, kr, ty, scale, cap)
+    if train:
+        out, lse, rec = ffa.ffa_fwd(qd, kd, vd, qr, kr, ty, scale, cap, train=True)
+        dq, dk, dv = ffa.ffa_bwd(qd, kd, vd, out, lse, od, qr, kr, ty, scale, cap, saved=rec)
+    else:
+        out, lse = ffa.ffa_fwd(qd, kd, vd, qr, kr, ty, scale, cap)
+        dq, dk, dv = ffa.ffa_bwd(qd, kd, vd, out, lse, od, qr, kr, ty, scale, cap)
     torch.cuda.synchronize()
     return dq, dk, dv
 
@@ -222,6 +229,48 @@ def test_full_size_long_list_keys(case):
     e = [_cmp("dq", dq[rows][:, heads], rq, ctx, None), _cmp("dk", dk[keys][:, [g]], rk, ctx, None),
          _cmp("dv", dv[keys][:, [g]], rv, ctx, None)]
     say(f"  {len(keys)} keys, {len(rows)} rows: dq/dk/dv max-abs {e[0]:.3e} {e[1]:.3e} {e[2]:.3e}")
+
+
+@pytest.mark.parametrize("case", [("config2", 0.0), ("sink", 30.0)])
+def test_plain_entry_points_rerun_the_forward_bitwise(case):
+    """ffa_bwd without a saved record re-runs the training forward to get
+    one: the same bits as the training path, split runs included."""
+    name, cap = case
+    say(f"bwd plain vs training path bitwise ({name})")
+    if name == "config2":
+        w = W.config(2)
+        q, k, v, do = W.workload_tensors(w)
+        qr, kr, ty = w.slices()
+        scale = w.scale
+    else:
+        q, k, v, do = W.make_tensors(4096, 4096, 8, 2, 128, seed=12)
+        qr, kr, ty = _sink_slices(4096, 512, 128, 1024)
+        scale = 128 ** -0.5
+    a = _bwd_gpu(q, k, v, do, qr, kr, ty, scale, cap, dev(), train=True)
+    b = _bwd_gpu(q, k, v, do, qr, kr, ty, scale, cap, dev(), train=False)
+    for n, x, y in zip(("dq", "dk", "dv"), a, b):
+        assert torch.equal(x, y), n
+
+
+def test_operand_range_scaling_is_exact():
+    """The fp16 operand copies are scaled by powers of two that map each
+    tensor's range onto fp16's, so scaling v by 2^12, dO by 2^-30, q by 2^9
+    and k by 2^-9 (far outside fp16's range for dO, near its top for v)
+    scales the gradients by exact powers of two, bit for bit:
+      dv -> 2^-30 dv,  dq -> 2^(12-30-9) dq,  dk -> 2^(12-30+9) dk."""
+    say("bwd range scaling exact")
+    Tq, Tk, hq, hkv, dd = 700, 500, 4, 2, 128
+    rng = np.random.default_rng(5)
+    qr, kr, ty = W.random_slices(rng, Tq, Tk, max_slices=6, n_dummies=2)
+    q, k, v, do = W.make_tensors(Tq, Tk, hq, hkv, dd, seed=77)
+    scale = 0.11
+    base = _bwd_gpu(q, k, v, do, qr, kr, ty, scale, 0.0, dev())
+    sq, sk, sv, sd = 2.0 ** 9, 2.0 ** -9, 2.0 ** 12, 2.0 ** -30
+    bf = torch.bfloat16
+    scaled = _bwd_gpu((q.float() * sq).to(bf), (k.float() * sk).to(bf), (v.float() * sv).to(bf),
+                      (do.float() * sd).to(bf), qr, kr, ty, scale, 0.0, dev())
+    for n, x, y, f in zip(("dq", "dk", "dv"), base, scaled, (sv * sd * sk, sv * sd * sq, sd)):
+        assert torch.equal((x.float() * f).to(bf), y), n
 
 
 def test_dummy_padding_and_determinism_bitwise():

@@ -46,8 +46,9 @@ def test_eager_operator_matches_c_abi():
     qr, kr, ty = w.slices()
     got = _run(_attn, q, k, v, do, _slices_tensor(qr, kr, ty, d), d)
     qd, kd, vd, od = q.to(d), k.to(d), v.to(d), do.to(d)
-    out, lse = ffa.ffa_fwd(qd, kd, vd, qr, kr, ty, w.scale, 0.0)
-    dq, dk, dv = ffa.ffa_bwd(qd, kd, vd, out, lse, od, qr, kr, ty, w.scale, 0.0)
+    # gradients are wanted, so the operator runs the training forward
+    out, lse, rec = ffa.ffa_fwd(qd, kd, vd, qr, kr, ty, w.scale, 0.0, train=True)
+    dq, dk, dv = ffa.ffa_bwd(qd, kd, vd, out, lse, od, qr, kr, ty, w.scale, 0.0, saved=rec)
     torch.cuda.synchronize()
     for a, b in zip(got, (out, lse, dq, dk, dv)):
         assert torch.equal(a, b)

@@ -121,6 +121,42 @@ def test_dummy_padding_bitwise():
     assert torch.equal(o0, o2) and torch.equal(l0, l2)
 
 
+def test_training_forward_record():
+    """The training forward (saved record) runs P V with fp16 P: lse keeps its
+    bits, out is at least as close to the oracle as the plain forward's, and
+    the record holds out's rounding residual (at most half an ulp of out,
+    with out + residual closer still) and v's fp16 copy."""
+    w = W.config(2)
+    say("fwd training record (config 2)")
+    q, k, v, _ = W.workload_tensors(w, with_dout=False)
+    d = dev()
+    qd, kd, vd = q.to(d), k.to(d), v.to(d)
+    qr, kr, ty = w.slices()
+    o0, l0 = ffa.ffa_fwd(qd, kd, vd, qr, kr, ty, w.scale, 0.0)
+    o1, l1, rec = ffa.ffa_fwd(qd, kd, vd, qr, kr, ty, w.scale, 0.0, train=True)
+    torch.cuda.synchronize()
+    assert torch.equal(l0, l1)
+    n = o1.numel()
+    res = rec[256:256 + 2 * n].view(torch.bfloat16).view(o1.shape)
+    ref, ref_lse = O.attention_fwd(to64(q), to64(k), to64(v), qr, kr, ty, w.scale)
+    compare_out_lse(o1.cpu(), l1.cpu(), ref, ref_lse, "training forward")
+    o, r = o1.double().cpu().numpy(), res.double().cpu().numpy()
+    # half an ulp of a bf16 value x is 2^(floor(log2 |x|) - 8)
+    half_ulp = np.where(o != 0, 2.0 ** (np.floor(np.log2(np.abs(np.where(o != 0, o, 1.0)))) - 8), 0.0)
+    assert np.all(np.abs(r) <= half_ulp)
+    e_plain = np.abs(o0.double().cpu().numpy() - ref).max()
+    e_train = np.abs(o - ref).max()
+    e_full = np.abs(o + r - ref).max()
+    say(f"  out max-abs plain {e_plain:.3e} training {e_train:.3e} with residual {e_full:.3e}")
+    assert e_full < e_train <= e_plain + 2.0 ** -8
+    # v's copy: fp16 of v times a power of two
+    kv = v.numel()
+    off = 256 + ((2 * n + 255) // 256) * 256
+    v16 = rec[off:off + 2 * kv].view(torch.float16).float().cpu()
+    ratio = (v16.flatten() / v.float().flatten())[v.float().flatten() != 0]
+    assert torch.all(ratio == ratio[0]) and float(torch.log2(ratio[0])) == round(float(torch.log2(ratio[0])))
+
+
 def test_run_twice_bitwise():
     w = W.config(3)
     say("fwd determinism (config 3, twice)")

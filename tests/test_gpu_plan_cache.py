@@ -46,8 +46,8 @@ def test_cache_hits_evicts_and_matches_one_shot():
         assert cache.misses - m0 == 6 and cache.hits - h0 == 6, (cache.misses - m0, cache.hits - h0)
         assert len(cache._plans) == 2
         for i, (qr, kr, ty) in enumerate(_lists(w)):
-            o, l = ffa.ffa_fwd(qd, kd, vd, qr, kr, ty, w.scale)
-            g = ffa.ffa_bwd(qd, kd, vd, o, l, od, qr, kr, ty, w.scale)
+            o, l, rec = ffa.ffa_fwd(qd, kd, vd, qr, kr, ty, w.scale, train=True)
+            g = ffa.ffa_bwd(qd, kd, vd, o, l, od, qr, kr, ty, w.scale, saved=rec)
             torch.cuda.synchronize()
             for r in (results[i], results[i + 3]):
                 assert torch.equal(r[0], o) and torch.equal(r[1], l)

@@ -35,10 +35,13 @@ def _fake_inputs(Tq=100, Tk=70, hq=8, hkv=2, d=128, R=5):
 def test_fake_shapes():
     with FakeTensorMode():
         q, k, v, qr, kr, ty = _fake_inputs()
-        out, lse = torch.ops.ffa_amd.fwd(q, k, v, qr, kr, ty, 0.1, 0.0)
+        out, lse, lo = torch.ops.ffa_amd.fwd(q, k, v, qr, kr, ty, 0.1, 0.0)
         assert out.shape == q.shape and out.dtype == torch.bfloat16 and out.device == q.device
         assert lse.shape == (100, 8) and lse.dtype == torch.float32
-        dq, dk, dv = torch.ops.ffa_amd.bwd(out, q, k, v, out, lse, qr, kr, ty, 0.1, 0.0)
+        assert lo.numel() == 0
+        out, lse, lo = torch.ops.ffa_amd.fwd(q, k, v, qr, kr, ty, 0.1, 0.0, None, True)
+        assert lo.shape == (ffa.ffa_saved_size(100, 70, 8, 2, 128),) and lo.dtype == torch.uint8
+        dq, dk, dv = torch.ops.ffa_amd.bwd(out, q, k, v, out, lse, lo, qr, kr, ty, 0.1, 0.0)
         assert (dq.shape, dk.shape, dv.shape) == (q.shape, k.shape, v.shape)
         assert dq.dtype == dk.dtype == dv.dtype == torch.bfloat16
 
@@ -63,7 +66,7 @@ def test_alibi_slopes_argument_is_optional_tensor():
     with FakeTensorMode():
         q, k, v, qr, kr, ty = _fake_inputs()
         slopes = torch.empty(8, dtype=torch.float32, device="cuda")
-        out, lse = torch.ops.ffa_amd.fwd(q, k, v, qr, kr, ty, 0.1, 0.0, slopes)
+        out, lse, _ = torch.ops.ffa_amd.fwd(q, k, v, qr, kr, ty, 0.1, 0.0, slopes)
         assert out.shape == q.shape and lse.shape == (100, 8)
 
 
