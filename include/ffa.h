@@ -136,6 +136,31 @@ int ffa_bwd(const void* q, const void* k, const void* v,
             void* stream);
 
 /*
+ * ffa_fwd_noalloc -- ffa_fwd for callers that cannot allocate: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, results (bitwise) and errors as ffa_fwd, and it allocates
+ * nothing: the slice arrays' device copy, the block-sparse plan (built on
+ * the device from that copy) and the forward's run scratch live in one
+ * 64 MiB device array of the library's (each GPU holds its own copy from the
+ * first call on it until the process ends).  The slice arrays are copied to
+ * it with hipMemcpyAsync on `stream`.  Limits, checked on the host before
+ * any GPU work (FFA_ERR_INVALID_ARG): at most 4096 slices, and the plan must
+ * fit the array: about 4 million (q tile, key tile, slice) entries at
+ * Tq = 64K, fewer as Tq grows (the message gives both counts).  Overlapping
+ * slices are not looked for under FFA_DEBUG.  All calls on one GPU share the
+ * array: calls that overlap in time on one GPU (different streams, or
+ * different host threads) race and must not be made.
+ */
+int ffa_fwd_noalloc(const void* q, const void* k, const void* v,
+                    int64_t Tq, int64_t Tk, int hq, int hkv, int d,
+                    const int32_t* q_ranges, const int32_t* k_ranges,
+                    const int32_t* attn_type_map, int R,
+                    float scale, float softcap,
+                    void* out, float* lse,
+                    void* stream);
+
+/*
  * Distance bias (ALiBi).  The FlexAttention paper summary lists ALiBi among
  * the attention variants as a bias that depends on the distance between the
  * query and key positions (section 2; section 3.1, a position-dependent score

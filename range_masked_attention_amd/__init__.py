@@ -30,7 +30,7 @@ __all__ = [
     "ffa_plan_create", "ffa_fwd_planned", "ffa_bwd_planned", "ffa_plan_destroy",
     "ffa_plan_device_workspace_size", "ffa_plan_create_device", "ffa_plan_refresh", "ffa_plan_status",
     "ffa_plan_export", "FFA_PLAN_BAD_SLICE", "FFA_PLAN_CAPACITY", "flex_flash_attn_func",
-    "alibi_geometric_slopes", "ffa_block_slices", "cached_plan", "clear_plan_cache", "ffa_fwd_ex", "ffa_bwd_ex", "ffa_saved_size", "ffa_fwd_planned_ex", "ffa_bwd_planned_ex",
+    "alibi_geometric_slopes", "ffa_block_slices", "cached_plan", "clear_plan_cache", "ffa_fwd_ex", "ffa_bwd_ex", "ffa_saved_size", "ffa_fwd_noalloc", "ffa_fwd_planned_ex", "ffa_bwd_planned_ex",
 ]
 
 FULL = 0
@@ -71,6 +71,9 @@ def load_library():
     lib.ffa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i32, i32, i32, ip32, ip32, ip32,
                             i32, f32, f32, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.ffa_bwd.restype = ctypes.c_int
+    lib.ffa_fwd_noalloc.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, ip32, ip32, ip32, i32,
+                                    f32, f32, vp, vp, vp]
+    lib.ffa_fwd_noalloc.restype = ctypes.c_int
     lib.ffa_fwd_ex.argtypes = [vp, vp, vp, i64, i64, i32, i32, i32, ip32, ip32, ip32, i32,
                                f32, f32, vp, vp, vp, vp, vp]
     lib.ffa_fwd_ex.restype = ctypes.c_int
@@ -250,6 +253,26 @@ def ffa_fwd(q, k, v, q_ranges, k_ranges, attn_type_map, scale: float, softcap: f
                             saved.data_ptr() if saved is not None else None, st)
     _check(rc)
     return (out, lse) if saved is None else (out, lse, saved)
+
+
+def ffa_fwd_noalloc(q, k, v, q_ranges, k_ranges, attn_type_map, scale: float, softcap: float, out, lse):
+    """C ABI ``ffa_fwd_noalloc``: ``ffa_fwd`` into the caller's ``out`` and ``lse``
+    with no device allocation (the library's own device array holds the plan)."""
+    import torch
+    lib = load_library()
+    for nm, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(nm, t, torch.bfloat16, 3)
+    _check_tensor("out", out, torch.bfloat16, 3)
+    _check_tensor("lse", lse, torch.float32, 2)
+    Tq, hq, d = q.shape
+    Tk, hkv, _ = k.shape
+    if tuple(out.shape) != tuple(q.shape) or tuple(lse.shape) != (Tq, hq):
+        raise ValueError("out must be shaped like q and lse [Tq, hq]")
+    qr, kr, ty = _host_slices(q_ranges, k_ranges, attn_type_map)
+    _check(lib.ffa_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), Tq, Tk, hq, hkv, d,
+                               _iptr(qr), _iptr(kr), _iptr(ty), qr.shape[0], float(scale), float(softcap),
+                               out.data_ptr(), lse.data_ptr(), _stream_handle(q)))
+    return out, lse
 
 
 def ffa_bwd_workspace_size(Tq: int, Tk: int, hq: int, hkv: int, d: int) -> int:

@@ -178,6 +178,34 @@ enum : int { kWantFwd = 1, kWantBwd = 2 };
 
 }  // namespace
 
+// For ffa_fwd_noalloc (noalloc.hip): the forward's argument checks with no
+// allocation on success.  Overlapping slices are not looked for (the check
+// under FFA_DEBUG keeps a list of the slices).
+namespace ffa_abi {
+int fail(int code, const std::string& msg) { return ::fail(code, msg); }
+int check_forward_args(const void* q, const void* k, const void* v, int64_t Tq, int64_t Tk, int hq, int hkv,
+                       int d, const int32_t* q_ranges, const int32_t* k_ranges, const int32_t* attn_type_map,
+                       int R, float scale, float softcap, const void* out, const float* lse) {
+  g_err.clear();
+  std::string m = check_sizes(Tq, Tk);
+  if (!m.empty()) return ::fail(FFA_ERR_INVALID_ARG, m);
+  int rc = check_heads(Tq, Tk, hq, hkv, d, scale, softcap);
+  if (rc != FFA_OK) return rc;
+  if (R < 0) return ::fail(FFA_ERR_INVALID_ARG, "R must be >= 0");
+  if (R > 0 && (!q_ranges || !k_ranges || !attn_type_map))
+    return ::fail(FFA_ERR_INVALID_ARG, "slice arrays must not be NULL when R > 0");
+  for (int r = 0; r < R; ++r) {
+    m = ffa::check_slice(Tq, Tk, q_ranges, k_ranges, attn_type_map, r);
+    if (!m.empty()) return ::fail(FFA_ERR_INVALID_ARG, m);
+  }
+  const bool has_q = Tq > 0, has_k = Tk > 0;
+  if ((rc = check_ptr(q, has_q, "q")) || (rc = check_ptr(out, has_q, "out")) ||
+      (rc = check_ptr(lse, has_q, "lse")) || (rc = check_ptr(k, has_k, "k")) || (rc = check_ptr(v, has_k, "v")))
+    return rc;
+  return FFA_OK;
+}
+}  // namespace ffa_abi
+
 // The plan handle: sizes, the non-empty slices and the device copy of the
 // block-sparse lists.
 struct ffa_plan_s {

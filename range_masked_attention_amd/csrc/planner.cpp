@@ -9,6 +9,23 @@
 
 namespace ffa {
 
+std::string check_slice(int64_t Tq, int64_t Tk, const int32_t* q_ranges, const int32_t* k_ranges,
+                        const int32_t* types, int r) {
+  const int64_t qs = q_ranges[2 * r], qe = q_ranges[2 * r + 1];
+  const int64_t ks = k_ranges[2 * r], ke = k_ranges[2 * r + 1];
+  const int32_t t = types[r];
+  if (qs < 0 || qe < qs || qe > Tq)
+    return "slice " + std::to_string(r) + ": q range [" + std::to_string(qs) + ", " +
+           std::to_string(qe) + ") is not inside [0, " + std::to_string(Tq) + ")";
+  if (ks < 0 || ke < ks || ke > Tk)
+    return "slice " + std::to_string(r) + ": k range [" + std::to_string(ks) + ", " +
+           std::to_string(ke) + ") is not inside [0, " + std::to_string(Tk) + ")";
+  if (t != kFull && t != kCausal)
+    return "slice " + std::to_string(r) + ": attention type " + std::to_string(t) +
+           " is neither FULL (0) nor CAUSAL (1)";
+  return "";
+}
+
 std::string validate_slices(int64_t Tq, int64_t Tk, const int32_t* q_ranges,
                             const int32_t* k_ranges, const int32_t* types, int R,
                             std::vector<Slice>* out) {
@@ -17,18 +34,11 @@ std::string validate_slices(int64_t Tq, int64_t Tk, const int32_t* q_ranges,
   if (R > 0 && (!q_ranges || !k_ranges || !types)) return "slice arrays must not be NULL when R > 0";
   out->reserve(static_cast<size_t>(R));
   for (int r = 0; r < R; ++r) {
+    std::string m = check_slice(Tq, Tk, q_ranges, k_ranges, types, r);
+    if (!m.empty()) return m;
     const int64_t qs = q_ranges[2 * r], qe = q_ranges[2 * r + 1];
     const int64_t ks = k_ranges[2 * r], ke = k_ranges[2 * r + 1];
     const int32_t t = types[r];
-    if (qs < 0 || qe < qs || qe > Tq)
-      return "slice " + std::to_string(r) + ": q range [" + std::to_string(qs) + ", " +
-             std::to_string(qe) + ") is not inside [0, " + std::to_string(Tq) + ")";
-    if (ks < 0 || ke < ks || ke > Tk)
-      return "slice " + std::to_string(r) + ": k range [" + std::to_string(ks) + ", " +
-             std::to_string(ke) + ") is not inside [0, " + std::to_string(Tk) + ")";
-    if (t != kFull && t != kCausal)
-      return "slice " + std::to_string(r) + ": attention type " + std::to_string(t) +
-             " is neither FULL (0) nor CAUSAL (1)";
     // a zero-length range on either axis covers no cell: drop it
     if (qs == qe || ks == ke) continue;
     out->push_back(Slice{static_cast<int32_t>(qs), static_cast<int32_t>(qe),

@@ -37,6 +37,11 @@ struct Plan {
   std::vector<int32_t> order;      // tiles by descending entry count
 };
 
+// Checks slice r against the token counts: "" if it is valid (no
+// allocation then), else a message.
+std::string check_slice(int64_t Tq, int64_t Tk, const int32_t* q_ranges, const int32_t* k_ranges,
+                        const int32_t* types, int r);
+
 // Checks the slice list against the token counts and keeps the non-empty
 // slices (in the caller's order).  Returns "" on success, else a message.
 std::string validate_slices(int64_t Tq, int64_t Tk, const int32_t* q_ranges,

@@ -160,3 +160,22 @@ def test_saved_record_validation(lib):
     r256 = lambda x: (x + 255) // 256 * 256
     assert lib.ffa_saved_size(100, 300, 8, 2, 128) == 256 + r256(100 * 8 * 128 * 2) + r256(300 * 2 * 128 * 2)
     assert lib.ffa_saved_size(100, 300, 8, 2, 96) == 0
+
+
+def test_noalloc_rejects_sizes_beyond_its_array(lib):
+    """ffa_fwd_noalloc checks its limits on the host, before any GPU work:
+    more than 4096 slices, or a plan larger than its device array."""
+    ip = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    R = 4097
+    qr = np.zeros((R, 2), np.int32); kr = np.zeros((R, 2), np.int32); ty = np.zeros(R, np.int32)
+    rc = lib.ffa_fwd_noalloc(64, 64, 64, 16, 16, 2, 1, 64, ip(qr), ip(kr), ip(ty), R, 0.1, 0.0, 64, 64, None)
+    assert rc == -1 and "4096 slices" in ffa.ffa_last_error()
+    # one FULL slice over 2^20 x 2^20 tokens: 8192 x 16384 tiles, far past the array
+    T = 1 << 20
+    qr = np.array([[0, T]], np.int32); kr = np.array([[0, T]], np.int32); ty = np.array([0], np.int32)
+    rc = lib.ffa_fwd_noalloc(64, 64, 64, T, T, 1, 1, 64, ip(qr), ip(kr), ip(ty), 1, 0.1, 0.0, 64, 64, None)
+    assert rc == -1 and "entries" in ffa.ffa_last_error() and "134217728" in ffa.ffa_last_error()
+    # bad slices are reported as by ffa_fwd
+    qr = np.array([[0, 17]], np.int32); kr = np.array([[0, 16]], np.int32); ty = np.array([0], np.int32)
+    rc = lib.ffa_fwd_noalloc(64, 64, 64, 16, 16, 2, 1, 64, ip(qr), ip(kr), ip(ty), 1, 0.1, 0.0, 64, 64, None)
+    assert rc == -1 and "q range" in ffa.ffa_last_error()
