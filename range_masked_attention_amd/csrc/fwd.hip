@@ -434,7 +434,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
         }
       }
       // fp32 sum of the unrounded weights (the lse must hold to 1e-3 even
-      // for rows with a handful of keys), four independent chains
+      // for rows with a handful of keys), four independent chains.  (Summing
+      // the fp16-rounded weights of the training forward two at a time with
+      // v_dot2_f32_f16 would do for the lse, but measured slower than these
+      // adds.)
       u32x4 pw[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -544,15 +547,25 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
       }
     if (hh == 0)
       a.partial_lse[pr] = l > 0.f ? (m_run * a.score_mult + fast_log2(l)) * 0.69314718055994531f : -INFINITY;
-  } else if (row < a.Tq) {
-    const int64_t oo = ((int64_t)row * a.hq + head) * D;
-    if (a.out_lo) {
-      // out and what its rounding to bf16 left out (the backward forms
-      // rowsum(dO * out) from both)
+  } else {
+    // out (and with the saved record, what rounding it to bf16 left out,
+    // from which the backward forms rowsum(dO * out)) through LDS: each wave
+    // writes its 32 rows into the K and V buffers, now free, and reads them
+    // back a row at a time, so every global store writes whole 256-byte rows
+    // instead of 16 bytes of 32 rows.  16-byte chunks are XOR-swizzled with
+    // the row so that both the writes and the read-back spread over the banks.
+    constexpr int kRowB = 2 * D, kCh = D / 8, kRowsPer = 64 / kCh;
+    __syncthreads();  // every wave is done with the K and V tiles
+    char* so = reinterpret_cast<char*>(w < 2 ? kb0 : kb1) + (w & 1) * 32 * kRowB;
+    char* sl = reinterpret_cast<char*>(w < 2 ? vb0 : vb1) + (w & 1) * 32 * kRowB;
+    const bool lo = a.out_lo != nullptr;
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 4; ++j) {
+        const int c = 4 * db + j;  // chunk of dims 32 db + 8 j .. + 8
+        const int off = n * kRowB + ((c ^ (n % kCh)) << 4) + 8 * hh;
+        if (lo) {
           uint16_t h[4], l[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) split_bf16(o[db][4 * j + i] * inv, &h[i], &l[i]);
@@ -561,21 +574,30 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
           w2[1] = h[2] | (uint32_t)h[3] << 16;
           r2[0] = l[0] | (uint32_t)l[1] << 16;
           r2[1] = l[2] | (uint32_t)l[3] << 16;
-          *reinterpret_cast<u32x2*>(a.out + oo + 32 * db + 8 * j + 4 * hh) = w2;
-          *reinterpret_cast<u32x2*>(a.out_lo + oo + 32 * db + 8 * j + 4 * hh) = r2;
-        }
-    } else {
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
+          *reinterpret_cast<u32x2*>(so + off) = w2;
+          *reinterpret_cast<u32x2*>(sl + off) = r2;
+        } else {
           u32x2 w2;
           w2[0] = pack_bf16x2(o[db][4 * j + 0] * inv, o[db][4 * j + 1] * inv);
           w2[1] = pack_bf16x2(o[db][4 * j + 2] * inv, o[db][4 * j + 3] * inv);
-          *reinterpret_cast<u32x2*>(a.out + oo + 32 * db + 8 * j + 4 * hh) = w2;
+          *reinterpret_cast<u32x2*>(so + off) = w2;
         }
+      }
+    // read back (the same wave's rows: LDS keeps a wave's accesses in order)
+#pragma unroll
+    for (int i = 0; i < kCh / 2; ++i) {
+      const int r = i * kRowsPer + lane / kCh, c = lane % kCh;
+      const int off = r * kRowB + ((c ^ (r % kCh)) << 4);
+      const int64_t grow = (int64_t)q0 + w * 32 + r;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(so + off);
+      const int64_t go = (grow * a.hq + head) * D + c * 8;
+      if (grow < a.Tq) *reinterpret_cast<u32x4*>(a.out + go) = x;
+      if (lo) {
+        const u32x4 y = *reinterpret_cast<const u32x4*>(sl + off);
+        if (grow < a.Tq) *reinterpret_cast<u32x4*>(a.out_lo + go) = y;
+      }
     }
-    if (hh == 0) {
+    if (hh == 0 && row < a.Tq) {
       const float lse = l > 0.f ? (m_run * a.score_mult + fast_log2(l)) * 0.69314718055994531f : -INFINITY;
       a.lse[(int64_t)row * a.hq + head] = lse;
     }

@@ -122,10 +122,11 @@ def test_dummy_padding_bitwise():
 
 
 def test_training_forward_record():
-    """The training forward (saved record) runs P V with fp16 P: lse keeps its
-    bits, out is at least as close to the oracle as the plain forward's, and
-    the record holds out's rounding residual (at most half an ulp of out,
-    with out + residual closer still) and v's fp16 copy."""
+    """The training forward (saved record) runs P V with fp16 P: lse keeps
+    its bits (the row sum is of the unrounded weights either way), out is at
+    least as close to the oracle as the plain forward's, and the record holds
+    out's rounding residual (at most half an ulp of out, with out + residual
+    closer still) and v's fp16 copy."""
     w = W.config(2)
     say("fwd training record (config 2)")
     q, k, v, _ = W.workload_tensors(w, with_dout=False)
