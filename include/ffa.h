@@ -38,7 +38,10 @@
  *  - Environment: FFA_DEBUG=1 makes planning reject slice lists in which two
  *    slices cover one cell (FFA_ERR_INVALID_ARG); FFA_INJECT_NOMEM=1 makes
  *    every host-side planning step fail with FFA_ERR_NOMEM, for testing a
- *    caller's handling of that error.
+ *    caller's handling of that error; FFA_FWD_PAIRED=1 / =0 makes the
+ *    forward take two q heads per workgroup wherever q heads pair up within
+ *    a kv head, or never, instead of choosing by grid size (the results are
+ *    the same bits either way).
  *  - stream is a hipStream_t (NULL = the default stream).  Calls enqueue work
  *    and return; argument errors are reported synchronously before any GPU
  *    work is enqueued.  The return value is FFA_OK or a negative FFA_ERR_*;

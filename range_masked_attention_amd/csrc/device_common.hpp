@@ -104,7 +104,10 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
 
 // bf16 bits of x rounded to nearest even, and the bf16 bits of what that
 // rounding left out (x - hi, rounded again): together 16 significant bits.
+// x is the fp32 value as given: the subtraction is never fused with a
+// product that formed x, so every kernel gets the same residual.
 __device__ __forceinline__ void split_bf16(float x, uint16_t* hi, uint16_t* lo) {
+#pragma clang fp contract(off)
   const __bf16 h = (__bf16)x;
   const float r = x - (float)h;
   *hi = __builtin_bit_cast(uint16_t, h);

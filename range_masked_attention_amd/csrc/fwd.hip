@@ -37,6 +37,9 @@
 // the only rounding is that of slope * (j - i).
 #include <type_traits>
 
+#include <cstdlib>
+#include <cstring>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -61,6 +64,9 @@ constexpr int kFwdBalance = 512;
 constexpr int kFwdMinSteps = 64;
 constexpr int kFwdMaxSlots = 512;
 constexpr int kFwdMaxD = 128;
+// Two q heads per workgroup only with at least this many such workgroups
+// (two per CU): with fewer the chip is better filled one head each.
+constexpr int64_t kFwdPairMinWorkgroups = 512;
 
 struct FwdArgs {
   const __bf16* q;
@@ -110,15 +116,16 @@ struct FwdSmem {
 // (wg % 8); all q heads that share a kv head for one run go to the same XCD
 // on consecutive slots, so the K/V tiles they read are shared in that XCD's
 // L2.  Units (run, kv head) are spread over XCDs in plan order, longest list
-// first.
+// first.  A workgroup takes hpw consecutive q heads; `head` is the first.
 struct FwdItem {
   int qt, head, g, e_begin, e_end, slot;
 };
-__device__ __forceinline__ bool decode_item(const FwdArgs& a, FwdItem* it) {
+__device__ __forceinline__ bool decode_item(const FwdArgs& a, int hpw, FwdItem* it) {
   const int wg = blockIdx.x;
   const int xcd = wg & 7, slot = wg >> 3;
-  const int r = slot % a.grp;
-  const int u = (slot / a.grp) * 8 + xcd;
+  const int wgs = a.grp / hpw;  // workgroups per (run, kv head): hpw q heads each
+  const int r = slot % wgs;
+  const int u = (slot / wgs) * 8 + xcd;
   const int item = u / a.hkv;
   if (a.direct) {
     if (u >= a.n_units) return false;
@@ -135,7 +142,7 @@ __device__ __forceinline__ bool decode_item(const FwdArgs& a, FwdItem* it) {
     it->slot = run[3];
   }
   it->g = u % a.hkv;
-  it->head = it->g * a.grp + r;
+  it->head = it->g * a.grp + hpw * r;
   return true;
 }
 
@@ -143,12 +150,12 @@ __device__ __forceinline__ bool decode_item(const FwdArgs& a, FwdItem* it) {
 // the instruction's LDS base + 16 L; each lane fetches the global chunk that
 // belongs at that slot under the swizzle.  Rows past the end of the tensor
 // read as zeros (buffer range check).
-template <int D>
+template <int D, int NT>
 struct TileDma {
   using Smem = FwdSmem<D>;
-  static constexpr int kPerThread = kBN * Smem::kChunks / kThreads;  // 16-byte loads per thread
-  static constexpr int kRowsPerLoad = 64 / Smem::kChunks;            // rows one wave load covers
-  static_assert(kPerThread * kThreads == kBN * Smem::kChunks, "tile must split evenly");
+  static constexpr int kPerThread = kBN * Smem::kChunks / NT;  // 16-byte loads per thread
+  static constexpr int kRowsPerLoad = 64 / Smem::kChunks;      // rows one wave load covers
+  static_assert(kPerThread * NT == kBN * Smem::kChunks, "tile must split evenly");
 
   // Load c of wave w: lane L fills chunk slot P = (w * kPerThread + c) * 64 + L,
   // i.e. row (w * kPerThread + c) * kRowsPerLoad + L / kChunks, slot L % kChunks.
@@ -284,8 +291,12 @@ __device__ __forceinline__ void mask_tile(const DevSlice& sl, int ktile, int row
 // s_v, P enters the P V product in fp16 (11 significant bits instead of 8),
 // and the epilogue divides by s_v as well; the output then carries P's
 // rounding at 2^-12 instead of 2^-9, which the backward's row term D needs.
-template <int D, bool SOFTCAP, bool BIAS, bool F16>
-__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
+//
+// HPW q heads of one kv head per workgroup (four waves each, on the same q
+// tile): the heads share every K and V tile fetched into LDS, which halves
+// the fetches per product when two heads share a kv head.
+template <int D, bool SOFTCAP, bool BIAS, bool F16, int HPW>
+__global__ __launch_bounds__(kThreads * HPW, 2) void fwd_kernel(FwdArgs a) {
   using Smem = FwdSmem<D>;
   constexpr int KS = D / 16;  // k steps of the QK^T contraction
   constexpr int DB = D / 32;  // 32-wide blocks of the head dim in O^T
@@ -299,20 +310,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) __bf16 vb1[kTileElems];
 
   FwdItem item;
-  if (!decode_item(a, &item)) return;
-  const int qt = item.qt, head = item.head, g = item.g;
-
+  if (!decode_item(a, HPW, &item)) return;
   const int tid = threadIdx.x;
+  // w: wave of the workgroup (its share of each tile fetch); wq: its 32
+  // rows of the q tile, for head item.head + w / 4
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, n = lane & 31, hh = lane >> 5;
+  const int wq = w & 3;
+  const int qt = item.qt, head = item.head + (w >> 2), g = item.g;
   const int q0 = qt * kBM;
-  const int row = q0 + w * 32 + n;  // the query row this lane's column holds
+  const int row = q0 + wq * 32 + n;  // the query row this lane's column holds
   const int64_t q_row_bytes = (int64_t)a.hq * D * 2;
 
   // Q fragments (B operand of S^T = K Q^T): lane (n, hh) holds row `row`,
   // dims 16*ks + 8*hh .. +8
   bf16x8 qf[KS];
   {
-    const int64_t wrow0 = q0 + w * 32;
+    const int64_t wrow0 = q0 + wq * 32;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(
         a.q + (wrow0 * a.hq + head) * D, ((int64_t)a.Tq - wrow0) * q_row_bytes - (int64_t)head * D * 2);
 #pragma unroll
@@ -330,7 +343,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   // so the list is walked from its last key tile down: the first tiles then
   // set the running max and later ones rarely move it (walked upwards, every
   // tile would raise the max by slope * 64 and force a rescale of O)
-  const bool down = BIAS && sigma > 0.f;
+  // (one direction for the workgroup: that of its first head)
+  const bool down = BIAS && (HPW == 1 ? sigma > 0.f : const_load<float>(a.slopes, item.head) > 0.f);
   auto entry = [&](int j) { return plan_entry(a.entries, down ? e_end - 1 - j : e_begin + j); };
   // S^T of a tile: accumulators start from the bias (no softcap), or the
   // bias joins the softcap
@@ -358,7 +372,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
   const int v_sw = Smem::v_swz(v_krow);  // every key row read by this lane shares it
 
   if (n_tiles > 0) {
-    TileDma<D> dma;
+    TileDma<D, kThreads * HPW> dma;
     dma.init(a, g, lane);
     // ---- prologue: K0, V0 and K1 in LDS; S0 and its row max
     dma.load_k(entry(0).tile, kb0, w);
@@ -459,7 +473,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          if (i < 2 * TileDma<D>::kPerThread + 1)
+          if (i < 2 * TileDma<D, kThreads * HPW>::kPerThread + 1)
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // entry load, direct-to-LDS fetches
           if (i < 12) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, SOFTCAP ? 5 : 7, 0);  // VALU
@@ -556,47 +570,47 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(FwdArgs a) {
     // the row so that both the writes and the read-back spread over the banks.
     constexpr int kRowB = 2 * D, kCh = D / 8, kRowsPer = 64 / kCh;
     __syncthreads();  // every wave is done with the K and V tiles
-    char* so = reinterpret_cast<char*>(w < 2 ? kb0 : kb1) + (w & 1) * 32 * kRowB;
-    char* sl = reinterpret_cast<char*>(w < 2 ? vb0 : vb1) + (w & 1) * 32 * kRowB;
+    // this wave's 32 rows: one of the eight 8 KB halves of the four buffers
+    __bf16* const buf = (w >> 1) == 0 ? kb0 : (w >> 1) == 1 ? kb1 : (w >> 1) == 2 ? vb0 : vb1;
+    char* so = reinterpret_cast<char*>(buf) + (w & 1) * 32 * kRowB;
     const bool lo = a.out_lo != nullptr;
+    u32x2 hw[DB * 4], lw[DB * 4];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int c = 4 * db + j;  // chunk of dims 32 db + 8 j .. + 8
-        const int off = n * kRowB + ((c ^ (n % kCh)) << 4) + 8 * hh;
-        if (lo) {
-          uint16_t h[4], l[4];
+        uint16_t h[4], lr[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) split_bf16(o[db][4 * j + i] * inv, &h[i], &l[i]);
-          u32x2 w2, r2;
-          w2[0] = h[0] | (uint32_t)h[1] << 16;
-          w2[1] = h[2] | (uint32_t)h[3] << 16;
-          r2[0] = l[0] | (uint32_t)l[1] << 16;
-          r2[1] = l[2] | (uint32_t)l[3] << 16;
-          *reinterpret_cast<u32x2*>(so + off) = w2;
-          *reinterpret_cast<u32x2*>(sl + off) = r2;
-        } else {
-          u32x2 w2;
-          w2[0] = pack_bf16x2(o[db][4 * j + 0] * inv, o[db][4 * j + 1] * inv);
-          w2[1] = pack_bf16x2(o[db][4 * j + 2] * inv, o[db][4 * j + 3] * inv);
-          *reinterpret_cast<u32x2*>(so + off) = w2;
+        for (int i = 0; i < 4; ++i) {
+          if (lo) {
+            split_bf16(o[db][4 * j + i] * inv, &h[i], &lr[i]);
+          } else {
+            h[i] = __builtin_bit_cast(uint16_t, (__bf16)(o[db][4 * j + i] * inv));
+            lr[i] = 0;
+          }
         }
+        hw[4 * db + j][0] = h[0] | (uint32_t)h[1] << 16;
+        hw[4 * db + j][1] = h[2] | (uint32_t)h[3] << 16;
+        lw[4 * db + j][0] = lr[0] | (uint32_t)lr[1] << 16;
+        lw[4 * db + j][1] = lr[2] | (uint32_t)lr[3] << 16;
       }
-    // read back (the same wave's rows: LDS keeps a wave's accesses in order)
+    // one output through the region: this lane's pieces in, whole rows out
+    // (LDS carries out a wave's accesses in order, so the residual can follow
+    // out through the same region)
+    auto emit = [&](const u32x2* x, __bf16* dst) {
 #pragma unroll
-    for (int i = 0; i < kCh / 2; ++i) {
-      const int r = i * kRowsPer + lane / kCh, c = lane % kCh;
-      const int off = r * kRowB + ((c ^ (r % kCh)) << 4);
-      const int64_t grow = (int64_t)q0 + w * 32 + r;
-      const u32x4 x = *reinterpret_cast<const u32x4*>(so + off);
-      const int64_t go = (grow * a.hq + head) * D + c * 8;
-      if (grow < a.Tq) *reinterpret_cast<u32x4*>(a.out + go) = x;
-      if (lo) {
-        const u32x4 y = *reinterpret_cast<const u32x4*>(sl + off);
-        if (grow < a.Tq) *reinterpret_cast<u32x4*>(a.out_lo + go) = y;
+      for (int c = 0; c < 4 * DB; ++c)  // chunk c: dims 8 c .. + 8
+        *reinterpret_cast<u32x2*>(so + n * kRowB + ((c ^ (n % kCh)) << 4) + 8 * hh) = x[c];
+#pragma unroll
+      for (int i = 0; i < kCh / 2; ++i) {
+        const int r = i * kRowsPer + lane / kCh, c = lane % kCh;
+        const int64_t grow = (int64_t)q0 + wq * 32 + r;
+        const u32x4 y = *reinterpret_cast<const u32x4*>(so + r * kRowB + ((c ^ (r % kCh)) << 4));
+        if (grow < a.Tq) *reinterpret_cast<u32x4*>(dst + (grow * a.hq + head) * D + c * 8) = y;
       }
-    }
+    };
+    emit(hw, a.out);
+    if (lo) emit(lw, a.out_lo);
     if (hh == 0 && row < a.Tq) {
       const float lse = l > 0.f ? (m_run * a.score_mult + fast_log2(l)) * 0.69314718055994531f : -INFINITY;
       a.lse[(int64_t)row * a.hq + head] = lse;
@@ -649,6 +663,30 @@ __global__ __launch_bounds__(kThreads) void fwd_combine_kernel(FwdArgs a) {
     }
     if (c == 0) a.lse[row * a.hq + head] = sum > 0.f ? m + fast_log2(sum) * 0.69314718055994531f : -INFINITY;
   }
+}
+
+// FFA_FWD_PAIRED=1 makes the forward take two q heads per workgroup
+// wherever q heads pair up within a kv head, =0 never (for tests and
+// measurements); unset, the grid size decides.
+int paired_mode() {
+  const char* s = std::getenv("FFA_FWD_PAIRED");
+  if (!s || !*s) return -1;
+  return std::strcmp(s, "0") != 0 ? 1 : 0;
+}
+
+// Launch of fwd_kernel over n_units (work item, kv head) units: two q heads
+// per workgroup (eight waves, one workgroup per CU) when heads pair up and
+// the pairs still fill the chip twice over, else one.
+template <int D, bool SC, bool BIAS, bool F16>
+void launch_fwd_kernel(const FwdArgs& a, int64_t n_units, hipStream_t stream) {
+  const int64_t n8 = ((n_units + 7) / 8) * 8;
+  const int mode = paired_mode();
+  const bool pairs = a.grp % 2 == 0;
+  if (pairs && (mode == 1 || (mode < 0 && n_units * (a.grp / 2) >= kFwdPairMinWorkgroups)))
+    hipLaunchKernelGGL((fwd_kernel<D, SC, BIAS, F16, 2>), dim3((unsigned)(n8 * (a.grp / 2))), dim3(2 * kThreads), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<D, SC, BIAS, F16, 1>), dim3((unsigned)(n8 * a.grp)), dim3(kThreads), 0, stream, a);
 }
 
 template <int D, bool SC, bool BIAS, bool F16>
@@ -718,8 +756,7 @@ hipError_t launch_fwd_t(const FwdLaunch& p, hipStream_t stream) {
     // no list can be cut: one work item per q tile, straight from the plan
     a.direct = 1;
     a.n_units = (int32_t)(n_qt * p.hkv);
-    const int64_t n_wg = ((a.n_units + 7) / 8) * 8 * (int64_t)a.grp;
-    hipLaunchKernelGGL((fwd_kernel<D, SC, BIAS, F16>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream, a);
+    launch_fwd_kernel<D, SC, BIAS, F16>(a, a.n_units, stream);
     return hipGetLastError();
   }
   a.direct = 0;
@@ -739,9 +776,7 @@ hipError_t launch_fwd_t(const FwdLaunch& p, hipStream_t stream) {
   sp.splits_cap = caps.splits;
   sp.counts = reinterpret_cast<int32_t*>(ws + S.counts);
   launch_split(sp, stream);
-  const int64_t n_units = caps.items * p.hkv;
-  const int64_t n_wg = ((n_units + 7) / 8) * 8 * (int64_t)a.grp;
-  hipLaunchKernelGGL((fwd_kernel<D, SC, BIAS, F16>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream, a);
+  launch_fwd_kernel<D, SC, BIAS, F16>(a, caps.items * p.hkv, stream);
   hipLaunchKernelGGL((fwd_combine_kernel<D>), dim3((unsigned)(caps.splits * p.hq)), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
