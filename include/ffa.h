@@ -80,6 +80,15 @@ enum {
  * (rows nothing sees included).  Deterministic: the same inputs give the
  * same bits, also when empty slices are added anywhere or the slices are
  * permuted.
+ *
+ * Precision.  QK^T runs on bf16 operands, P V on fp16 ones, both with fp32
+ * accumulation.  fp16 gives the probabilities 11 significant bits instead of
+ * bf16's 8: each enters P V rounded while out is divided by the sum of the
+ * unrounded ones, which with bf16 can move out by up to 2^-9 max |v|.  v is
+ * copied to fp16 first (exact: at scale 1 when max |v| lies in [2^-3, 16),
+ * else times the power of two that maps max |v| into [8, 16)), into
+ * stream-ordered device memory (2 Tk hkv d bytes) allocated on `stream` and
+ * released after the kernel.
  */
 int ffa_fwd(const void* q, const void* k, const void* v,
             int64_t Tq, int64_t Tk, int hq, int hkv, int d,
@@ -144,13 +153,16 @@ int ffa_bwd(const void* q, const void* k, const void* v,
  *
  * Same arguments, results (bitwise) and errors as ffa_fwd, and it allocates
  * nothing: the slice arrays' device copy, the block-sparse plan (built on
- * the device from that copy) and the forward's run scratch live in one
- * 64 MiB device array of the library's (each GPU holds its own copy from the
- * first call on it until the process ends).  The slice arrays are copied to
- * it with hipMemcpyAsync on `stream`.  Limits, checked on the host before
- * any GPU work (FFA_ERR_INVALID_ARG): at most 4096 slices, and the plan must
- * fit the array: about 4 million (q tile, key tile, slice) entries at
- * Tq = 64K, fewer as Tq grows (the message gives both counts).  Overlapping
+ * the device from that copy), the forward's run scratch and the fp16 copy of
+ * v live in one 256 MiB device array of the library's (each GPU holds its
+ * own copy from the first call on it until the process ends).  The slice
+ * arrays are copied to it with hipMemcpyAsync on `stream`.  Limits, checked
+ * on the host before any GPU work (FFA_ERR_INVALID_ARG): at most 4096
+ * slices, v's fp16 copy (2 Tk hkv d bytes) and the run scratch (about
+ * 32 MiB) must fit the array, and the plan must fit what is left: about
+ * 10 million (q tile, key tile, slice) entries at Tk hkv d = 64M (the
+ * 64K-token, 8-kv-head, d = 128 size), more for smaller v (the message gives
+ * the counts).  Overlapping
  * slices are not looked for under FFA_DEBUG.  All calls on one GPU share the
  * array: calls that overlap in time on one GPU (different streams, or
  * different host threads) race and must not be made.
@@ -183,13 +195,10 @@ int ffa_fwd_noalloc(const void* q, const void* k, const void* v,
  * can save what that backward needs:
  *   saved         DEVICE memory of ffa_saved_size(Tq, Tk, hq, hkv, d) bytes,
  *                 16-byte aligned, or NULL (the plain forward).  With it the
- *                 forward first copies v to fp16 (times the power of two
- *                 that maps its range onto fp16's: exact) into the record,
- *                 runs P V with P in fp16 (11 significant bits, not bf16's
- *                 8), and stores out's bf16 rounding residual bf16(x - out)
- *                 for each fp32 result x; out and lse are written as usual
- *                 (out may differ from the plain forward's in the last bit,
- *                 being more accurate).
+ *                 forward puts v's fp16 copy (see Precision under ffa_fwd)
+ *                 into the record instead of temporary memory, and stores
+ *                 out's bf16 rounding residual bf16(x - out) for each fp32
+ *                 result x; out and lse are the plain forward's bits.
  * The _ex backward takes the record (NULL: re-run the training forward to
  * get one, see ffa_bwd) and forms D = rowsum(dout * (out + residual)) from
  * it, reusing the fp16 v.  A record belongs to the q, k, v, slices, scale,
@@ -204,8 +213,9 @@ int ffa_fwd_ex(const void* q, const void* k, const void* v,
                void* out, float* lse, void* saved, void* stream);
 
 /* Bytes of the training forward's saved record (0 for invalid sizes): a
- * 256-byte header, out's residual (2 bytes per element of q) and the fp16
- * copy of v (2 bytes per element of v), each 256-byte aligned. */
+ * 256-byte header, out's residual (2 bytes per element of q), the fp16 copy
+ * of v (2 bytes per element of v), each 256-byte aligned, and 8 KiB of
+ * scratch for the pass that makes the copy. */
 size_t ffa_saved_size(int64_t Tq, int64_t Tk, int hq, int hkv, int d);
 
 int ffa_bwd_ex(const void* q, const void* k, const void* v,
@@ -300,8 +310,14 @@ int ffa_plan_create(int64_t Tq, int64_t Tk,
                     const int32_t* attn_type_map, int R,
                     void* stream, ffa_plan_t* plan);
 
-/* ffa_fwd with a plan from ffa_plan_create: launches the forward kernel only
- * (no host planning, no copy, no allocation).  Tensors as for ffa_fwd. */
+/* ffa_fwd with a plan from ffa_plan_create: launches the forward kernels
+ * only (no host planning, no host copy).  Tensors as for ffa_fwd.  The fp16
+ * copy of v that the kernel reads goes to room the plan keeps for it
+ * (2 Tk hkv d bytes and 8.25 KiB): allocated stream-ordered on `stream` by the
+ * first call that needs it (or needs more), and freed by ffa_plan_destroy.
+ * With a saved record (ffa_fwd_planned_ex) the copy goes to the record
+ * instead and nothing is allocated; ffa_fwd_noalloc allocates nothing
+ * either. */
 int ffa_fwd_planned(ffa_plan_t plan,
                     const void* q, const void* k, const void* v,
                     int hq, int hkv, int d, float scale, float softcap,
@@ -338,7 +354,8 @@ int ffa_bwd_planned_ex(ffa_plan_t plan,
 
 /* Release a plan: its device memory is freed in order on `stream`, after the
  * work already enqueued there (a plan from ffa_plan_create_device lives in
- * the caller's workspace, which is left alone).  NULL is a no-op. */
+ * the caller's workspace, which is left alone; its room for v's fp16 copy,
+ * if a forward allocated one, is freed).  NULL is a no-op. */
 int ffa_plan_destroy(ffa_plan_t plan, void* stream);
 
 /*
@@ -349,8 +366,10 @@ int ffa_plan_destroy(ffa_plan_t plan, void* stream);
  * same tile order) with kernels that read those arrays in device memory: no
  * host copy, no synchronisation, no allocation.  ffa_plan_refresh re-runs
  * the build on the current contents of the same arrays, so a sequence
- * "refresh, forward, backward" can be captured once in a HIP graph and
- * replayed for every new slice list of the same length.
+ * "refresh, forward into a saved record, backward on that record" (calls
+ * that allocate nothing when given the record and a workspace) can be
+ * captured once in a HIP graph and replayed for every new slice list of the
+ * same length.
  *
  * q_ranges [R][2], k_ranges [R][2], attn_type_map [R]: DEVICE int32 arrays,
  *            4-byte aligned, read by every build; they must stay valid

@@ -80,7 +80,8 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const u32x4* __restr
                                                           int64_t Tq, int hq) {
   constexpr int kL = D / 8;  // lanes per (row, head)
   const float sq = range_scale(range[kRgQ], kRangeQ), sk = range_scale(range[kRgK], kRangeK);
-  const float sv = range_scale(vwords[kRgV], kRangeV), sdo = range_scale(range[kRgDO], kRangeDO);
+  const float sv = copy_scale(vwords[kRgV], kRangeV);
+  const float sdo = range_scale(range[kRgDO], kRangeDOV - range_top(vwords[kRgV], sv));
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (i == 0) {
     scales[kRgQ] = sq;

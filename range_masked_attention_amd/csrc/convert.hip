@@ -1,11 +1,16 @@
 // fp16 operand copies for the products that need more than bf16's 8
-// significant bits (the training forward's P V, every backward product).
+// significant bits (the forward's P V, every backward product).
 //
 // A tensor is copied to fp16 times s = 2^e, the power of two that maps its
 // largest |x| into [2^(L-1), 2^L) (range_scale): exact, since a bf16 value
 // has 8 significant bits and fp16 keeps 11, for every value down to 2^-14 of
 // 2^L; below that fp16 rounds at 2^-25 of 2^L.  The largest |x| comes from a
-// grid-stride pass (one atomic per wave and tensor) before the copy.
+// grid-stride pass (one atomic per workgroup and tensor) before the copy.
+// v's copy instead takes scale 1 whenever its range allows (copy_scale), is
+// made in the pass that finds its range (partial maxima per workgroup, no
+// atomics), and is redone only when it does not.
+#include <algorithm>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -64,6 +69,59 @@ __global__ __launch_bounds__(kThreads) void range_max_kernel(RangeJob job) {
   }
 }
 
+// The largest of m over a workgroup's threads, in every thread.
+__device__ __forceinline__ uint32_t block_max(uint32_t m) {
+  __shared__ uint32_t wmax[kThreads / 64];
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  uint32_t b = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) b = max(b, wmax[w]);
+  return b;
+}
+
+// v's copy, first pass: dst = fp16(src) at scale 1, two chunks in flight per
+// thread, and parts[workgroup] = fp32 bits of the largest |src| it saw.
+__global__ __launch_bounds__(kThreads) void convert_track_kernel(const u32x4* __restrict__ src,
+                                                                u32x4* __restrict__ dst, int64_t n,
+                                                                uint32_t* __restrict__ parts) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  uint32_t m = 0;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + stride < n; i += 2 * stride) {
+    const u32x4 a = src[i], b = src[i + stride];
+    m = max(m, max(max_mag16(a), max_mag16(b)));
+    dst[i] = to_f16x8(a, 1.0f);
+    dst[i + stride] = to_f16x8(b, 1.0f);
+  }
+  if (i < n) {
+    const u32x4 a = src[i];
+    m = max(m, max_mag16(a));
+    dst[i] = to_f16x8(a, 1.0f);
+  }
+  m = block_max(m);
+  if (threadIdx.x == 0) parts[blockIdx.x] = m << 16;
+}
+
+// v's copy, second pass: max |src| from the first pass's n_parts partial
+// maxima (every workgroup reduces them; workgroup 0 also writes the range
+// words), then the copy redone at copy_scale where that is not 1 (a range
+// outside [2^-3, 2^L)); otherwise every workgroup returns there.
+__global__ __launch_bounds__(kThreads) void convert_fix_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                              int64_t n, const uint32_t* __restrict__ parts,
+                                                              int n_parts, uint32_t* __restrict__ words, int word,
+                                                              int L) {
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < n_parts; i += kThreads) m = max(m, parts[i]);
+  m = block_max(m);
+  if (blockIdx.x == 0 && threadIdx.x < 4) words[threadIdx.x] = (int)threadIdx.x == word ? m : 0u;
+  const float s = copy_scale(m, L);
+  if (s == 1.0f) return;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) dst[i] = to_f16x8(src[i], s);
+}
+
 // dst = fp16(src * s), s from words[word] and range bound L.
 __global__ __launch_bounds__(kThreads) void convert_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                           int64_t n, const uint32_t* __restrict__ words, int word,
@@ -101,6 +159,21 @@ void launch_convert(const void* src, void* dst, int64_t chunks, const uint32_t* 
                      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), chunks, words, word, L);
 }
 
+void launch_convert_tracked(const void* src, void* dst, int64_t chunks, uint32_t* parts, uint32_t* words, int word,
+                            int L, hipStream_t stream) {
+  // two chunks per thread and step: about 4 steps per thread at the largest
+  // sizes, and at least a few workgroups per CU on small tensors; the
+  // second pass, which copies again only for a range outside its window,
+  // takes one workgroup per CU
+  const unsigned g = (unsigned)grid_for((chunks + 1) / 2, kVRangeParts);
+  if (chunks > 0)
+    hipLaunchKernelGGL(convert_track_kernel, dim3(g), dim3(kThreads), 0, stream, static_cast<const u32x4*>(src),
+                       static_cast<u32x4*>(dst), chunks, parts);
+  hipLaunchKernelGGL(convert_fix_kernel, dim3(chunks > 0 ? std::min(g, 256u) : 1u), dim3(kThreads), 0, stream,
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), chunks,
+                     static_cast<const uint32_t*>(parts), chunks > 0 ? (int)g : 0, words, word, L);
+}
+
 SavedLayout saved_layout(int64_t Tq, int64_t Tk, int hq, int hkv, int d) {
   auto r256 = [](size_t x) { return (x + 255) & ~size_t(255); };
   SavedLayout L{};
@@ -113,6 +186,8 @@ SavedLayout saved_layout(int64_t Tq, int64_t Tk, int hq, int hkv, int d) {
   off += r256(nq * 2);
   L.v16 = off;
   off += r256(nk * 2);
+  L.parts = off;
+  off += r256((size_t)kVRangeParts * 4);
   L.total = off;
   return L;
 }

@@ -127,13 +127,35 @@ __device__ __forceinline__ float range_scale(uint32_t max_bits, int L) {
   return __uint_as_float((uint32_t)(se + 127) << 23);
 }
 
+// Scale of v's fp16 copy: 1 when max |v| already lies in [2^-3, 2^L) (the
+// copy at scale 1 is then exact for every value from 2^-17 up, and what lies
+// below rounds at 2^-25, under 2^-22 of max |v|), else range_scale.  The
+// copy is made at scale 1 in the same pass that finds max |v| and redone only
+// outside that window.
+__device__ __forceinline__ float copy_scale(uint32_t max_bits, int L) {
+  const uint32_t lo = (uint32_t)(127 - 3) << 23, hi = (uint32_t)(127 + L) << 23;
+  return (max_bits >= lo && max_bits < hi) ? 1.0f : range_scale(max_bits, L);
+}
+
 // Range bounds L (largest |x| mapped into [2^(L-1), 2^L)) of the fp16
-// operand copies: 15 for q and k; for v and dO 4 and 3, which also keep
-// |dS| = P |dP - D| below 2^15 in the backward (|dP| <= d max|dO| max|v| <
+// operand copies: 15 for q and k, 4 for v (bounding it; copy_scale may leave
+// it lower).  dO's bound is kRangeDOV - (v's): max |dO| max |v| after
+// scaling lies in [2^5, 2^7) whatever v's scale, which keeps |dS| =
+// P |dP - D| below 2^15 in the backward (|dP| <= d max|dO| max|v| <
 // 128 * 2^7, and |D| <= max |dP| since D is a convex combination of a row's
-// dP).  Word slots of the ranges in a range-word array.
-constexpr int kRangeQ = 15, kRangeK = 15, kRangeV = 4, kRangeDO = 3;
+// dP) and as far above fp16's subnormal range as that allows.  Word slots
+// of the ranges in a range-word array.
+constexpr int kRangeQ = 15, kRangeK = 15, kRangeV = 4, kRangeDOV = 7;
 enum { kRgQ = 0, kRgK = 1, kRgV = 2, kRgDO = 3 };
+
+// L with max_abs * s in [2^(L-1), 2^L), for the fp32 bits of a non-negative
+// finite max_abs and a power of two s (L = kRangeV for 0).
+__device__ __forceinline__ int range_top(uint32_t max_bits, float s) {
+  if (max_bits == 0) return kRangeV;
+  int e = (int)(max_bits >> 23);  // max in [2^(e-127), 2^(e-126)) for e > 0
+  if (e == 0) e = 1;
+  return e - 126 + (int)((__float_as_uint(s) >> 23) & 0xFF) - 127;
+}
 
 // 8 bf16 values times s (a power of two) to fp16, round to nearest even.
 __device__ __forceinline__ u32x4 to_f16x8(u32x4 w, float s) {

@@ -217,6 +217,10 @@ struct ffa_plan_s {
   unsigned char* dev = nullptr;
   size_t bytes = 0;
   size_t off_fwd_scratch = 0;  // the forward's scratch (fwd_scratch_layout), after the lists
+  // room for v's fp16 copy for forwards without a saved record: allocated by
+  // the first that needs it (or more room), freed with the plan
+  mutable unsigned char* v16 = nullptr;
+  mutable size_t v16_bytes = 0;
   // host-built plans: the caller's index of each slice in the device table
   std::vector<int32_t> slice_index;
   // plans built on the device: the planner's arguments (re-run by
@@ -311,7 +315,11 @@ int plan_create(int64_t Tq, int64_t Tk, const int32_t* qr, const int32_t* kr, co
 int plan_destroy(ffa_plan_s* p, hipStream_t stream) {
   if (!p) return FFA_OK;
   hipError_t e = hipSuccess;
-  if (p->dev && !p->on_device) e = hipFreeAsync(p->dev, stream);
+  if (p->v16) e = hipFreeAsync(p->v16, stream);
+  if (p->dev && !p->on_device) {
+    const hipError_t ef = hipFreeAsync(p->dev, stream);
+    if (e == hipSuccess) e = ef;
+  }
   delete p;
   if (e != hipSuccess) return hip_fail(e, "hipFreeAsync(plan)");
   return FFA_OK;
@@ -348,6 +356,25 @@ int fwd_planned(const ffa_plan_s* p, const void* q, const void* k, const void* v
   L.scratch = p->dev + p->off_fwd_scratch;
   L.n_entries = p->fwd.n_entries;
   L.max_len = p->fwd.max_len;
+  // without a record, the fp16 copy of v goes to the plan's room for it
+  if (!saved) {
+    const size_t need = ffa::fwd_v16_bytes(p->Tk, hkv, d);
+    if (p->v16_bytes < need) {
+      if (p->v16) {
+        const hipError_t ef = hipFreeAsync(p->v16, stream);
+        p->v16 = nullptr;
+        p->v16_bytes = 0;
+        if (ef != hipSuccess) return hip_fail(ef, "hipFreeAsync(v16)");
+      }
+      const hipError_t ea = hipMallocAsync(reinterpret_cast<void**>(&p->v16), need, stream);
+      if (ea != hipSuccess) {
+        p->v16 = nullptr;
+        return fail(FFA_ERR_NOMEM, std::string("hipMallocAsync(v16): ") + hipGetErrorString(ea));
+      }
+      p->v16_bytes = need;
+    }
+    L.v16 = p->v16;
+  }
   hipError_t e = ffa::launch_fwd(L, stream);
   if (e != hipSuccess) return hip_fail(e, "forward kernel launch");
   return FFA_OK;

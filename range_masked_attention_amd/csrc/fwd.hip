@@ -287,10 +287,11 @@ __device__ __forceinline__ void mask_tile(const DevSlice& sl, int ktile, int row
     }
 }
 
-// F16 (the training forward): v is the fp16 copy of v times its range scale
-// s_v, P enters the P V product in fp16 (11 significant bits instead of 8),
-// and the epilogue divides by s_v as well; the output then carries P's
-// rounding at 2^-12 instead of 2^-9, which the backward's row term D needs.
+// F16 (every forward the library launches): v is the fp16 copy of v times
+// its range scale s_v, P enters the P V product in fp16 (11 significant bits
+// instead of 8), and the epilogue divides by s_v as well; the output then
+// carries P's rounding at 2^-12 instead of 2^-9, which both out's accuracy
+// and the backward's row term D need.
 //
 // HPW q heads of one kv head per workgroup (four waves each, on the same q
 // tile): the heads share every K and V tile fetched into LDS, which halves
@@ -543,7 +544,7 @@ __global__ __launch_bounds__(kThreads * HPW, 2) void fwd_kernel(FwdArgs a) {
   const float l_part = (l4[0] + l4[1]) + (l4[2] + l4[3]);
   const float l = l_part + __shfl_xor(l_part, 32);
   float inv = l > 0.f ? 1.0f / l : 0.f;
-  if constexpr (F16) inv *= 1.0f / range_scale(const_load<uint32_t>(a.v_words, kRgV), kRangeV);
+  if constexpr (F16) inv *= 1.0f / copy_scale(const_load<uint32_t>(a.v_words, kRgV), kRangeV);
   if (item.slot >= 0) {
     // one run of a split q tile: fp32 output and lse for fwd_combine
     const int64_t pr = ((int64_t)item.slot * a.hq + head) * kBM + (row - q0);
@@ -700,23 +701,29 @@ hipError_t launch_fwd_t(const FwdLaunch& p, hipStream_t stream) {
   a.out_lo = nullptr;
   a.v_words = nullptr;
   if constexpr (F16) {
-    // the record for the backward: v's range, its fp16 copy (read below as
-    // v), out's rounding residual
-    const SavedLayout S = saved_layout(p.Tq, p.Tk, p.hq, p.hkv, D);
-    unsigned char* sv = static_cast<unsigned char*>(p.saved);
-    uint32_t* words = reinterpret_cast<uint32_t*>(sv + S.words);
+    // v's range and fp16 copy (read below as v): in the record for the
+    // backward, with out's rounding residual, or in the caller's room for
+    // them (fwd_v16_bytes), without a residual
+    unsigned char* v16 = nullptr;
+    uint32_t* words = nullptr;
+    uint32_t* parts = nullptr;
+    if (p.saved) {
+      const SavedLayout S = saved_layout(p.Tq, p.Tk, p.hq, p.hkv, D);
+      unsigned char* sv = static_cast<unsigned char*>(p.saved);
+      words = reinterpret_cast<uint32_t*>(sv + S.words);
+      v16 = sv + S.v16;
+      parts = reinterpret_cast<uint32_t*>(sv + S.parts);
+      a.out_lo = reinterpret_cast<__bf16*>(sv + S.out_lo);
+    } else {
+      if (!p.v16) return hipErrorInvalidValue;
+      unsigned char* room = static_cast<unsigned char*>(p.v16);
+      words = reinterpret_cast<uint32_t*>(room);
+      v16 = room + 256;
+      parts = reinterpret_cast<uint32_t*>(room + fwd_v16_parts(p.Tk, p.hkv, D));
+    }
     const int64_t nk = p.Tk * p.hkv * D / 8;
-    launch_range_clear(words, 4, stream);
-    RangeJob job{};
-    job.n = 1;
-    job.src[0] = p.v;
-    job.chunks[0] = nk;
-    job.word[0] = kRgV;
-    job.words = words;
-    launch_range_max(job, stream);
-    launch_convert(p.v, sv + S.v16, nk, words, kRgV, kRangeV, stream);
-    a.v = reinterpret_cast<const __bf16*>(sv + S.v16);
-    a.out_lo = reinterpret_cast<__bf16*>(sv + S.out_lo);
+    launch_convert_tracked(p.v, v16, nk, parts, words, kRgV, kRangeV, stream);
+    a.v = reinterpret_cast<const __bf16*>(v16);
     a.v_words = words;
   }
   a.entries = reinterpret_cast<const DevEntry*>(p.entries);
@@ -806,6 +813,15 @@ FwdScratchLayout fwd_scratch_layout(int64_t Tq) {
   return L;
 }
 
+size_t fwd_v16_parts(int64_t Tk, int hkv, int d) {
+  const size_t nk = (size_t)(Tk > 0 ? Tk : 0) * (size_t)(hkv > 0 ? hkv : 0) * (size_t)(d > 0 ? d : 0);
+  return 256 + round256(nk * 2);
+}
+
+size_t fwd_v16_bytes(int64_t Tk, int hkv, int d) {
+  return fwd_v16_parts(Tk, hkv, d) + round256((size_t)kVRangeParts * 4);
+}
+
 int fwd_tile_rows() { return kBM; }
 int fwd_tile_cols() { return kBN; }
 
@@ -816,9 +832,15 @@ hipError_t launch_fwd_df(const FwdLaunch& p, hipStream_t stream) {
   return sc ? launch_fwd_t<D, true, false, F16>(p, stream) : launch_fwd_t<D, false, false, F16>(p, stream);
 }
 
+// Every forward runs P V on fp16 operands (the bf16 path stays in the
+// kernel template, unused).  Each weight enters P V rounded (relative error
+// up to half an ulp) while the row sum that divides out is of the unrounded
+// weights, so out can be off by up to that half ulp times max |v|: 2^-9 for
+// bf16, which with out's own rounding comes near 2e-2 for |v| around 6,
+// against 2^-12 for fp16.
 template <int D>
 hipError_t launch_fwd_d(const FwdLaunch& p, hipStream_t stream) {
-  return p.saved ? launch_fwd_df<D, true>(p, stream) : launch_fwd_df<D, false>(p, stream);
+  return launch_fwd_df<D, true>(p, stream);
 }
 
 hipError_t launch_fwd(const FwdLaunch& p, hipStream_t stream) {

@@ -15,14 +15,25 @@ struct HostDevEntry {
   int32_t meta;  // slice << 1 | partial
 };
 
+// Workgroups of the pass that copies v to fp16: each leaves the largest |v|
+// it saw in a slot of its own (kVRangeParts words after the copy).
+constexpr int kVRangeParts = 2048;
+
 // What the training forward saves for the backward (device memory of
 // saved_layout(...).total bytes): range words (word kRgV: fp32 bits of
-// max |v|), out's bf16 rounding residual [Tq][hq][d], and the fp16 copy of v
-// [Tk][hkv][d] that the forward's P V product read (times its range scale).
+// max |v|), out's bf16 rounding residual [Tq][hq][d], the fp16 copy of v
+// [Tk][hkv][d] that the forward's P V product read (times its scale), and
+// the copy pass's partial maxima.
 struct SavedLayout {
-  size_t words, out_lo, v16, total;
+  size_t words, out_lo, v16, parts, total;
 };
 SavedLayout saved_layout(int64_t Tq, int64_t Tk, int hq, int hkv, int d);
+
+// Room for the forward's fp16 copy of v (P V runs in fp16) when it saves no
+// record: v's range words (256 bytes), the copy [Tk][hkv][d], then the copy
+// pass's partial maxima (fwd_v16_parts: the byte offset of those).
+size_t fwd_v16_bytes(int64_t Tk, int hkv, int d);
+size_t fwd_v16_parts(int64_t Tk, int hkv, int d);
 
 // fp16 operand copies (convert.hip): largest |x| of up to four bf16 tensors
 // into range words, then copies scaled by their range scale.
@@ -37,6 +48,11 @@ void launch_range_clear(uint32_t* words, int n, hipStream_t stream);
 void launch_range_max(const RangeJob& job, hipStream_t stream);
 void launch_convert(const void* src, void* dst, int64_t chunks, const uint32_t* words, int word, int L,
                     hipStream_t stream);
+// v's copy: dst = fp16(src * copy_scale) in one pass where that scale is
+// 1, two otherwise; words[0..3] = 0 but words[word] = fp32 bits of max |src|.
+// parts: kVRangeParts words of scratch.
+void launch_convert_tracked(const void* src, void* dst, int64_t chunks, uint32_t* parts, uint32_t* words, int word,
+                            int L, hipStream_t stream);
 
 struct FwdLaunch {
   const void* q;
@@ -44,7 +60,8 @@ struct FwdLaunch {
   const void* v;
   void* out;
   float* lse;
-  void* saved = nullptr;  // device, saved_layout(): filled for the backward (P V then runs in fp16), or null
+  void* saved = nullptr;  // device, saved_layout(): filled for the backward, or null
+  void* v16 = nullptr;    // device, fwd_v16_bytes(): room for v's fp16 copy when saved is null
   int64_t Tq, Tk;
   int hq, hkv, d;
   float scale, softcap;

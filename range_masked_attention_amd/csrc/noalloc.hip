@@ -5,7 +5,8 @@
 //
 // The array holds a copy of the slice arrays, the block-sparse plan built
 // from them on the device (the device planner of plan_device.hip, forward
-// list only) and the forward's run scratch.  Each GPU has its own copy of
+// list only), the forward's run scratch and the fp16 copy of v that its
+// P V product reads.  Each GPU has its own copy of
 // the array; its address comes from hipGetSymbolAddress once per device.
 // Calls on one GPU share it, so calls that overlap on one GPU race.
 #include <hip/hip_runtime.h>
@@ -19,7 +20,7 @@
 
 namespace ffa {
 
-constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+constexpr size_t kNoAllocScratchBytes = size_t(256) << 20;
 
 static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
@@ -50,11 +51,11 @@ hipError_t scratch_ptr(void** out) {
 
 // Layout of the array for one call (byte offsets, 256-byte aligned).
 struct NoAllocLayout {
-  size_t status, qr, kr, ty, slices, rank, row_ptr, order, count, key, glen, entries, fwd, total;
+  size_t status, qr, kr, ty, slices, rank, row_ptr, order, count, key, glen, entries, fwd, v16, total;
   int64_t cap;  // entries the rest of the array holds
 };
 
-NoAllocLayout layout(int64_t Tq, int R) {
+NoAllocLayout layout(int64_t Tq, int64_t Tk, int hkv, int d, int R) {
   NoAllocLayout L{};
   const size_t r = (size_t)(R > 0 ? R : 1);
   const size_t nt = (size_t)((Tq + fwd_tile_rows() - 1) / fwd_tile_rows());
@@ -71,6 +72,7 @@ NoAllocLayout layout(int64_t Tq, int R) {
   L.key = off; off += r256((nt > 0 ? nt : 1) * 4);
   L.glen = off; off += r256((nt > 0 ? nt : 1) * 4);
   L.fwd = off; off += r256(fwd_scratch_layout(Tq).total);
+  L.v16 = off; off += r256(fwd_v16_bytes(Tk, hkv, d));
   L.entries = off;
   L.cap = off < kNoAllocScratchBytes ? (int64_t)((kNoAllocScratchBytes - off) / sizeof(HostDevEntry)) : -1;
   L.total = kNoAllocScratchBytes;
@@ -119,7 +121,12 @@ extern "C" int ffa_fwd_noalloc(const void* q, const void* k, const void* v, int6
   if (R > plan_device_max_slices())
     return ffa_abi::fail(FFA_ERR_INVALID_ARG, "ffa_fwd_noalloc takes at most " +
                                                   std::to_string(plan_device_max_slices()) + " slices");
-  const NoAllocLayout L = layout(Tq, R);
+  const NoAllocLayout L = layout(Tq, Tk, hkv, d, R);
+  if (L.cap < 0)
+    return ffa_abi::fail(FFA_ERR_INVALID_ARG,
+                         "ffa_fwd_noalloc: the fp16 copy of v and the run scratch need " + std::to_string(L.entries) +
+                             " bytes; its " + std::to_string(kNoAllocScratchBytes >> 20) + " MiB device array holds " +
+                             std::to_string(kNoAllocScratchBytes));
   const int64_t need = forward_entries(q_ranges, k_ranges, attn_type_map, R);
   if (L.cap < 0 || need > L.cap)
     return ffa_abi::fail(FFA_ERR_INVALID_ARG,
@@ -174,6 +181,7 @@ extern "C" int ffa_fwd_noalloc(const void* q, const void* k, const void* v, int6
   F.order = pp.order;
   F.slices = P.slices;
   F.scratch = b + L.fwd;
+  F.v16 = b + L.v16;
   e = launch_fwd(F, st);
   if (e != hipSuccess) return ffa_abi::fail(FFA_ERR_HIP, std::string("forward kernel launch: ") + hipGetErrorString(e));
   return FFA_OK;

@@ -148,7 +148,8 @@ def test_alibi_slopes_validation(lib):
 
 def test_saved_record_validation(lib):
     """A misaligned saved-record pointer is rejected before any GPU work, and
-    the record's size is its header plus 2 bytes per element of q and of v."""
+    the record's size is its header plus 2 bytes per element of q and of v,
+    plus the v copy pass's 2048 partial maxima."""
     ip = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     qr = np.array([[0, 4]], np.int32); kr = np.array([[0, 4]], np.int32); ty = np.array([1], np.int32)
     rc = lib.ffa_fwd_ex(64, 64, 64, 4, 4, 2, 2, 64, ip(qr), ip(kr), ip(ty), 1, 0.1, 0.0, None, 64, 64, 72,
@@ -158,7 +159,8 @@ def test_saved_record_validation(lib):
                         0.1, 0.0, None, 64, 64, 64, None, 0, None)
     assert rc == -1 and "saved" in ffa.ffa_last_error()
     r256 = lambda x: (x + 255) // 256 * 256
-    assert lib.ffa_saved_size(100, 300, 8, 2, 128) == 256 + r256(100 * 8 * 128 * 2) + r256(300 * 2 * 128 * 2)
+    assert lib.ffa_saved_size(100, 300, 8, 2, 128) == \
+        256 + r256(100 * 8 * 128 * 2) + r256(300 * 2 * 128 * 2) + 2048 * 4
     assert lib.ffa_saved_size(100, 300, 8, 2, 96) == 0
 
 
@@ -175,6 +177,9 @@ def test_noalloc_rejects_sizes_beyond_its_array(lib):
     qr = np.array([[0, T]], np.int32); kr = np.array([[0, T]], np.int32); ty = np.array([0], np.int32)
     rc = lib.ffa_fwd_noalloc(64, 64, 64, T, T, 1, 1, 64, ip(qr), ip(kr), ip(ty), 1, 0.1, 0.0, 64, 64, None)
     assert rc == -1 and "entries" in ffa.ffa_last_error() and "134217728" in ffa.ffa_last_error()
+    # v's fp16 copy alone past the array: 2^20 tokens x 2 kv heads x d 128 x 2 bytes = 512 MiB
+    rc = lib.ffa_fwd_noalloc(64, 64, 64, T, T, 2, 2, 128, ip(qr), ip(kr), ip(ty), 1, 0.1, 0.0, 64, 64, None)
+    assert rc == -1 and "fp16 copy of v" in ffa.ffa_last_error() and "268435456" in ffa.ffa_last_error()
     # bad slices are reported as by ffa_fwd
     qr = np.array([[0, 17]], np.int32); kr = np.array([[0, 16]], np.int32); ty = np.array([0], np.int32)
     rc = lib.ffa_fwd_noalloc(64, 64, 64, 16, 16, 2, 1, 64, ip(qr), ip(kr), ip(ty), 1, 0.1, 0.0, 64, 64, None)

@@ -124,9 +124,11 @@ def test_status_bad_slice_and_capacity():
 
 
 def test_graph_capture_replays_new_slice_lists():
-    """refresh + forward + backward captured once, replayed on three slice
-    lists copied into the same device arrays; every replay equals the eager
-    one-shot calls bitwise, with eager work and synchronisation between."""
+    """refresh + training forward (into a saved record, which holds v's fp16
+    copy, so that nothing is allocated under capture) + backward on that
+    record, captured once and replayed on three slice lists copied into the
+    same device arrays; every replay equals the eager one-shot calls
+    bitwise, with eager work and synchronisation between."""
     w = W.config(2)
     say("HIP graph: refresh + fwd + bwd, replayed on new slice lists")
     d = dev()
@@ -143,12 +145,13 @@ def test_graph_capture_replays_new_slice_lists():
     lse = torch.empty((w.Tq, w.hq), dtype=torch.float32, device=d)
     dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
     bws = torch.empty(max(ffa.ffa_bwd_workspace_size(w.Tq, w.Tk, w.hq, w.hkv, w.d), 16), dtype=torch.uint8, device=d)
+    rec = torch.empty(ffa.ffa_saved_size(w.Tq, w.Tk, w.hq, w.hkv, w.d), dtype=torch.uint8, device=d)
 
     def body():
         ffa.ffa_plan_refresh(plan)
-        ffa.ffa_fwd_planned(plan, qd, kd, vd, w.scale, 0.0, out=out, lse=lse)
+        ffa.ffa_fwd_planned(plan, qd, kd, vd, w.scale, 0.0, out=out, lse=lse, saved=rec)
         ffa.ffa_bwd_planned(plan, qd, kd, vd, out, lse, od, w.scale, 0.0, dq=dq, dk=dk, dv=dv,
-                            workspace=bws)
+                            workspace=bws, saved=rec)
 
     try:
         side = torch.cuda.Stream(device=d)
