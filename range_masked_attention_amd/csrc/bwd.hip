@@ -279,8 +279,12 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a0) {
     const int64_t valid = ((int64_t)a.Tk - r0) * kv_row_bytes - (int64_t)g * D * 2;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc((producer ? a.k : a.v) + off, valid);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      frag[ks] = __builtin_bit_cast(bf16x8, buf_load16(rs, (uint32_t)(n * kv_row_bytes + (16 * ks + 8 * hh) * 2)));
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 f = buf_load16(rs, (uint32_t)(n * kv_row_bytes + (16 * ks + 8 * hh) * 2));
+      // the consumer holds -V (fp16 sign bits): its products give -dP
+      if (!producer) f ^= u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+      frag[ks] = __builtin_bit_cast(bf16x8, f);
+    }
   }
 
   f32x16 acc[DB];  // dV^T (producer) or dK^T (consumer): rows dims, column key
@@ -421,46 +425,58 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a0) {
     dma_barrier();
   };
 
-  // consumer step st: dS, dK of step st - 1, then dP of step st
-  f32x16 dp[2];
+  // consumer step st: D - dP of step st on the matrix cores (accumulators
+  // start from the rows' D, and the consumer's V fragment is held negated),
+  // then -dS = P (D - dP) of step st - 1 from what the previous step left,
+  // whose arithmetic runs in the shadow of those products, and dK of step
+  // st - 1 (accumulating -dK^T; the final scaling flips the sign back).
+  // D - dP alternates between two register sets by step parity.
+  f32x16 dp0[2], dp1[2];
   auto cstep = [&](int st, auto r) {
     constexpr int R = decltype(r)::value;
+    f32x16* dcur = R % 2 == 0 ? dp0 : dp1;   // D - dP of step st
+    f32x16* dprev = R % 2 == 0 ? dp1 : dp0;  // D - dP of step st - 1
+    const char* ot = ob2[R % 2];             // rows of dO, step st
+    const char* qt = qb3[(R + 5) % 3];       // transposed Q of step st - 1
+    const float* xch = xchg[(st - 1) & 1][pair];
     if (st + 1 < n_steps) issue(obuf(IC<R + 1>{}));
-    if (st > 0) {
-      const float* xch = xchg[(st - 1) & 1][pair];
-      const char* qt = qb3[(R + 5) % 3];  // transposed Q of step st - 1
-      u32x4 dw[4];
+    auto dp_products = [&]() {
+      // element (qb, 4 v4 + i) is row 32 qb + 8 v4 + 4 hh + i
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int v4 = 0; v4 < 4; ++v4) {
-          const int rbase = 32 * qb + 8 * v4 + 4 * hh;
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&s_dv[(st - 1) % 3][rbase]);
-          const f32x4 px = *reinterpret_cast<const f32x4*>(xch + ((qb * 4 + v4) * 64 + lane) * 4);
-          float ds[4];
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&s_dv[st % 3][32 * qb + 8 * v4 + 4 * hh]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ds[i] = px[i] * (dp[qb][4 * v4 + i] - d4[i]);
-          dw[2 * qb + (v4 >> 1)][2 * (v4 & 1)] = pack_f16x2(ds[0], ds[1]);
-          dw[2 * qb + (v4 >> 1)][2 * (v4 & 1) + 1] = pack_f16x2(ds[2], ds[3]);
+          for (int i = 0; i < 4; ++i) dcur[qb][4 * v4 + i] = d4[i];
         }
-      // dK^T += Q^T dS
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          dcur[qb] = mfma_32x32x16_f16(T::row8(ot, 0, 32 * qb, 2 * ks), frag[ks], dcur[qb]);
+    };
+    auto ds_dk = [&]() {
+      u32x4 dw[4];
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const int qb = x >> 2, v4 = x & 3;
+        const f32x4 px = *reinterpret_cast<const f32x4*>(xch + (x * 64 + lane) * 4);
+        float ds[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ds[i] = px[i] * dprev[qb][4 * v4 + i];
+        dw[2 * qb + (v4 >> 1)][2 * (v4 & 1)] = pack_f16x2(ds[0], ds[1]);
+        dw[2 * qb + (v4 >> 1)][2 * (v4 & 1) + 1] = pack_f16x2(ds[2], ds[3]);
+      }
+      // -dK^T += Q^T (-dS)
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4)
 #pragma unroll
         for (int db = 0; db < DB; ++db)
           acc[db] = mfma_32x32x16_f16(tr8<D>(qt, 0, db, t4), __builtin_bit_cast(bf16x8, dw[t4]), acc[db]);
-    }
-    if (st < n_steps) {
-      const char* ot = ob2[R % 2];  // rows of dO
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        dp[qb] = f32x16{};
-      }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) dp[qb] = mfma_32x32x16_f16(T::row8(ot, 0, 32 * qb, 2 * ks), frag[ks], dp[qb]);
-    }
+    };
+    if (st < n_steps) dp_products();
+    if (st > 0) ds_dk();
     dma_barrier();
   };
 
@@ -512,7 +528,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a0) {
 
   // accumulator column n is key `key`, rows are head dims
   if (slot >= 0) {
-    // one run of a split key tile: fp32 partial sums, [dK^T | dV^T][key][dim]
+    // one run of a split key tile: fp32 partial sums, [-dK^T | dV^T][key][dim]
     float* dst = a.partial + ((int64_t)slot * a.hkv + g) * (2 * kDkvKeys * D) +
                  (producer ? kDkvKeys * D : 0) + (32 * pair + n) * D;
 #pragma unroll
@@ -529,8 +545,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a0) {
   } else if (key < a.Tk) {
     const int64_t off = ((int64_t)key * a.hkv + g) * D;
     __bf16* dst = producer ? a.dv : a.dk;
-    // dV^T accumulated sdo dV; dK^T accumulated sdo sv sq dK / scale
-    const float mul = producer ? 1.0f / sdo : a.scale / (sdo * sv * sq);
+    // dV^T accumulated sdo dV; the consumer accumulated -sdo sv sq dK^T / scale
+    const float mul = producer ? 1.0f / sdo : -a.scale / (sdo * sv * sq);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -576,7 +592,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_reduce_kernel(BwdArgs a0) {
     const int r = is_v ? i - kDkvKeys * D : i;
     const int key = kt * kDkvKeys + r / D, dim = r % D;
     if (key < a.Tk) {
-      const float mul = is_v ? 1.0f / sdo : a.scale / (sdo * sv * sq);
+      const float mul = is_v ? 1.0f / sdo : -a.scale / (sdo * sv * sq);  // dK^T partials carry -dK
       u32x2 w;
       w[0] = pack_bf16x2(mul * sum[0], mul * sum[1]);
       w[1] = pack_bf16x2(mul * sum[2], mul * sum[3]);
