@@ -295,7 +295,7 @@ int plan_create(int64_t Tq, int64_t Tk, const int32_t* qr, const int32_t* kr, co
   p->bytes = img.size();
   if (want & kWantFwd) {
     p->off_fwd_scratch = align256(img.size());
-    p->bytes = p->off_fwd_scratch + ffa::fwd_scratch_layout(Tq).total;
+    p->bytes = p->off_fwd_scratch + ffa::fwd_scratch_bytes(Tq, p->fwd.max_len);
   }
   hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&p->dev), p->bytes, stream);
   if (e != hipSuccess) {

@@ -813,6 +813,13 @@ FwdScratchLayout fwd_scratch_layout(int64_t Tq) {
   return L;
 }
 
+size_t fwd_scratch_bytes(int64_t Tq, int64_t max_len) {
+  const FwdScratchLayout L = fwd_scratch_layout(Tq);
+  // split_possible() needs a list longer than the minimum run of
+  // kFwdMinSteps entries, whatever the head count
+  return max_len <= kFwdMinSteps ? L.partial_lse : L.total;
+}
+
 size_t fwd_v16_parts(int64_t Tk, int hkv, int d) {
   const size_t nk = (size_t)(Tk > 0 ? Tk : 0) * (size_t)(hkv > 0 ? hkv : 0) * (size_t)(d > 0 ? d : 0);
   return 256 + round256(nk * 2);

@@ -85,6 +85,10 @@ struct FwdScratchLayout {
   int64_t items_cap, splits_cap;
 };
 FwdScratchLayout fwd_scratch_layout(int64_t Tq);
+// Bytes of that scratch a plan whose longest forward list has max_len
+// entries needs: no list that short is ever cut into runs, so such a plan
+// needs none of the partial-output buffers.
+size_t fwd_scratch_bytes(int64_t Tq, int64_t max_len);
 
 struct BwdLaunch {
   const void* q;
