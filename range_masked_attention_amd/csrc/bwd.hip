@@ -572,20 +572,26 @@ constexpr int kDkvMinSteps = 32;   // (entry, q head) steps: never split below t
 constexpr int kDkvMaxSlots = 512;  // partial buffers: runs of split tiles x kv heads
 
 // Sum of the partial dK^T / dV^T of a split tile's runs, in run order, to
-// bf16 dK (times the softmax scale) and dV.
+// bf16 dK (times the softmax scale) and dV: one 16-byte chunk per thread,
+// kDkvReduceParts workgroups per (split tile, kv head).
+template <int D>
+constexpr int kDkvReduceParts = 2 * kDkvKeys * D / 4 / kThreads;
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_dkdv_reduce_kernel(BwdArgs a0) {
   BwdArgs a = a0;
   float sq, sk, sv, sdo;
   fold_scales(&a, &sq, &sk, &sv, &sdo);
-  const int u = blockIdx.x;
+  constexpr int kSlot = 2 * kDkvKeys * D;  // floats per (run, kv head)
+  const int u = blockIdx.x / kDkvReduceParts<D>, part = blockIdx.x % kDkvReduceParts<D>;
   const int s = u / a.hkv, g = u % a.hkv;
   if (s >= plan_i32(a.counts, 1)) return;
   const i32x4 sp = const_load<i32x4>(a.splits, s);
   const int kt = sp[0], slot0 = sp[1], ns = sp[2];
-  constexpr int kSlot = 2 * kDkvKeys * D;  // floats per (run, kv head)
-  for (int i = 4 * threadIdx.x; i < kSlot; i += 4 * kThreads) {
+  {
+    const int i = 4 * (part * kThreads + (int)threadIdx.x);
     f32x4 sum = f32x4{};
+#pragma unroll 4
     for (int c = 0; c < ns; ++c)
       sum += *reinterpret_cast<const f32x4*>(a.partial + ((int64_t)(slot0 + c) * a.hkv + g) * kSlot + i);
     const bool is_v = i >= kDkvKeys * D;
@@ -805,18 +811,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a0) {
   }
 }
 
-// Sum of the fp32 dQ of a split q tile's runs, in run order, to bf16 dQ.
+// Sum of the fp32 dQ of a split q tile's runs, in run order, to bf16 dQ: one
+// 16-byte chunk per thread, kDqReduceParts workgroups per (split tile, head).
+template <int D>
+constexpr int kDqReduceParts = kDqRows * D / 4 / kThreads;
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_dq_reduce_kernel(BwdArgs a) {
-  const int u = blockIdx.x;
+  const int u = blockIdx.x / kDqReduceParts<D>, part = blockIdx.x % kDqReduceParts<D>;
   const int s = u / a.hq, head = u % a.hq;
   if (s >= plan_i32(a.counts, 1)) return;
   const i32x4 sp = const_load<i32x4>(a.splits, s);
   const int qt = sp[0], slot0 = sp[1], ns = sp[2];
-  for (int i = 4 * threadIdx.x; i < kDqRows * D; i += 4 * kThreads) {
+  {
+    const int i = 4 * (part * kThreads + (int)threadIdx.x);
     const int64_t row = (int64_t)qt * kDqRows + i / D;
-    if (row >= a.Tq) continue;
+    if (row >= a.Tq) return;
     f32x4 sum = f32x4{};
+#pragma unroll 4
     for (int c = 0; c < ns; ++c)
       sum += *reinterpret_cast<const f32x4*>(a.partial + ((int64_t)(slot0 + c) * a.hq + head) * kDqRows * D + i);
     u32x2 w;
@@ -934,7 +946,8 @@ hipError_t launch_bwd_t(const BwdLaunch& p, hipStream_t stream) {
     launch_split(sp, stream);
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, SC, BIAS>), dim3((unsigned)(L.items_cap * p.hkv)), dim3(kDkvThreads), 0,
                        stream, a);
-    hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<D>), dim3((unsigned)(L.splits_cap * p.hkv)), dim3(kThreads), 0,
+    hipLaunchKernelGGL((bwd_dkdv_reduce_kernel<D>), dim3((unsigned)(L.splits_cap * p.hkv * kDkvReduceParts<D>)),
+                       dim3(kThreads), 0,
                        stream, a);
   }
   // dQ: one workgroup per (q tile or run of its list, q head), then the
@@ -973,7 +986,8 @@ hipError_t launch_bwd_t(const BwdLaunch& p, hipStream_t stream) {
     const int64_t n_units = caps.items * p.hkv;
     const int64_t n_wg = ((n_units + 7) / 8) * 8 * (int64_t)a.grp;
     hipLaunchKernelGGL((bwd_dq_kernel<D, SC, BIAS>), dim3((unsigned)n_wg), dim3(kThreads), 0, stream, a);
-    hipLaunchKernelGGL((bwd_dq_reduce_kernel<D>), dim3((unsigned)(caps.splits * p.hq)), dim3(kThreads), 0,
+    hipLaunchKernelGGL((bwd_dq_reduce_kernel<D>), dim3((unsigned)(caps.splits * p.hq * kDqReduceParts<D>)),
+                       dim3(kThreads), 0,
                        stream, a);
   }
   return hipGetLastError();

@@ -620,50 +620,57 @@ __global__ __launch_bounds__(kThreads * HPW, 2) void fwd_kernel(FwdArgs a) {
 }
 
 // Merge of the runs of a split q tile, per (row, head): lse = log sum_r
-// exp(lse_r), out = sum_r exp(lse_r - lse) out_r, runs taken in order.
+// exp(lse_r), out = sum_r exp(lse_r - lse) out_r, runs taken in order.  One
+// (row, 4-dim chunk) per thread, kCombineParts workgroups per (split tile,
+// head): each thread's loads are a few dependent rounds, not a loop of them.
+template <int D>
+constexpr int kCombineParts = kBM * (D / 4) / kThreads;
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void fwd_combine_kernel(FwdArgs a) {
-  const int u = blockIdx.x;
+  constexpr int kChunks = D / 4;
+  const int u = blockIdx.x / kCombineParts<D>, part = blockIdx.x % kCombineParts<D>;
   const int s = u / a.hq, head = u % a.hq;
   if (s >= plan_i32(a.counts, 1)) return;
   const i32x4 sp = const_load<i32x4>(a.splits, s);
   const int qt = sp[0], slot0 = sp[1], ns = sp[2];
-  constexpr int kChunks = D / 4;
   const float log2e = 1.4426950408889634f;
-  for (int i = threadIdx.x; i < kBM * kChunks; i += kThreads) {
-    const int rl = i / kChunks, c = i % kChunks;
-    const int64_t row = (int64_t)qt * kBM + rl;
-    if (row >= a.Tq) continue;
-    auto at = [&](int r) { return ((int64_t)(slot0 + r) * a.hq + head) * kBM + rl; };
-    float m = -INFINITY;
-    for (int r = 0; r < ns; ++r) m = fmaxf(m, a.partial_lse[at(r)]);
-    f32x4 acc = f32x4{};
-    float sum = 0.f;
-    if (m != -INFINITY) {
-      for (int r = 0; r < ns; ++r) {
-        const float lr = a.partial_lse[at(r)];
-        if (lr == -INFINITY) continue;
-        const float wr = fast_exp2((lr - m) * log2e);
-        sum += wr;
-        acc += wr * *reinterpret_cast<const f32x4*>(a.partial_o + at(r) * D + 4 * c);
-      }
+  const int i = part * kThreads + threadIdx.x;
+  const int rl = i / kChunks, c = i % kChunks;
+  const int64_t row = (int64_t)qt * kBM + rl;
+  if (row >= a.Tq) return;
+  auto at = [&](int r) { return ((int64_t)(slot0 + r) * a.hq + head) * kBM + rl; };
+  float m = -INFINITY;
+#pragma unroll 4
+  for (int r = 0; r < ns; ++r) m = fmaxf(m, a.partial_lse[at(r)]);
+  f32x4 acc = f32x4{};
+  float sum = 0.f;
+  if (m != -INFINITY) {
+#pragma unroll 4
+    for (int r = 0; r < ns; ++r) {
+      const float lr = a.partial_lse[at(r)];
+      const f32x4 o = *reinterpret_cast<const f32x4*>(a.partial_o + at(r) * D + 4 * c);
+      if (lr == -INFINITY) continue;
+      const float wr = fast_exp2((lr - m) * log2e);
+      sum += wr;
+      acc += wr * o;
     }
-    const float inv = sum > 0.f ? 1.0f / sum : 0.f;
-    uint16_t h[4], l[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) split_bf16(acc[i] * inv, &h[i], &l[i]);
-    u32x2 w2;
-    w2[0] = h[0] | (uint32_t)h[1] << 16;
-    w2[1] = h[2] | (uint32_t)h[3] << 16;
-    *reinterpret_cast<u32x2*>(a.out + (row * a.hq + head) * D + 4 * c) = w2;
-    if (a.out_lo) {
-      u32x2 r2;
-      r2[0] = l[0] | (uint32_t)l[1] << 16;
-      r2[1] = l[2] | (uint32_t)l[3] << 16;
-      *reinterpret_cast<u32x2*>(a.out_lo + (row * a.hq + head) * D + 4 * c) = r2;
-    }
-    if (c == 0) a.lse[row * a.hq + head] = sum > 0.f ? m + fast_log2(sum) * 0.69314718055994531f : -INFINITY;
   }
+  const float inv = sum > 0.f ? 1.0f / sum : 0.f;
+  uint16_t h[4], l[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) split_bf16(acc[j] * inv, &h[j], &l[j]);
+  u32x2 w2;
+  w2[0] = h[0] | (uint32_t)h[1] << 16;
+  w2[1] = h[2] | (uint32_t)h[3] << 16;
+  *reinterpret_cast<u32x2*>(a.out + (row * a.hq + head) * D + 4 * c) = w2;
+  if (a.out_lo) {
+    u32x2 r2;
+    r2[0] = l[0] | (uint32_t)l[1] << 16;
+    r2[1] = l[2] | (uint32_t)l[3] << 16;
+    *reinterpret_cast<u32x2*>(a.out_lo + (row * a.hq + head) * D + 4 * c) = r2;
+  }
+  if (c == 0) a.lse[row * a.hq + head] = sum > 0.f ? m + fast_log2(sum) * 0.69314718055994531f : -INFINITY;
 }
 
 // FFA_FWD_PAIRED=1 makes the forward take two q heads per workgroup
@@ -784,7 +791,8 @@ hipError_t launch_fwd_t(const FwdLaunch& p, hipStream_t stream) {
   sp.counts = reinterpret_cast<int32_t*>(ws + S.counts);
   launch_split(sp, stream);
   launch_fwd_kernel<D, SC, BIAS, F16>(a, caps.items * p.hkv, stream);
-  hipLaunchKernelGGL((fwd_combine_kernel<D>), dim3((unsigned)(caps.splits * p.hq)), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((fwd_combine_kernel<D>), dim3((unsigned)(caps.splits * p.hq * kCombineParts<D>)), dim3(kThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
