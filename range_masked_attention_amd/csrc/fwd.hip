@@ -247,14 +247,16 @@ __device__ __forceinline__ void qk_tile(const __bf16* kl, const bf16x8* qf, int 
 // sigma * (j - i) (sigma in exp2 units; see bias_tile).
 template <bool BIAS>
 __device__ __forceinline__ void softcap_tile(const FwdArgs& a, f32x16* s, float sigma, int ktile, int d0) {
-  const float base = BIAS ? sigma * (float)(ktile * kBN + d0) : 0.f;
+  // cap_out tanh(x) = cap_out - 2 cap_out / (2^y + 1): one multiply-add
+  // after the reciprocal (the bias joins the constant term)
+  const float base = (BIAS ? sigma * (float)(ktile * kBN + d0) : 0.f) + a.cap_out;
+  const float m2 = -2.0f * a.cap_out;
 #pragma unroll
   for (int b = 0; b < 2; ++b)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const float th = tanh_from_2xlog2e(s[b][v] * a.cap_in);
-      s[b][v] = BIAS ? __builtin_fmaf(a.cap_out, th, __builtin_fmaf(sigma, (float)key_off(b, v), base))
-                     : a.cap_out * th;
+      const float r = fast_rcp(fast_exp2(s[b][v] * a.cap_in) + 1.0f);
+      s[b][v] = __builtin_fmaf(m2, r, BIAS ? __builtin_fmaf(sigma, (float)key_off(b, v), base) : base);
     }
 }
 
