@@ -95,7 +95,7 @@ def fwd_kernel_name(w: W.Workload, alibi: bool) -> str:
     grp = w.hq // w.hkv
     units = ((w.Tq + 127) // 128) * w.hkv
     hpw = 2 if grp % 2 == 0 and units * (grp // 2) >= 512 else 1
-    return f"fwd_kernel<{w.d}, {str(w.softcap > 0).lower()}, {str(alibi).lower()}, true, {hpw}>"
+    return f"fwd_kernel<{w.d}, {str(w.softcap > 0).lower()}, {str(alibi).lower()}, {hpw}>"
 
 
 def cpu_baseline(w: W.Workload, q, k, v, budget_s: float):

@@ -75,7 +75,7 @@ struct FwdArgs {
   __bf16* out;
   float* lse;
   __bf16* out_lo;           // rounding residual of out (training forward), or null
-  const uint32_t* v_words;  // training forward: range words of v (v is then its fp16 copy)
+  const uint32_t* v_words;  // range words of v (v is its fp16 copy times the scale they give)
   const DevEntry* entries;  // grouped by q tile
   const DevSlice* slices;
   const int32_t* row_ptr;   // [n_qtiles + 1]
@@ -289,16 +289,18 @@ __device__ __forceinline__ void mask_tile(const DevSlice& sl, int ktile, int row
     }
 }
 
-// F16 (every forward the library launches): v is the fp16 copy of v times
-// its range scale s_v, P enters the P V product in fp16 (11 significant bits
-// instead of 8), and the epilogue divides by s_v as well; the output then
-// carries P's rounding at 2^-12 instead of 2^-9, which both out's accuracy
-// and the backward's row term D need.
+// P V on fp16 operands: v is the fp16 copy of v times its scale s_v (made
+// before the kernel, see launch_fwd_t), P enters the product in fp16 (11
+// significant bits instead of bf16's 8), and the epilogue divides by s_v as
+// well.  Each weight enters P V rounded (relative error up to half an ulp)
+// while the row sum that divides out is of the unrounded weights, so out can
+// be off by up to that half ulp times max |v|: 2^-12 with fp16 P, where
+// bf16's 2^-9 would, with out's own rounding, come near 2e-2 for |v| around 6.
 //
 // HPW q heads of one kv head per workgroup (four waves each, on the same q
 // tile): the heads share every K and V tile fetched into LDS, which halves
 // the fetches per product when two heads share a kv head.
-template <int D, bool SOFTCAP, bool BIAS, bool F16, int HPW>
+template <int D, bool SOFTCAP, bool BIAS, int HPW>
 __global__ __launch_bounds__(kThreads * HPW, 2) void fwd_kernel(FwdArgs a) {
   using Smem = FwdSmem<D>;
   constexpr int KS = D / 16;  // k steps of the QK^T contraction
@@ -466,7 +468,7 @@ __global__ __launch_bounds__(kThreads * HPW, 2) void fwd_kernel(FwdArgs a) {
           l4[e8 & 3] += p[e8];
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pw[t][i] = F16 ? pack_f16x2(p[2 * i], p[2 * i + 1]) : pack_bf16x2(p[2 * i], p[2 * i + 1]);
+        for (int i = 0; i < 4; ++i) pw[t][i] = pack_f16x2(p[2 * i], p[2 * i + 1]);
       }
 
       if constexpr (MORE) {
@@ -497,10 +499,7 @@ __global__ __launch_bounds__(kThreads * HPW, 2) void fwd_kernel(FwdArgs a) {
           const u32x2 hi4 = lds_read_tr16(vp + 8 * D);
           u32x4 av;
           av[0] = lo4[0]; av[1] = lo4[1]; av[2] = hi4[0]; av[3] = hi4[1];
-          if constexpr (F16)
-            o[db] = mfma_32x32x16_f16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, pw[t]), o[db]);
-          else
-            o[db] = mfma_32x32x16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, pw[t]), o[db]);
+          o[db] = mfma_32x32x16_f16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, pw[t]), o[db]);
         }
       if constexpr (MORE) {
         if constexpr (SOFTCAP) softcap_tile<BIAS>(a, s_next, sigma, e1.tile, d0);
@@ -546,7 +545,7 @@ __global__ __launch_bounds__(kThreads * HPW, 2) void fwd_kernel(FwdArgs a) {
   const float l_part = (l4[0] + l4[1]) + (l4[2] + l4[3]);
   const float l = l_part + __shfl_xor(l_part, 32);
   float inv = l > 0.f ? 1.0f / l : 0.f;
-  if constexpr (F16) inv *= 1.0f / copy_scale(const_load<uint32_t>(a.v_words, kRgV), kRangeV);
+  inv *= 1.0f / copy_scale(const_load<uint32_t>(a.v_words, kRgV), kRangeV);
   if (item.slot >= 0) {
     // one run of a split q tile: fp32 output and lse for fwd_combine
     const int64_t pr = ((int64_t)item.slot * a.hq + head) * kBM + (row - q0);
@@ -687,19 +686,19 @@ int paired_mode() {
 // Launch of fwd_kernel over n_units (work item, kv head) units: two q heads
 // per workgroup (eight waves, one workgroup per CU) when heads pair up and
 // the pairs still fill the chip twice over, else one.
-template <int D, bool SC, bool BIAS, bool F16>
+template <int D, bool SC, bool BIAS>
 void launch_fwd_kernel(const FwdArgs& a, int64_t n_units, hipStream_t stream) {
   const int64_t n8 = ((n_units + 7) / 8) * 8;
   const int mode = paired_mode();
   const bool pairs = a.grp % 2 == 0;
   if (pairs && (mode == 1 || (mode < 0 && n_units * (a.grp / 2) >= kFwdPairMinWorkgroups)))
-    hipLaunchKernelGGL((fwd_kernel<D, SC, BIAS, F16, 2>), dim3((unsigned)(n8 * (a.grp / 2))), dim3(2 * kThreads), 0,
+    hipLaunchKernelGGL((fwd_kernel<D, SC, BIAS, 2>), dim3((unsigned)(n8 * (a.grp / 2))), dim3(2 * kThreads), 0,
                        stream, a);
   else
-    hipLaunchKernelGGL((fwd_kernel<D, SC, BIAS, F16, 1>), dim3((unsigned)(n8 * a.grp)), dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL((fwd_kernel<D, SC, BIAS, 1>), dim3((unsigned)(n8 * a.grp)), dim3(kThreads), 0, stream, a);
 }
 
-template <int D, bool SC, bool BIAS, bool F16>
+template <int D, bool SC, bool BIAS>
 hipError_t launch_fwd_t(const FwdLaunch& p, hipStream_t stream) {
   FwdArgs a;
   a.q = static_cast<const __bf16*>(p.q);
@@ -708,8 +707,7 @@ hipError_t launch_fwd_t(const FwdLaunch& p, hipStream_t stream) {
   a.out = static_cast<__bf16*>(p.out);
   a.lse = p.lse;
   a.out_lo = nullptr;
-  a.v_words = nullptr;
-  if constexpr (F16) {
+  {
     // v's range and fp16 copy (read below as v): in the record for the
     // backward, with out's rounding residual, or in the caller's room for
     // them (fwd_v16_bytes), without a residual
@@ -772,7 +770,7 @@ hipError_t launch_fwd_t(const FwdLaunch& p, hipStream_t stream) {
     // no list can be cut: one work item per q tile, straight from the plan
     a.direct = 1;
     a.n_units = (int32_t)(n_qt * p.hkv);
-    launch_fwd_kernel<D, SC, BIAS, F16>(a, a.n_units, stream);
+    launch_fwd_kernel<D, SC, BIAS>(a, a.n_units, stream);
     return hipGetLastError();
   }
   a.direct = 0;
@@ -792,7 +790,7 @@ hipError_t launch_fwd_t(const FwdLaunch& p, hipStream_t stream) {
   sp.splits_cap = caps.splits;
   sp.counts = reinterpret_cast<int32_t*>(ws + S.counts);
   launch_split(sp, stream);
-  launch_fwd_kernel<D, SC, BIAS, F16>(a, caps.items * p.hkv, stream);
+  launch_fwd_kernel<D, SC, BIAS>(a, caps.items * p.hkv, stream);
   hipLaunchKernelGGL((fwd_combine_kernel<D>), dim3((unsigned)(caps.splits * p.hq * kCombineParts<D>)), dim3(kThreads), 0,
                      stream, a);
   return hipGetLastError();
@@ -842,22 +840,11 @@ size_t fwd_v16_bytes(int64_t Tk, int hkv, int d) {
 int fwd_tile_rows() { return kBM; }
 int fwd_tile_cols() { return kBN; }
 
-template <int D, bool F16>
-hipError_t launch_fwd_df(const FwdLaunch& p, hipStream_t stream) {
-  const bool sc = p.softcap > 0.f, bias = p.alibi_slopes != nullptr;
-  if (bias) return sc ? launch_fwd_t<D, true, true, F16>(p, stream) : launch_fwd_t<D, false, true, F16>(p, stream);
-  return sc ? launch_fwd_t<D, true, false, F16>(p, stream) : launch_fwd_t<D, false, false, F16>(p, stream);
-}
-
-// Every forward runs P V on fp16 operands (the bf16 path stays in the
-// kernel template, unused).  Each weight enters P V rounded (relative error
-// up to half an ulp) while the row sum that divides out is of the unrounded
-// weights, so out can be off by up to that half ulp times max |v|: 2^-9 for
-// bf16, which with out's own rounding comes near 2e-2 for |v| around 6,
-// against 2^-12 for fp16.
 template <int D>
 hipError_t launch_fwd_d(const FwdLaunch& p, hipStream_t stream) {
-  return launch_fwd_df<D, true>(p, stream);
+  const bool sc = p.softcap > 0.f, bias = p.alibi_slopes != nullptr;
+  if (bias) return sc ? launch_fwd_t<D, true, true>(p, stream) : launch_fwd_t<D, false, true>(p, stream);
+  return sc ? launch_fwd_t<D, true, false>(p, stream) : launch_fwd_t<D, false, false>(p, stream);
 }
 
 hipError_t launch_fwd(const FwdLaunch& p, hipStream_t stream) {
