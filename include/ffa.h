@@ -298,8 +298,9 @@ typedef struct ffa_plan_s* ffa_plan_t;
  * memory on `stream`.  *plan receives the handle.  Use the plan on `stream`
  * (or after synchronising with it).  Errors as for ffa_fwd.
  *
- * The plan also holds the forward's scratch (about 32 MiB): a q tile whose
- * list is longer than one workgroup slot's share of the work (a short query
+ * The plan also holds the forward's scratch (about 32 MiB, reserved only
+ * when some q tile's list is longer than 64 key tiles): a q tile whose list
+ * is longer than one workgroup slot's share of the work (a short query
  * block against a long context) is walked by several workgroups whose
  * partial outputs are merged by their lse, in a fixed order.  Forward calls
  * on one plan therefore must not run concurrently on different streams;
