@@ -129,9 +129,9 @@ size_t ffa_bwd_workspace_size(int64_t Tq, int64_t Tk, int hq, int hkv, int d);
  *
  * Precision.  The products run on the matrix cores with fp16 operands
  * (11 significant bits) and fp32 accumulation: q, k, v and dout are copied
- * to fp16, each times the power of two that maps its largest |x| onto
- * fp16's range (exact), and P and dS are rounded to fp16 for the second
- * products.  The row term D = rowsum(dout * out) needs out more precisely
+ * to fp16, each times a power of two that fits its largest |x| into fp16's
+ * range (exact; v's copy is the forward's), and P and dS are rounded to
+ * fp16 for the second products.  The row term D = rowsum(dout * out) needs out more precisely
  * than bf16 holds it: ffa_bwd (no saved record) re-runs the forward into the
  * workspace in its training form (see ffa_fwd_ex, `saved`), which costs one
  * forward pass; ffa_bwd_ex takes the record a training forward saved and

@@ -36,9 +36,10 @@
 // has 8) at the same matrix-core rate, so P and dS enter them with 2^-11
 // relative rounding instead of 2^-8.  The fp16 copies of q, k, v and dO are
 // exact (bf16 values times a power of two, inside fp16's normal range up to
-// values below 2^-14 of the largest, which round at 2^-25 of it), and the
-// powers of two come back out exactly in the score multiplier and the final
-// scaling of dq, dk and dv.  D is formed from out plus its rounding
+// values far below the largest, which round at 2^-25 after scaling; v's copy
+// comes from the forward, at scale 1 when its range allows), and the powers
+// of two come back out exactly in the score multiplier and the final scaling
+// of dq, dk and dv.  D is formed from out plus its rounding
 // residual, from a forward whose P V product also ran in fp16, so it carries
 // neither out's bf16 rounding nor a bf16 rounding of P.
 //

@@ -454,9 +454,8 @@ __global__ __launch_bounds__(kThreads * HPW, 2) void fwd_kernel(FwdArgs a) {
       }
       // fp32 sum of the unrounded weights (the lse must hold to 1e-3 even
       // for rows with a handful of keys), four independent chains.  (Summing
-      // the fp16-rounded weights of the training forward two at a time with
-      // v_dot2_f32_f16 would do for the lse, but measured slower than these
-      // adds.)
+      // the fp16-rounded weights two at a time with v_dot2_f32_f16 would do
+      // for the lse, but measured slower than these adds.)
       u32x4 pw[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
