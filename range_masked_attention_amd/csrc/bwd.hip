@@ -13,7 +13,8 @@
 // varlen backward design open (CUTLASS issue #2192); this one is built for
 // the slice plan:
 //
-//  bwd_prep  (after the range pass of convert.hip over q, k and dO)
+//  bwd_prep  (after the range pass of convert.hip over dO and k's tracked
+//            fp16 copy; q's range comes with the forward's record)
 //            fp16 copies of q and dO, each times the power of two that maps
 //            its range onto fp16's (k's comes from convert.hip, v's with the
 //            record the training forward saved); D for every (row, q head)
@@ -80,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(const u32x4* __restr
                                                           float* __restrict__ lse2, float* __restrict__ scales,
                                                           int64_t Tq, int hq) {
   constexpr int kL = D / 8;  // lanes per (row, head)
-  const float sq = range_scale(range[kRgQ], kRangeQ), sk = range_scale(range[kRgK], kRangeK);
+  const float sq = range_scale(vwords[kRgQ], kRangeQ), sk = copy_scale(range[kRgK], kRangeK);
   const float sv = copy_scale(vwords[kRgV], kRangeV);
   const float sdo = range_scale(range[kRgDO], kRangeDOV - range_top(vwords[kRgV], sv));
   const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -884,26 +885,23 @@ hipError_t launch_bwd_t(const BwdLaunch& p, hipStream_t stream) {
   a.splits = reinterpret_cast<const i32x4*>(ws + L.splits);
   a.partial = reinterpret_cast<float*>(ws + L.partial);
   a.slopes = p.alibi_slopes;
-  // ranges of q, k, dO (v's and its fp16 copy come with the saved record);
-  // the fp16 copies; D and lse in exp2 units
+  // ranges: dO's from a pass over it; q's and v's (with v's fp16 copy) come
+  // with the saved record; k's from its tracked copy.  Then the fp16 copies
+  // of q and dO, D and lse in exp2 units
   const SavedLayout S = saved_layout(p.Tq, p.Tk, p.hq, p.hkv, D);
   const unsigned char* saved = static_cast<const unsigned char*>(p.saved);
   uint32_t* range = reinterpret_cast<uint32_t*>(ws + L.range);
   const int64_t nq = rows * D / 8, nk = p.Tk * p.hkv * D / 8;  // 16-byte chunks
   launch_range_clear(range, 8, stream);
   RangeJob job{};
-  job.n = 3;
-  job.src[0] = p.q;
+  job.n = 1;
+  job.src[0] = p.dout;
   job.chunks[0] = nq;
-  job.word[0] = kRgQ;
-  job.src[1] = p.dout;
-  job.chunks[1] = nq;
-  job.word[1] = kRgDO;
-  job.src[2] = p.k;
-  job.chunks[2] = nk;
-  job.word[2] = kRgK;
+  job.word[0] = kRgDO;
   job.words = range;
   launch_range_max(job, stream);
+  launch_convert_tracked(p.k, ws + L.k16, nk, reinterpret_cast<uint32_t*>(ws + L.parts), range, kRgK, kRangeK, false,
+                         stream);
   {
     // also writes the scales (thread 0), so it runs even without rows
     const int64_t blocks = std::max<int64_t>((nq + kThreads - 1) / kThreads, 1);
@@ -914,7 +912,6 @@ hipError_t launch_bwd_t(const BwdLaunch& p, hipStream_t stream) {
                        reinterpret_cast<u32x4*>(ws + L.q16), reinterpret_cast<u32x4*>(ws + L.do16), dvec, lse2,
                        reinterpret_cast<float*>(ws + L.range + 16), p.Tq, p.hq);
   }
-  launch_convert(p.k, ws + L.k16, nk, range, kRgK, kRangeK, stream);
   a.v = reinterpret_cast<const __bf16*>(saved + S.v16);
   // dK, dV: key tiles cut into runs, one workgroup per (run, kv head), then
   // the sums over the runs of split tiles
@@ -1043,6 +1040,8 @@ BwdWorkspaceLayout bwd_workspace_layout(int64_t Tq, int64_t Tk, int hq, int hkv,
   off = round256(off);
   L.range = off;
   off += 256;
+  L.parts = off;
+  off += round256((size_t)kVRangeParts * 4);
   L.q16 = off;
   off += round256(nq * 2);
   L.do16 = off;

@@ -6,9 +6,10 @@
 // has 8 significant bits and fp16 keeps 11, for every value down to 2^-14 of
 // 2^L; below that fp16 rounds at 2^-25 of 2^L.  The largest |x| comes from a
 // grid-stride pass (one atomic per workgroup and tensor) before the copy.
-// v's copy instead takes scale 1 whenever its range allows (copy_scale), is
-// made in the pass that finds its range (partial maxima per workgroup, no
-// atomics), and is redone only when it does not.
+// The copies of v (forward) and k (backward) instead take scale 1 whenever
+// their range allows (copy_scale), are made in the pass that finds the range
+// (partial maxima per workgroup, no atomics), and are redone only when it
+// does not.
 #include <algorithm>
 
 #include "device_common.hpp"
@@ -81,8 +82,9 @@ __device__ __forceinline__ uint32_t block_max(uint32_t m) {
   return b;
 }
 
-// v's copy, first pass: dst = fp16(src) at scale 1, two chunks in flight per
-// thread, and parts[workgroup] = fp32 bits of the largest |src| it saw.
+// Tracked copy (v's in the forward, k's in the backward), first pass: dst =
+// fp16(src) at scale 1, two chunks in flight per thread, and
+// parts[workgroup] = fp32 bits of the largest |src| it saw.
 __global__ __launch_bounds__(kThreads) void convert_track_kernel(const u32x4* __restrict__ src,
                                                                 u32x4* __restrict__ dst, int64_t n,
                                                                 uint32_t* __restrict__ parts) {
@@ -104,32 +106,24 @@ __global__ __launch_bounds__(kThreads) void convert_track_kernel(const u32x4* __
   if (threadIdx.x == 0) parts[blockIdx.x] = m << 16;
 }
 
-// v's copy, second pass: max |src| from the first pass's n_parts partial
-// maxima (every workgroup reduces them; workgroup 0 also writes the range
-// words), then the copy redone at copy_scale where that is not 1 (a range
-// outside [2^-3, 2^L)); otherwise every workgroup returns there.
+// Second pass: max |src| from the first pass's n_parts partial maxima
+// (every workgroup reduces them; workgroup 0 writes words[word], and with
+// clear_others sets words[0..3] but that one to 0), then the copy redone at
+// copy_scale where that is not 1 (a range outside [2^-3, 2^L)); otherwise
+// every workgroup returns there.
 __global__ __launch_bounds__(kThreads) void convert_fix_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                               int64_t n, const uint32_t* __restrict__ parts,
                                                               int n_parts, uint32_t* __restrict__ words, int word,
-                                                              int L) {
+                                                              int L, int clear_others) {
   uint32_t m = 0;
   for (int i = threadIdx.x; i < n_parts; i += kThreads) m = max(m, parts[i]);
   m = block_max(m);
-  if (blockIdx.x == 0 && threadIdx.x < 4) words[threadIdx.x] = (int)threadIdx.x == word ? m : 0u;
+  if (blockIdx.x == 0 && threadIdx.x < 4 && (clear_others || (int)threadIdx.x == word))
+    words[threadIdx.x] = (int)threadIdx.x == word ? m : 0u;
   const float s = copy_scale(m, L);
   if (s == 1.0f) return;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) dst[i] = to_f16x8(src[i], s);
-}
-
-// dst = fp16(src * s), s from words[word] and range bound L.
-__global__ __launch_bounds__(kThreads) void convert_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
-                                                          int64_t n, const uint32_t* __restrict__ words, int word,
-                                                          int L) {
-  const float s = range_scale(words[word], L);
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride)
-    dst[i] = to_f16x8(src[i], s);
 }
 
 int64_t grid_for(int64_t n, int64_t cap) {
@@ -152,15 +146,8 @@ void launch_range_max(const RangeJob& job, hipStream_t stream) {
                      job);
 }
 
-void launch_convert(const void* src, void* dst, int64_t chunks, const uint32_t* words, int word, int L,
-                    hipStream_t stream) {
-  if (chunks <= 0) return;
-  hipLaunchKernelGGL(convert_kernel, dim3((unsigned)grid_for(chunks, 4096)), dim3(kThreads), 0, stream,
-                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), chunks, words, word, L);
-}
-
 void launch_convert_tracked(const void* src, void* dst, int64_t chunks, uint32_t* parts, uint32_t* words, int word,
-                            int L, hipStream_t stream) {
+                            int L, bool clear_others, hipStream_t stream) {
   // two chunks per thread and step: about 4 steps per thread at the largest
   // sizes, and at least a few workgroups per CU on small tensors; the
   // second pass, which copies again only for a range outside its window,
@@ -171,7 +158,8 @@ void launch_convert_tracked(const void* src, void* dst, int64_t chunks, uint32_t
                        static_cast<u32x4*>(dst), chunks, parts);
   hipLaunchKernelGGL(convert_fix_kernel, dim3(chunks > 0 ? std::min(g, 256u) : 1u), dim3(kThreads), 0, stream,
                      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), chunks,
-                     static_cast<const uint32_t*>(parts), chunks > 0 ? (int)g : 0, words, word, L);
+                     static_cast<const uint32_t*>(parts), chunks > 0 ? (int)g : 0, words, word, L,
+                     clear_others ? 1 : 0);
 }
 
 SavedLayout saved_layout(int64_t Tq, int64_t Tk, int hq, int hkv, int d) {

@@ -127,11 +127,11 @@ __device__ __forceinline__ float range_scale(uint32_t max_bits, int L) {
   return __uint_as_float((uint32_t)(se + 127) << 23);
 }
 
-// Scale of v's fp16 copy: 1 when max |v| already lies in [2^-3, 2^L) (the
-// copy at scale 1 is then exact for every value from 2^-17 up, and what lies
-// below rounds at 2^-25, under 2^-22 of max |v|), else range_scale.  The
-// copy is made at scale 1 in the same pass that finds max |v| and redone only
-// outside that window.
+// Scale of the fp16 copies of v and k: 1 when max |x| already lies in
+// [2^-3, 2^L) (the copy at scale 1 is then exact for every value from 2^-17
+// up, and what lies below rounds at 2^-25, under 2^-22 of max |x|), else
+// range_scale.  The copy is made at scale 1 in the same pass that finds
+// max |x| and redone only outside that window.
 __device__ __forceinline__ float copy_scale(uint32_t max_bits, int L) {
   const uint32_t lo = (uint32_t)(127 - 3) << 23, hi = (uint32_t)(127 + L) << 23;
   return (max_bits >= lo && max_bits < hi) ? 1.0f : range_scale(max_bits, L);

@@ -76,6 +76,7 @@ struct FwdArgs {
   float* lse;
   __bf16* out_lo;           // rounding residual of out (training forward), or null
   const uint32_t* v_words;  // range words of v (v is its fp16 copy times the scale they give)
+  uint32_t* q_range;        // training forward: the record's word for max |q| (kRgQ), or null
   const DevEntry* entries;  // grouped by q tile
   const DevSlice* slices;
   const int32_t* row_ptr;   // [n_qtiles + 1]
@@ -336,6 +337,21 @@ __global__ __launch_bounds__(kThreads * HPW, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qf[ks] = __builtin_bit_cast(bf16x8, buf_load16(rq, (uint32_t)(n * q_row_bytes + (16 * ks + 8 * hh) * 2)));
+  }
+  // the training forward also leaves max |q| in its record for the
+  // backward's fp16 copy of q (every q row is loaded by some wave; rows past
+  // the end load as 0): the largest bf16 magnitude bits, one atomic per wave
+  if (a.q_range) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 w4 = __builtin_bit_cast(u32x4, qf[ks]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) m = max(m, max(w4[j] & 0x7FFFu, (w4[j] >> 16) & 0x7FFFu));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+    if (lane == 0 && m) atomicMax(&a.q_range[kRgQ], m << 16);
   }
 
   const int e_begin = item.e_begin, e_end = item.e_end;
@@ -706,6 +722,7 @@ hipError_t launch_fwd_t(const FwdLaunch& p, hipStream_t stream) {
   a.out = static_cast<__bf16*>(p.out);
   a.lse = p.lse;
   a.out_lo = nullptr;
+  a.q_range = nullptr;
   {
     // v's range and fp16 copy (read below as v): in the record for the
     // backward, with out's rounding residual, or in the caller's room for
@@ -720,6 +737,7 @@ hipError_t launch_fwd_t(const FwdLaunch& p, hipStream_t stream) {
       v16 = sv + S.v16;
       parts = reinterpret_cast<uint32_t*>(sv + S.parts);
       a.out_lo = reinterpret_cast<__bf16*>(sv + S.out_lo);
+      a.q_range = words;  // cleared by the copy's second pass below, before the kernel
     } else {
       if (!p.v16) return hipErrorInvalidValue;
       unsigned char* room = static_cast<unsigned char*>(p.v16);
@@ -728,7 +746,7 @@ hipError_t launch_fwd_t(const FwdLaunch& p, hipStream_t stream) {
       parts = reinterpret_cast<uint32_t*>(room + fwd_v16_parts(p.Tk, p.hkv, D));
     }
     const int64_t nk = p.Tk * p.hkv * D / 8;
-    launch_convert_tracked(p.v, v16, nk, parts, words, kRgV, kRangeV, stream);
+    launch_convert_tracked(p.v, v16, nk, parts, words, kRgV, kRangeV, true, stream);
     a.v = reinterpret_cast<const __bf16*>(v16);
     a.v_words = words;
   }

@@ -20,8 +20,8 @@ struct HostDevEntry {
 constexpr int kVRangeParts = 2048;
 
 // What the training forward saves for the backward (device memory of
-// saved_layout(...).total bytes): range words (word kRgV: fp32 bits of
-// max |v|), out's bf16 rounding residual [Tq][hq][d], the fp16 copy of v
+// saved_layout(...).total bytes): range words (fp32 bits of max |v| in word
+// kRgV, of max |q| in word kRgQ), out's bf16 rounding residual [Tq][hq][d], the fp16 copy of v
 // [Tk][hkv][d] that the forward's P V product read (times its scale), and
 // the copy pass's partial maxima.
 struct SavedLayout {
@@ -36,7 +36,7 @@ size_t fwd_v16_bytes(int64_t Tk, int hkv, int d);
 size_t fwd_v16_parts(int64_t Tk, int hkv, int d);
 
 // fp16 operand copies (convert.hip): largest |x| of up to four bf16 tensors
-// into range words, then copies scaled by their range scale.
+// into range words (range_max), and the tracked copies below.
 struct RangeJob {
   int n;
   const void* src[4];
@@ -46,13 +46,12 @@ struct RangeJob {
 };
 void launch_range_clear(uint32_t* words, int n, hipStream_t stream);
 void launch_range_max(const RangeJob& job, hipStream_t stream);
-void launch_convert(const void* src, void* dst, int64_t chunks, const uint32_t* words, int word, int L,
-                    hipStream_t stream);
-// v's copy: dst = fp16(src * copy_scale) in one pass where that scale is
-// 1, two otherwise; words[0..3] = 0 but words[word] = fp32 bits of max |src|.
+// v's copy (and k's in the backward): dst = fp16(src * copy_scale) in one
+// pass where that scale is 1, two otherwise; words[word] = fp32 bits of
+// max |src|, and with clear_others the other three of words[0..3] = 0.
 // parts: kVRangeParts words of scratch.
 void launch_convert_tracked(const void* src, void* dst, int64_t chunks, uint32_t* parts, uint32_t* words, int word,
-                            int L, hipStream_t stream);
+                            int L, bool clear_others, hipStream_t stream);
 
 struct FwdLaunch {
   const void* q;
@@ -194,7 +193,7 @@ void launch_split(const SplitLaunch& s, hipStream_t stream);
 struct BwdWorkspaceLayout {
   size_t dvec, lse2, counts, items, splits, partial;
   size_t dq_counts, dq_items, dq_splits, dq_partial;
-  size_t range, q16, k16, do16, re_saved, re_out, re_lse, total;
+  size_t range, parts, q16, k16, do16, re_saved, re_out, re_lse, total;
   int64_t items_cap, splits_cap;
 };
 BwdWorkspaceLayout bwd_workspace_layout(int64_t Tq, int64_t Tk, int hq, int hkv, int d);
