@@ -123,9 +123,9 @@ def test_dummy_padding_bitwise():
 
 def test_training_forward_record():
     """The training forward (saved record) runs the plain forward's kernel:
-    out and lse keep their bits, and the record holds out's rounding residual
-    (at most half an ulp of out, with out + residual closer to the oracle)
-    and v's fp16 copy."""
+    out and lse keep their bits, and the record holds the ranges of q and v,
+    out's rounding residual (at most half an ulp of out, with out + residual
+    closer to the oracle) and v's fp16 copy."""
     w = W.config(2)
     say("fwd training record (config 2)")
     q, k, v, _ = W.workload_tensors(w, with_dout=False)
@@ -148,6 +148,12 @@ def test_training_forward_record():
     e_full = np.abs(o + r - ref).max()
     say(f"  out max-abs {e_train:.3e}, with the residual {e_full:.3e}")
     assert e_full < e_train
+    # the record's range words: max |q| (word 0, left by the forward's waves
+    # for the backward's copy of q) and max |v| (word 2), as fp32 bits; the
+    # other two are 0
+    words = rec[:16].view(torch.int32).cpu()
+    want = torch.tensor([float(q.float().abs().max()), 0.0, float(v.float().abs().max()), 0.0]).view(torch.int32)
+    assert torch.equal(words, want), (words, want)
     # v's copy: fp16 of v times a power of two s, exact where |s v| is at
     # least 2^-14 (fp16's normal range), else within fp16's subnormal half
     # spacing 2^-25
