@@ -246,10 +246,14 @@ __device__ __forceinline__ void qk_tile(const __bf16* kl, const bf16x8* qf, int 
 
 // Softcap in exp2 units: cap*log2(e) * tanh(scale * s / cap), plus with BIAS
 // sigma * (j - i) (sigma in exp2 units; see bias_tile).
+// cap_out tanh(x) = cap_out - 2 cap_out r with r = 1 / (2^y + 1).  With the
+// bias, the capped score is formed here (the bias joins the constant term).
+// Without it the tile keeps r itself: the capped score falls as r grows, so
+// the row max comes from the row min of r (capped_max), invisible cells hold
+// r = +inf, and the exp2 weight takes one multiply-add of r, which also
+// subtracts the running max.
 template <bool BIAS>
 __device__ __forceinline__ void softcap_tile(const FwdArgs& a, f32x16* s, float sigma, int ktile, int d0) {
-  // cap_out tanh(x) = cap_out - 2 cap_out / (2^y + 1): one multiply-add
-  // after the reciprocal (the bias joins the constant term)
   const float base = (BIAS ? sigma * (float)(ktile * kBN + d0) : 0.f) + a.cap_out;
   const float m2 = -2.0f * a.cap_out;
 #pragma unroll
@@ -257,7 +261,10 @@ __device__ __forceinline__ void softcap_tile(const FwdArgs& a, f32x16* s, float 
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const float r = fast_rcp(fast_exp2(s[b][v] * a.cap_in) + 1.0f);
-      s[b][v] = __builtin_fmaf(m2, r, BIAS ? __builtin_fmaf(sigma, (float)key_off(b, v), base) : base);
+      if constexpr (BIAS)
+        s[b][v] = __builtin_fmaf(m2, r, __builtin_fmaf(sigma, (float)key_off(b, v), base));
+      else
+        s[b][v] = r;
     }
 }
 
@@ -273,8 +280,24 @@ __device__ __forceinline__ float tile_max(const f32x16* s) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// Invisible cells of a PARTIAL tile become -inf (cell (row, key) of slice sl).
-__device__ __forceinline__ void mask_tile(const DevSlice& sl, int ktile, int row, int hh, f32x16* s) {
+// The same row max for a tile that holds softcap's r (no bias): the capped
+// score cap_out - 2 cap_out r of the smallest r (a row with no visible cell
+// has r = +inf everywhere and gets -inf).
+__device__ __forceinline__ float capped_max(const f32x16* s, float cap_out) {
+  float mn = INFINITY;
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mn = fminf(mn, s[b][v]);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(mn), __float_as_uint(mn), false, false);
+  mn = fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return __builtin_fmaf(-2.0f * cap_out, mn, cap_out);
+}
+
+// Invisible cells of a PARTIAL tile become `hidden` (cell (row, key) of
+// slice sl): -inf for scores, +inf for softcap's r.
+__device__ __forceinline__ void mask_tile(const DevSlice& sl, int ktile, int row, int hh, f32x16* s,
+                                          float hidden) {
   int lo = sl.ks, hi = sl.ke;
   if (sl.causal) hi = min(hi, row + 1 + (sl.ke - sl.qe));
   if (row < sl.qs || row >= sl.qe) hi = lo;  // row outside the slice: nothing visible
@@ -286,7 +309,7 @@ __device__ __forceinline__ void mask_tile(const DevSlice& sl, int ktile, int row
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int off = 32 * b + 8 * (v >> 2) + (v & 3);
-      if (off < lo || off >= hi) s[b][v] = -INFINITY;
+      if (off < lo || off >= hi) s[b][v] = hidden;
     }
 }
 
@@ -307,6 +330,8 @@ __global__ __launch_bounds__(kThreads * HPW, 2) void fwd_kernel(FwdArgs a) {
   constexpr int KS = D / 16;  // k steps of the QK^T contraction
   constexpr int DB = D / 32;  // 32-wide blocks of the head dim in O^T
   constexpr int kTileElems = Smem::kTileBytes / 2;
+  // score tiles hold softcap's r in place of the capped score
+  constexpr bool RCAP = SOFTCAP && !BIAS;
   // K and V double buffers as separate LDS objects: the compiler can then
   // tell a direct-to-LDS fetch into one buffer from reads of another and
   // does not make those reads wait for the fetch
@@ -378,6 +403,12 @@ __global__ __launch_bounds__(kThreads * HPW, 2) void fwd_kernel(FwdArgs a) {
     }
     if constexpr (SOFTCAP) softcap_tile<BIAS>(a, s, sigma, ktile, d0);
   };
+  auto row_max = [&](const f32x16* s) {
+    if constexpr (RCAP)
+      return capped_max(s, a.cap_out);
+    else
+      return tile_max(s);
+  };
 
   f32x16 o[DB];
 #pragma unroll
@@ -402,7 +433,7 @@ __global__ __launch_bounds__(kThreads * HPW, 2) void fwd_kernel(FwdArgs a) {
     dma_barrier();
     f32x16 sa[2], sb[2];
     scores(kb0, entry(0).tile, sa);
-    float mx_cur = tile_max(sa);
+    float mx_cur = row_max(sa);
     // entries of walk positions j, j + 1 and j + 2 for step j (positions
     // past the end of the list repeat its last entry).  Later entries arrive
     // by vector loads issued with a step's fetches, so the step's closing
@@ -424,8 +455,8 @@ __global__ __launch_bounds__(kThreads * HPW, 2) void fwd_kernel(FwdArgs a) {
       // ---- tile j: mask (PARTIAL only) and the running max
       const DevEntry ent = e0;
       if (ent.meta & 1) {
-        mask_tile(plan_slice(a.slices, ent.meta >> 1), ent.tile, row, hh, s_cur);
-        mx_cur = tile_max(s_cur);
+        mask_tile(plan_slice(a.slices, ent.meta >> 1), ent.tile, row, hh, s_cur, RCAP ? INFINITY : -INFINITY);
+        mx_cur = row_max(s_cur);
       }
       // move the running max only when this tile's max exceeds it by more
       // than 2^8 in exp2 units (all lanes together, so the branch is
@@ -443,6 +474,10 @@ __global__ __launch_bounds__(kThreads * HPW, 2) void fwd_kernel(FwdArgs a) {
         m_run = m_new;
       }
       const float neg = (m_run == -INFINITY) ? 0.f : -m_run * a.score_mult;
+      // exp2 argument: score * score_mult - m_run * score_mult, or with r,
+      // cap_out - 2 cap_out r - m_run (score_mult is 1 with softcap)
+      const float p_mult = RCAP ? -2.0f * a.cap_out : a.score_mult;
+      const float p_add = RCAP ? a.cap_out + neg : neg;
 
       // ---- A: S_{j+1} = K_{j+1} Q^T on the matrix cores, while
       //      B: the VALU turns tile j into exp2 weights
@@ -479,7 +514,7 @@ __global__ __launch_bounds__(kThreads * HPW, 2) void fwd_kernel(FwdArgs a) {
         float p[8];
 #pragma unroll
         for (int e8 = 0; e8 < 8; ++e8) {
-          p[e8] = fast_exp2(__builtin_fmaf(s_cur[b][h8 + e8], a.score_mult, neg));
+          p[e8] = fast_exp2(__builtin_fmaf(s_cur[b][h8 + e8], p_mult, p_add));
           l4[e8 & 3] += p[e8];
         }
 #pragma unroll
@@ -518,7 +553,7 @@ __global__ __launch_bounds__(kThreads * HPW, 2) void fwd_kernel(FwdArgs a) {
         }
       if constexpr (MORE) {
         if constexpr (SOFTCAP) softcap_tile<BIAS>(a, s_next, sigma, e1.tile, d0);
-        mx_cur = tile_max(s_next);
+        mx_cur = row_max(s_next);
         // Instruction order for the block above: the V transpose reads run 8
         // ahead of the PV products, with the row max of the next tile in
         // their shadows.
