@@ -75,13 +75,17 @@ def test_random_slices_full_compare(case):
         compare_out_lse(out.cpu(), lse.cpu(), ref_out, ref_lse, f"{case} trial {trial}")
 
 
-def test_short_key_range_causal_rows_empty():
-    say("fwd causal slice with Lk < Lq")
+# with softcap the score tiles of the unbiased forward hold the cap's
+# reciprocal, whose masked value is +inf: rows with nothing visible must
+# still come out as 0 and -inf
+@pytest.mark.parametrize("cap", [0.0, 30.0])
+def test_short_key_range_causal_rows_empty(cap):
+    say(f"fwd causal slice with Lk < Lq, softcap {cap}")
     q, k, v, _ = W.make_tensors(300, 100, 2, 1, 128, seed=11, with_dout=False)
     qr, kr, ty = [[0, 300]], [[0, 100]], [1]
-    out, lse = run_fwd(q, k, v, qr, kr, ty, 0.1, 0.0, dev())
-    ref_out, ref_lse = O.attention_fwd(to64(q), to64(k), to64(v), qr, kr, ty, 0.1, 0.0)
-    compare_out_lse(out.cpu(), lse.cpu(), ref_out, ref_lse, "Lk<Lq")
+    out, lse = run_fwd(q, k, v, qr, kr, ty, 0.1, cap, dev())
+    ref_out, ref_lse = O.attention_fwd(to64(q), to64(k), to64(v), qr, kr, ty, 0.1, cap)
+    compare_out_lse(out.cpu(), lse.cpu(), ref_out, ref_lse, f"Lk<Lq cap {cap}")
     assert torch.all(lse[:200] == float("-inf")) and torch.all(out[:200] == 0)
 
 
