@@ -184,3 +184,26 @@ def test_noalloc_rejects_sizes_beyond_its_array(lib):
     qr = np.array([[0, 17]], np.int32); kr = np.array([[0, 16]], np.int32); ty = np.array([0], np.int32)
     rc = lib.ffa_fwd_noalloc(64, 64, 64, 16, 16, 2, 1, 64, ip(qr), ip(kr), ip(ty), 1, 0.1, 0.0, 64, 64, None)
     assert rc == -1 and "q range" in ffa.ffa_last_error()
+
+
+def test_injected_host_allocation_failure(lib, monkeypatch):
+    """FFA_INJECT_NOMEM makes every host planning step fail as if the host
+    allocator had run out: the host-only entry points then return
+    FFA_ERR_NOMEM (-4) with a message, and work again once it is unset."""
+    qr, kr, ty = [[0, 300]], [[0, 300]], [1]
+    monkeypatch.setenv("FFA_INJECT_NOMEM", "1")
+    with pytest.raises(ffa.FfaError) as e:
+        ffa.ffa_plan_host(300, 300, qr, kr, ty, 128, 64)
+    assert e.value.code == -4 and "out of host memory" in str(e.value)
+    with pytest.raises(ffa.FfaError) as e:
+        ffa.ffa_block_slices([1, 2], [[0, 0], [0, 1]], 256, 256)
+    assert e.value.code == -4 and "out of host memory" in str(e.value)
+    # the plan handle entry point fails before any device work
+    ip = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    q = np.array(qr, np.int32); k = np.array(kr, np.int32); t = np.array(ty, np.int32)
+    h = ctypes.c_void_p()
+    assert lib.ffa_plan_create(300, 300, ip(q), ip(k), ip(t), 1, None, ctypes.byref(h)) == -4
+    assert h.value is None and "out of host memory" in ffa.ffa_last_error()
+    monkeypatch.setenv("FFA_INJECT_NOMEM", "0")
+    row_ptr, ent, order = ffa.ffa_plan_host(300, 300, qr, kr, ty, 128, 64)
+    assert row_ptr[-1] == len(ent) > 0
