@@ -432,9 +432,11 @@ int64_t ffa_plan_export(ffa_plan_t plan, int which, int64_t* n_tiles, int64_t* r
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* ffa_last_error(void);
 
-/* Build facts: target architecture, tile sizes, compiler (cf. the build-flag
- * file exposed at run time in flash-attention PR "Add torch.compile support
- * to flash attention 3"). */
+/* Build facts: target architecture, tile sizes, a hash of the sources the
+ * library was built from (source=, 16 hex digits) and the compiler (cf. the
+ * build-flag file exposed at run time in flash-attention PR "Add
+ * torch.compile support to flash attention 3").  A static string owned by
+ * the library. */
 const char* ffa_build_info(void);
 
 #ifdef __cplusplus

@@ -8,6 +8,7 @@ sanitizer-instrumented test driver (CPU only, plain g++).
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import shutil
 import subprocess
@@ -40,9 +41,23 @@ def sources():
                   if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str, hipcc: str) -> str:
+def source_hash() -> str:
+    """First 16 hex digits of a SHA-256 over the library's sources (csrc/
+    and include/ffa.h, names and contents); ffa_build_info reports the value
+    the library was built with, so a stale build can be told apart."""
+    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp", ".hpp")))
+    h = hashlib.sha256()
+    for rel in [os.path.join("csrc", f) for f in files] + [os.path.join("..", "include", "ffa.h")]:
+        h.update(rel.encode())
+        with open(os.path.join(PKG, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _compile(src: str, hipcc: str, src_hash: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc, *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c", src, "-o", obj]
+    cmd = [hipcc, *HIP_FLAGS, f'-DFFA_SOURCE_HASH="{src_hash}"', "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           "-c", src, "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -56,8 +71,9 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
     srcs = sources()
+    src_hash = source_hash()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, hipcc), srcs))
+        objs = list(ex.map(lambda s: _compile(s, hipcc, src_hash), srcs))
     tmp = LIB + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -511,13 +511,20 @@ extern "C" {
 
 const char* ffa_last_error(void) { return g_err.c_str(); }
 
+// hash of the sources the library was built from (the build passes it;
+// see range_masked_attention_amd/_build.py source_hash)
+#ifndef FFA_SOURCE_HASH
+#define FFA_SOURCE_HASH "unknown"
+#endif
+
 const char* ffa_build_info(void) {
   static std::string info = [] {
     std::string s = "arch=gfx950 fwd_tile=" + std::to_string(ffa::fwd_tile_rows()) + "x" +
                     std::to_string(ffa::fwd_tile_cols()) + " bwd_kv_tile=" +
                     std::to_string(ffa::bwd_kv_tile_rows()) + "x" + std::to_string(ffa::bwd_kv_tile_cols()) +
                     " bwd_q_tile=" + std::to_string(ffa::bwd_q_tile_rows()) + "x" +
-                    std::to_string(ffa::bwd_q_tile_cols()) + " head_dims=64,128 softcap=tanh compiler=" + __VERSION__;
+                    std::to_string(ffa::bwd_q_tile_cols()) + " head_dims=64,128 softcap=tanh source=" +
+                    FFA_SOURCE_HASH + " compiler=" + __VERSION__;
     return s;
   }();
   return info.c_str();

@@ -36,6 +36,10 @@ def test_exports_every_declared_symbol(lib):
 def test_build_info(lib):
     info = ffa.ffa_build_info()
     assert "arch=gfx950" in info
+    # the library was built from the sources in this tree (a stale build
+    # would carry another hash: rebuild with __graft_entry__.build())
+    from range_masked_attention_amd import _build
+    assert f"source={_build.source_hash()}" in info, info
     # every tile shape the planner is asked for is reported
     for key in ("fwd_tile=", "bwd_kv_tile=", "bwd_q_tile="):
         assert key in info, info
