@@ -10,9 +10,9 @@ workload: 8 packed causal sequences of 8192 tokens (65536 tokens), 32 q heads,
 
 Reported (one JSON line):
   value        forward TFLOP/s over unmasked pairs: 4 * d * hq * pairs divided
-               by the mean duration of ffa_fwd (out and lse; one kernel launch
-               here), timed after the steps with HIP events recorded on the
-               stream the kernel runs on
+               by the mean duration of ffa_fwd (out and lse: v's fp16 copy and
+               the forward kernel), timed after the steps with HIP events
+               recorded on the stream the kernels run on
   fwd_train_*  the same for the step's training forward (ffa_fwd_ex with a
                saved record: fp16 copy of v, P V in fp16, out's residual)
   bwd_tflops   backward TFLOP/s, 10 * d * hq * pairs over the backward kernels
@@ -126,6 +126,34 @@ def cpu_baseline(w: W.Workload, q, k, v, budget_s: float):
                       f"all {w.hq} heads) in {dt:.1f} s, fp64 NumPy"}
 
 
+def mfma_ceiling() -> int:
+    """The matrix cores' rate on their own, by operand values (probe library
+    range_masked_attention_amd/_lib/libffa_probe.so): one JSON line.  With the
+    pipes busy all the time, the rate over the nominal peak is the clock over
+    the nominal 2.4 GHz, which the GPU's power limit lowers as the operands'
+    bits get busier."""
+    import ctypes
+    from range_masked_attention_amd import _build
+    if not os.path.exists(_build.PROBE_LIB):
+        _build.build()
+    lib = ctypes.CDLL(_build.PROBE_LIB)
+    lib.ffa_probe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    lib.ffa_probe_mfma_rate.restype = ctypes.c_int
+    res = []
+    for f16, dtype in ((0, "bf16"), (1, "f16")):
+        for kind, name in ((0, "N(0,1)"), (1, "constant 0.7"), (2, "zeros")):
+            t = ctypes.c_double(0.0)
+            rc = lib.ffa_probe_mfma_rate(f16, kind, 2000, ctypes.byref(t))
+            if rc != 0:
+                print(json.dumps({"error": f"probe failed ({rc})", "dtype": dtype, "operands": name}))
+                return 1
+            res.append({"dtype": dtype, "operands": name, "value": round(t.value, 1),
+                        "frac": round(t.value / PEAK_BF16_TFLOPS, 4)})
+    print(json.dumps({"metric": "matrix-core TFLOP/s, 32x32x16 products on register operands", "unit": "TFLOP/s",
+                      "peak": PEAK_BF16_TFLOPS, "waves_per_simd": 2, "results": res}))
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,7 +167,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="time budget of the oracle sample")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="instead of the benchmark: matrix-core TFLOP/s of 32x32x16 products on register "
+                         "operands (bf16 and fp16; N(0,1), constant and zero values)")
     args = ap.parse_args()
+    if args.mfma_ceiling:
+        sys.exit(mfma_ceiling())
 
     if args.gpus != 1:
         print(json.dumps({"error": "the benchmark runs on one GPU only; pass --gpus 1",

@@ -19,6 +19,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libffa.so")
+PROBE_SRC = os.path.join(PKG, "probe", "mfma_rate.hip")
+PROBE_LIB = os.path.join(LIBDIR, "libffa_probe.so")
 BUILD = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
@@ -80,9 +82,22 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    build_probe(hipcc)
     if verbose:
         print(f"built {LIB}")
     return LIB
+
+
+def build_probe(hipcc: str) -> str:
+    """The matrix-core rate probe bench.py --mfma-ceiling loads: a library of
+    its own, so nothing of it sits in libffa.so."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc, "-x", "hip", *HIP_FLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"probe build failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 def build_planner_sanitized(out: str) -> str:
