@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libffa.so")
-PROBE_SRC = os.path.join(PKG, "probe", "mfma_rate.hip")
+PROBE_SRC = os.path.join(ROOT, "tests", "native", "mfma_rate.hip")
 PROBE_LIB = os.path.join(LIBDIR, "libffa_probe.so")
 BUILD = os.path.join(ROOT, "_build")
 ARCH = "gfx950"

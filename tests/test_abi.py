@@ -211,3 +211,14 @@ def test_injected_host_allocation_failure(lib, monkeypatch):
     monkeypatch.setenv("FFA_INJECT_NOMEM", "0")
     row_ptr, ent, order = ffa.ffa_plan_host(300, 300, qr, kr, ty, 128, 64)
     assert row_ptr[-1] == len(ent) > 0
+
+
+def test_probe_library_exports_its_entry_point(lib):
+    """The matrix-core rate probe bench.py --mfma-ceiling loads is a library
+    of its own (nothing of it is in libffa.so) with one C entry point."""
+    from range_masked_attention_amd import _build
+    if not os.path.exists(_build.PROBE_LIB):
+        _build.build_probe(_build._hipcc())
+    probe = ctypes.CDLL(_build.PROBE_LIB)
+    assert hasattr(probe, "ffa_probe_mfma_rate")
+    assert not hasattr(lib, "ffa_probe_mfma_rate")
