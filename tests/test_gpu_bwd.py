@@ -378,3 +378,19 @@ def test_short_lists(Tk, causal):
                                        magnitudes=True)
     for (n, g, r), m in zip((("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)), mags):
         _cmp(n, g, r, f"Tk {Tk} causal {causal}", m)
+
+
+# nearly uniform attention (scale 1e-4): every weight within a few ulps of
+# 1/l, dV the row average of dO, dq and dk of order the scale
+@pytest.mark.parametrize("cap", [0.0, 30.0])
+def test_tiny_scale(cap):
+    say(f"bwd scale 1e-4 softcap {cap}")
+    Tq, Tk, hq, hkv, d = 300, 500, 4, 2, 128
+    rng = np.random.default_rng(78)
+    qr, kr, ty = W.random_slices(rng, Tq, Tk, max_slices=5, n_dummies=1)
+    q, k, v, do = W.make_tensors(Tq, Tk, hq, hkv, d, seed=78)
+    dq, dk, dv = _bwd_gpu(q, k, v, do, qr, kr, ty, 1e-4, cap, dev())
+    rq, rk, rv, mags = O.attention_bwd(to64(q), to64(k), to64(v), to64(do), qr, kr, ty, 1e-4, cap,
+                                       magnitudes=True)
+    for (n, g, r), m in zip((("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)), mags):
+        _cmp(n, g, r, f"scale 1e-4 cap {cap}", m)

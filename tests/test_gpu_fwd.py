@@ -357,3 +357,21 @@ def test_short_key_lists(Tk, walk):
         slopes = st.double().cpu().numpy()
     ref_out, ref_lse = O.attention_fwd(to64(q), to64(k), to64(v), qr, kr, ty, scale, 0.0, alibi_slopes=slopes)
     compare_out_lse(out.cpu(), lse.cpu(), ref_out, ref_lse, f"Tk {Tk} {walk}")
+
+
+# softmax temperatures far from the workloads' 1/sqrt(d): nearly uniform
+# weights (scale 1e-4: every exponent within a few ulps of the max) and
+# nearly one-hot rows (scale 3: logits with a spread of hundreds, so the
+# running max moves by far more than the lazy-rescale threshold), with and
+# without softcap
+@pytest.mark.parametrize("scale", [1e-4, 3.0])
+@pytest.mark.parametrize("cap", [0.0, 30.0])
+def test_extreme_scales(scale, cap):
+    say(f"fwd extreme scale {scale} softcap {cap}")
+    Tq, Tk, hq, hkv, d = 300, 500, 4, 2, 128
+    rng = np.random.default_rng(77)
+    qr, kr, ty = W.random_slices(rng, Tq, Tk, max_slices=5, n_dummies=1)
+    q, k, v, _ = W.make_tensors(Tq, Tk, hq, hkv, d, seed=77, with_dout=False)
+    out, lse = run_fwd(q, k, v, qr, kr, ty, scale, cap, dev())
+    ref_out, ref_lse = O.attention_fwd(to64(q), to64(k), to64(v), qr, kr, ty, scale, cap)
+    compare_out_lse(out.cpu(), lse.cpu(), ref_out, ref_lse, f"scale {scale} cap {cap}")
