@@ -227,6 +227,11 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a0) {
   fold_scales(&a, &sq, &sk, &sv, &sdo);
   constexpr int KS = D / 16, DB = D / 32;
   constexpr int kXchg = kDkvRows * 32;  // fp32 P of one pair and step (floats)
+  // softcap without the bias: the producer works from r = 1 / (2^y + 1)
+  // (tanh = 1 - 2r, 1 - tanh^2 = 4r(1 - r)) and forms 4P, its rows' lse
+  // term holding cap_out + 2 - lse; dV then accumulates 4 dV
+  constexpr bool RCAP = SOFTCAP && !BIAS;
+  const float cap_m2 = -2.0f * a.cap_out;
   __shared__ __attribute__((aligned(1024))) char q_s0[T::kBytes];
   __shared__ __attribute__((aligned(1024))) char q_s1[T::kBytes];
   __shared__ __attribute__((aligned(1024))) char q_s2[T::kBytes];
@@ -345,7 +350,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a0) {
   auto publish = [&](int slot) {
     if (tid < kDkvRows) {
       // lse in exp2 units (+inf for rows nothing sees, so their P is 0)
-      s_lse[slot][tid] = lse_raw + bias_row;
+      s_lse[slot][tid] = RCAP ? (a.cap_out + 2.0f) - lse_raw : lse_raw + bias_row;
       s_dv[slot][tid] = d_raw;
     }
   };
@@ -399,13 +404,22 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a0) {
             float p4[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              float th;
-              const float t = score_to_t<SOFTCAP>(a, s[qb][4 * v4 + i], &th);
-              float p = BIAS ? fast_exp2(t + (bias_key - l4[i])) : fast_exp2(t - l4[i]);
-              if constexpr (PARTIAL)
-                if (rbase + i < lo || rbase + i >= hi) p = 0.f;
-              p4[i] = p;
-              px[i] = SOFTCAP ? p * (1.0f - th * th) : p;
+              if constexpr (RCAP) {
+                const float rc = fast_rcp(fast_exp2(s[qb][4 * v4 + i] * a.cap_in) + 1.0f);
+                float p = fast_exp2(__builtin_fmaf(rc, cap_m2, l4[i]));  // 4P
+                if constexpr (PARTIAL)
+                  if (rbase + i < lo || rbase + i >= hi) p = 0.f;
+                p4[i] = p;
+                px[i] = p * __builtin_fmaf(-rc, rc, rc);  // P (1 - tanh^2)
+              } else {
+                float th;
+                const float t = score_to_t<SOFTCAP>(a, s[qb][4 * v4 + i], &th);
+                float p = BIAS ? fast_exp2(t + (bias_key - l4[i])) : fast_exp2(t - l4[i]);
+                if constexpr (PARTIAL)
+                  if (rbase + i < lo || rbase + i >= hi) p = 0.f;
+                p4[i] = p;
+                px[i] = SOFTCAP ? p * (1.0f - th * th) : p;
+              }
             }
             *reinterpret_cast<f32x4*>(xch + ((qb * 4 + v4) * 64 + lane) * 4) = px;
             pw[2 * qb + (v4 >> 1)][2 * (v4 & 1)] = pack_f16x2(p4[0], p4[1]);
@@ -547,8 +561,9 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_kernel(BwdArgs a0) {
   } else if (key < a.Tk) {
     const int64_t off = ((int64_t)key * a.hkv + g) * D;
     __bf16* dst = producer ? a.dv : a.dk;
-    // dV^T accumulated sdo dV; the consumer accumulated -sdo sv sq dK^T / scale
-    const float mul = producer ? 1.0f / sdo : -a.scale / (sdo * sv * sq);
+    // dV^T accumulated sdo dV (4 sdo dV in the reciprocal form); the consumer
+    // accumulated -sdo sv sq dK^T / scale
+    const float mul = producer ? (RCAP ? 0.25f : 1.0f) / sdo : -a.scale / (sdo * sv * sq);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -600,7 +615,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_reduce_kernel(BwdArgs a0) {
     const int r = is_v ? i - kDkvKeys * D : i;
     const int key = kt * kDkvKeys + r / D, dim = r % D;
     if (key < a.Tk) {
-      const float mul = is_v ? 1.0f / sdo : -a.scale / (sdo * sv * sq);  // dK^T partials carry -dK
+      // dK^T partials carry -dK; dV partials 4 dV with softcap and no bias
+      const float vmul = (a.cap_out > 0.f && a.slopes == nullptr) ? 0.25f : 1.0f;
+      const float mul = is_v ? vmul / sdo : -a.scale / (sdo * sv * sq);
       u32x2 w;
       w[0] = pack_bf16x2(mul * sum[0], mul * sum[1]);
       w[1] = pack_bf16x2(mul * sum[2], mul * sum[3]);
